@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+A step is one call of the C ABI (attention kernel + split-KV merge) over one
+batch of the synthetic workload, inputs resident in HBM.  Before every timed
+step the L2 and the 256 MB last-level cache are flushed (outside the events),
+so the KV bytes really come from HBM.  The default workload is the int8 decode
+case (B=64, q_len 1, 32/8 heads, D=128, page 64, KV lens U[512, 4096],
+per-channel scales, chunk 512): the one the decode KV-bandwidth metric is
+quoted on.  --config 1..5 selects another workload.
+
+Prints ONE JSON line with the headline metric, the roofline of the attention
+kernel (its duration isolated with HIP events on the launch stream: the
+merge-only time, measured with the public split_kv_merge call on the same
+partials, is subtracted from the full call) and the oracle's throughput on a
+bounded sample of the same workload (cpu_baseline).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFS = 2516.6  # dense f16/bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+
+WORKLOAD_TEXT = {
+    1: "tiny_append: B=2 H_q=4 H_kv=1 D=64 P=16 L={37,50} n={3,1} fp32 Q int8 per-head causal",
+    2: "decode_int8: B=64 q_len=1 H_q=32 H_kv=8 D=128 P=64 L~U[512,4096] int8 per-channel chunk=512",
+    3: "append_prefill: B=8 n~U[256,1024] L~U[0,2048] H_q=32 H_kv=8 D=128 P=64 int8 per-head causal",
+    4: "spec_decode: B=128 q_len=5 H_q=64 H_kv=8 D=128 P=64 L~lognormal(2048,1)[128,32768] int8 per-channel chunk=1024",
+    5: "mla_decode: B=32 q_len=1 H_q=128 H_kv=1 D_qk=576 D_v=512 P=64 L~U[4096,16384] fp8 per-tensor chunk=512",
+}
+
+
+def work_figures(w):
+    """Algorithmic work of one call: KV bytes, total bytes, useful flops."""
+    T = w.kv_tokens().astype(np.int64)
+    H, Dq, Dv = w.num_kv_heads, w.head_dim_qk, w.head_dim_v
+    row_bytes = Dq if w.shared_kv else Dq + Dv
+    kv = int((T * H * row_bytes).sum())
+    q_bytes = w.q.nbytes
+    out_bytes = w.total_q * w.num_q_heads * (Dv * 2 + 4)
+    table = int(((T + w.page_size - 1) // w.page_size).sum()) * 4
+    scales = w.k_scale.nbytes + w.v_scale.nbytes
+    total = kv + q_bytes + out_bytes + table + scales
+    vis = 0
+    for b in range(w.batch):
+        n, L = int(w.q_lens[b]), int(w.seq_lens_kv[b])
+        if w.causal:
+            vis += n * L + n * (n + 1) // 2
+        else:
+            vis += n * (L + n)
+    flops = vis * w.num_q_heads * 2 * (Dq + Dv)
+    return kv, total, flops
+
+
+def cpu_baseline(idx, budget_s=15.0):
+    """Time the fp64 oracle (as it stands) on a bounded sample of requests."""
+    import oracle
+    from workloads import config_workload
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    w = config_workload(idx)
+    T = w.kv_tokens().astype(np.int64)
+    order = np.random.default_rng(7).permutation(w.batch)
+    done, t0 = [], time.perf_counter()
+    for b in order:
+        oracle.attention(w, requests=[int(b)])
+        done.append(int(b))
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    row_bytes = w.head_dim_qk if w.shared_kv else w.head_dim_qk + w.head_dim_v
+    kv = int((T[done] * w.num_kv_heads * row_bytes).sum())
+    vis = sum(int(w.q_lens[b]) * int(w.seq_lens_kv[b]) + int(w.q_lens[b]) * (int(w.q_lens[b]) + 1) // 2
+              for b in done)
+    flops = vis * w.num_q_heads * 2 * (w.head_dim_qk + w.head_dim_v)
+    if idx in (1, 3):
+        val, unit = flops / dt / 1e12, "TFLOP/s"
+    else:
+        val, unit = kv / dt / 1e9, "GB/s"
+    return {"value": round(val, 6), "unit": unit, "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(done)} of {w.batch} requests of {w.name} ({dt:.1f} s, fp64 NumPy, "
+                      f"host cores visible: {len(os.sched_getaffinity(0))})"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--chunk", type=int, default=None, help="override chunk_size")
+    ap.add_argument("--no-flush", action="store_true", help="skip the per-step cache flush")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py runs on one GPU: the paged attention path has no multi-GPU leg in this "
+              "build (sharding by request or KV head needs no communication; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_attention_gather_amd import _lib as L
+    from paged_kv_attention_gather_amd.harness import DeviceProblem
+    from workloads import config_workload
+
+    print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
+    w = config_workload(args.config)
+    dp = DeviceProblem(w, chunk_size=args.chunk)
+    chunk = dp.prob.chunk_size
+    kv_bytes, alg_bytes, flops = work_figures(w)
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def do_flush():
+        if not args.no_flush:
+            flush.add_(1)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        do_flush()
+        dp.run()
+    torch.cuda.synchronize()
+
+    # Full ABI call (attention + merge), per step, flushed caches.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        do_flush()
+        ev[i][0].record(stream)
+        dp.run()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    ms = float(np.mean(step_ms))
+
+    # Merge-only time on the same partials (public split_kv_merge entry point),
+    # with the partials cache-resident as they are right after the attention kernel.
+    merge_ms = 0.0
+    if chunk > 0:
+        mc = -(-(int(w.seq_lens_kv.max()) + int(w.q_lens.max())) // chunk)
+        po_bytes = dp.total_q * mc * w.num_q_heads * w.head_dim_v * 4
+        lse_off = (po_bytes + 255) // 256 * 256
+        base = dp.workspace.data_ptr()
+        out2 = torch.empty_like(dp.out)
+        lse2 = torch.empty_like(dp.lse)
+        cu = None if dp.decode else dp.cu_seqlens_q
+        qlu = int(w.decode_q_len) if dp.decode else 0
+        mev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.steps):
+            mev[i][0].record(stream)
+            L.split_kv_merge(base, base + lse_off, cu, dp.seq_lens_kv, qlu, w.batch, dp.total_q,
+                             int(w.q_lens.max()), w.num_q_heads, w.head_dim_v, chunk, mc, out2, lse2)
+            mev[i][1].record(stream)
+        torch.cuda.synchronize()
+        merge_ms = float(np.mean([a.elapsed_time(b) for a, b in mev]))
+    attn_ms = max(ms - merge_ms, 1e-6)
+
+    if args.config in (1, 3):
+        value, unit = flops / (ms * 1e-3) / 1e12, "TFLOP/s"
+    else:
+        value, unit = kv_bytes / (ms * 1e-3) / 1e9, "GB/s"
+    if args.config in (3, 5):
+        achieved = flops / (attn_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_F16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFS, 4), "traffic": None}
+    else:
+        achieved = alg_bytes / (attn_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    roof["kernel"] = "paged_attn_kernel"
+    roof["kernel_ms"] = round(attn_ms, 5)
+    roof["merge_ms"] = round(merge_ms, 5)
+
+    line = {
+        "metric": "decode: KV GB/s & %HBM peak; append: attention TFLOP/s & %MFMA peak",
+        "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.config], "global_batch": int(w.batch),
+                   "kv_dtype": w.kv_dtype, "chunk_size": int(chunk), "cache_flush": not args.no_flush,
+                   "kv_bytes": kv_bytes, "alg_bytes": alg_bytes, "flops": flops,
+                   "min_ms": round(float(np.min(step_ms)), 5),
+                   "wall_ms_per_step_incl_flush": round(t_wall / args.steps * 1e3, 4)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

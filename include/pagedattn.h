@@ -1,0 +1,203 @@
+/*
+ * pagedattn.h - C ABI of the MI355X (gfx950) paged-KV append/decode attention
+ * library (libpagedattn.so).
+ *
+ * The operation (stated in full by the pages' kernels, see each entry point):
+ * for request b with n_b appended query tokens and L_b cached tokens, the
+ * appended tokens attend over the T_b = L_b + n_b keys of the request, whose
+ * K/V rows (the appended tokens' rows included) are already stored in a paged,
+ * quantized cache.  Key j of request b lives in physical page
+ * block_table[b][j / page_size], slot j % page_size.  Query head h reads KV
+ * head g = h / G with G = H_q / H_kv (GQA).  Values are decode(byte) * scale
+ * with int8 (two's complement) or fp8 E4M3 (OCP "fn", max 448) bytes and a
+ * per-tensor, per-KV-head or per-(KV-head, channel) fp32 scale.  Logits are
+ * z_j = sm_scale * q . K[j]; with causal masking, appended token t sees keys
+ * j <= L_b + t (bottom-right aligned).  The outputs are
+ *   out[t, h, :] = sum_j softmax(z)_j * V[j, :]      (bf16)
+ *   lse[t, h]    = ln sum_j exp(z_j)                 (fp32, natural log)
+ * Long contexts may be split into KV chunks of chunk_size keys; each chunk's
+ * normalized partial output and natural LSE are then merged by log-sum-exp.
+ *
+ * Conventions shared by every entry point:
+ *  - Every array argument is a DEVICE pointer owned by the caller.  The library
+ *    never allocates, frees or retains a pointer after the enqueued work ends.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *    Calls are stateless and re-entrant and never synchronize the host.
+ *  - All arguments are validated before anything is enqueued: a call that
+ *    returns a non-zero status has enqueued nothing.  A kernel launch failure
+ *    is reported as PA_ERR_HIP.  The contents of device arrays (lengths, page
+ *    ids) are the caller's contract and are not checked: page ids must be valid
+ *    for every key j < T_b, entries past ceil(T_b / page_size) are never read.
+ *  - pa_last_error() returns a thread-local description of the last failure.
+ */
+#ifndef PAGEDATTN_H_
+#define PAGEDATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,         /* null pointer, bad size or inconsistent shape */
+  PA_ERR_UNSUPPORTED = 2,         /* valid but not compiled (head dim, dtype, ...) */
+  PA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < paged_attn_workspace_size() */
+  PA_ERR_HIP = 4                  /* a HIP runtime call or launch failed */
+};
+
+/* Element types. */
+enum {
+  PA_DTYPE_BF16 = 0,
+  PA_DTYPE_F32 = 1,
+  PA_DTYPE_I8 = 2,       /* two's-complement int8 cache bytes */
+  PA_DTYPE_FP8_E4M3 = 3  /* OCP E4M3 "fn" cache bytes (max 448, no inf) */
+};
+
+/* Dequant scale granularity.  PER_TENSOR: k_scale/v_scale hold 1 float;
+ * PER_HEAD: [H_kv]; PER_CHANNEL: [H_kv, D] (D_qk for K, D_v for V). */
+enum {
+  PA_SCALE_PER_TENSOR = 0,
+  PA_SCALE_PER_HEAD = 1,
+  PA_SCALE_PER_CHANNEL = 2
+};
+
+/* Problem description (host struct, read during the call only).
+ * Cache strides are in elements (= bytes, the cache is 1 byte per element);
+ * the head dimension is contiguous.  Keys of request b come from
+ *   k_cache + page * k_stride_page + g * k_stride_head + slot * k_stride_token.
+ * For the MLA layout pass v_cache == k_cache with head_dim_v < head_dim_qk:
+ * V is then the first head_dim_v bytes of each K row. */
+typedef struct pa_problem {
+  int32_t batch;              /* B, number of requests */
+  int32_t num_q_heads;        /* H_q */
+  int32_t num_kv_heads;       /* H_kv, divides H_q */
+  int32_t head_dim_qk;        /* D_qk: 64, 128 or 576 */
+  int32_t head_dim_v;         /* D_v: 64 (D_qk 64), 128 (D_qk 128) or 512 (D_qk 576, MLA) */
+  int32_t page_size;          /* P: power of two, 16..1024 */
+  int32_t num_pages;          /* pages in the pool (bounds the page ids) */
+  int32_t max_pages_per_seq;  /* row length of block_table */
+  int32_t max_q_len;          /* host upper bound of every n_b (sizes the grid) */
+  int32_t max_kv_len;         /* host upper bound of every L_b (sizes the grid) */
+  int64_t q_row_stride;       /* elements between consecutive query tokens */
+  int64_t k_stride_page, k_stride_head, k_stride_token;
+  int64_t v_stride_page, v_stride_head, v_stride_token;
+  int32_t q_dtype;            /* PA_DTYPE_BF16 or PA_DTYPE_F32 */
+  int32_t kv_dtype;           /* PA_DTYPE_I8 or PA_DTYPE_FP8_E4M3 */
+  int32_t scale_mode;         /* PA_SCALE_* */
+  int32_t causal;             /* 1: bottom-right causal mask, 0: none */
+  float sm_scale;             /* softmax scale on q . k (> 0) */
+  int32_t chunk_size;         /* 0: no split-KV; else a multiple of 64 keys */
+} pa_problem;
+
+/*
+ * paged_attn_workspace_size - bytes of workspace the attention calls need.
+ *
+ * Split-KV (chunk_size > 0) keeps, for every query token and head, one
+ * normalized fp32 partial output row and one natural-log fp32 partial LSE per
+ * chunk: [total_q, C_max, H_q, D_v] floats followed (256-byte aligned) by
+ * [total_q, C_max, H_q] floats, with C_max = ceil((max_kv_len + max_q_len) /
+ * chunk_size).  This is the partial-buffer layout of FastDeploy
+ * append_attention_c8_impl.cuh (tmp_workspace / tmp_m / tmp_d, indexed
+ * [token, chunk, head, dim]), with FlashInfer persistent.cuh's normalized
+ * output + LSE pair in place of the (m, d) pair.  Returns 0 when chunk_size is
+ * 0 and (size_t)-1 for an invalid problem.
+ */
+size_t paged_attn_workspace_size(const pa_problem* prob, int32_t total_q);
+
+/*
+ * paged_attn_append - ragged append / chunked-prefill attention.
+ *
+ * Follows FastDeploy append_attention_c8_impl.cuh (CascadeAppendAttentionC8Kernel
+ * and multi_query_append_attention_c8_kernel): ragged queries by cu_seqlens_q,
+ * kv_len = seq_lens_kv + q_len with the appended K/V read from the cache,
+ * GQA-packed query rows, causal bound, KV chunks of chunk_size keys.
+ *
+ *  q            [total_q, H_q, D_qk] in q_dtype, token rows q_row_stride apart.
+ *  k_cache      paged K bytes, v_cache paged V bytes (see pa_problem strides).
+ *  k_scale      fp32 dequant scales of K, v_scale of V (see PA_SCALE_*).
+ *  cu_seqlens_q int32 [B+1] prefix sums of n_b (cu_seqlens_q[0] = 0); n_b <= max_q_len.
+ *  seq_lens_kv  int32 [B] cached tokens L_b <= max_kv_len.
+ *  block_table  int32 [B, max_pages_per_seq] physical page ids.
+ *  out          bf16 [total_q, H_q, D_v] (contiguous).
+ *  lse          fp32 [total_q, H_q] natural-log LSE, or NULL.
+ *  workspace    device buffer of workspace_bytes (may be NULL when
+ *               paged_attn_workspace_size() is 0).
+ * Requests with n_b = 0 write nothing.  With chunk_size > 0, requests that
+ * span more than one chunk go through the workspace and split_kv_merge is
+ * enqueued on the same stream; single-chunk requests are written directly.
+ */
+int32_t paged_attn_append(const pa_problem* prob, int32_t total_q, const void* q,
+                          const void* k_cache, const void* v_cache, const float* k_scale,
+                          const float* v_scale, const int32_t* cu_seqlens_q,
+                          const int32_t* seq_lens_kv, const int32_t* block_table, void* out,
+                          float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attn_decode - decode and multi-token (speculative) decode.
+ *
+ * Same operation with a uniform host q_len (1..64) per request: q is
+ * [B * q_len, H_q, D_qk] and request b's tokens are rows b*q_len .. b*q_len +
+ * q_len - 1 (FastDeploy's decoder path with speculate_max_draft_token_num
+ * drafts; XQA mla_sm120.cu's inputSeqLen tokens with a per-token causal
+ * length).  Causal masking among the drafts is the bottom-right rule above.
+ * Arguments are as for paged_attn_append with cu_seqlens_q replaced by q_len.
+ */
+int32_t paged_attn_decode(const pa_problem* prob, int32_t q_len, const void* q,
+                          const void* k_cache, const void* v_cache, const float* k_scale,
+                          const float* v_scale, const int32_t* seq_lens_kv,
+                          const int32_t* block_table, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * split_kv_merge - log-sum-exp merge of split-KV partials.
+ *
+ * For every query token t of request b and head h, with C_b = ceil((L_b + n_b)
+ * / chunk_size) > 1: M = max_c lse_c, w_c = exp(lse_c - M), out = sum_c w_c O_c
+ * / sum_c w_c (bf16), lse = M + ln sum_c w_c.  Chunks with lse_c = -inf carry
+ * weight 0.  Rows with C_b <= 1 are left untouched (they were written
+ * directly).  Follows FlashInfer persistent.cuh (BlockBatchReductionPersistent,
+ * which skips rows with 0 or 1 partials) and XQA mla_sm120.cu
+ * (mergePartialOutputs); C_b is derived from the lengths as in FastDeploy's
+ * merge launches.
+ *
+ *  partial_o    fp32 [total_q, max_chunks, H_q, D_v] normalized partial outputs.
+ *  partial_lse  fp32 [total_q, max_chunks, H_q] natural-log partial LSE.
+ *  cu_seqlens_q int32 [B+1], or NULL with q_len_uniform > 0 (token b*q_len + t).
+ *  seq_lens_kv  int32 [B] cached tokens L_b.
+ *  out          bf16 [total_q, H_q, D_v]; lse fp32 [total_q, H_q] or NULL.
+ * D_v must be a multiple of 4 and at most 1024.
+ */
+int32_t split_kv_merge(const float* partial_o, const float* partial_lse,
+                       const int32_t* cu_seqlens_q, const int32_t* seq_lens_kv,
+                       int32_t q_len_uniform, int32_t batch, int32_t total_q, int32_t max_q_len,
+                       int32_t num_q_heads, int32_t head_dim_v, int32_t chunk_size,
+                       int32_t max_chunks, void* out, float* lse, void* stream);
+
+/*
+ * pa_gather_debug - raw-byte page gather (test aid).
+ *
+ * Copies the K rows of keys 0..T_b-1 of every request and KV head, in key
+ * order, to dst [B, H_kv, t_max, D_qk] bytes (rows past T_b are left as they
+ * are), using the same page-address function as the attention kernels
+ * (FlashInfer persistent.cuh prefetch_offest; XQA KVTilePartLoader::loadPages).
+ * T_b = seq_lens_kv[b] + q_lens[b]; q_lens int32 [B]; t_max >= max_b T_b.
+ */
+int32_t pa_gather_debug(const pa_problem* prob, const void* k_cache, const int32_t* block_table,
+                        const int32_t* seq_lens_kv, const int32_t* q_lens, int32_t t_max,
+                        uint8_t* dst, void* stream);
+
+/* Human-readable name of a status code. */
+const char* pa_status_string(int32_t status);
+
+/* Thread-local description of the last failing call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H_ */

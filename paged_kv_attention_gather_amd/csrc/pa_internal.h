@@ -1,0 +1,92 @@
+// Internal launch parameters shared by the C-ABI front end (pagedattn_api.cpp)
+// and the gfx950 kernels (pa_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "pagedattn.h"
+
+namespace pa {
+
+// One launch of the paged attention kernel.  A work unit is (request b, KV
+// head g, packed-row tile, KV chunk); grid = (row_tiles * chunk_slots, H_kv, B).
+struct AttnParams {
+  const void* q;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* cu_seqlens_q;  // null: uniform q_len_uniform tokens per request
+  const int32_t* seq_lens_kv;
+  const int32_t* block_table;
+  uint16_t* out;                // bf16 [total_q, H_q, D_v]
+  float* lse;                   // [total_q, H_q] or null
+  float* part_o;                // [total_q, max_chunks, H_q, D_v] (split only)
+  float* part_lse;              // [total_q, max_chunks, H_q]
+  int64_t q_row_stride;         // elements
+  int64_t k_stride_page, k_stride_head, k_stride_token;
+  int64_t v_stride_page, v_stride_head, v_stride_token;
+  int32_t num_q_heads;
+  int32_t group;                // G = H_q / H_kv
+  int32_t page_shift;           // log2(page_size)
+  int32_t max_pages_per_seq;
+  int32_t q_len_uniform;
+  int32_t chunk_size;           // 0 = no split
+  int32_t max_chunks;           // chunk slots in the grid / partial buffers
+  int32_t row_tiles;
+  int32_t q_is_f32;
+  int32_t scale_mode;
+  int32_t causal;
+  float qk_mult;                // sm_scale * log2(e)
+};
+
+struct MergeParams {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* cu_seqlens_q;
+  const int32_t* seq_lens_kv;
+  uint16_t* out;
+  float* lse;
+  int32_t q_len_uniform;
+  int32_t num_q_heads;
+  int32_t chunk_size;
+  int32_t max_chunks;
+};
+
+struct GatherParams {
+  const uint8_t* k_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens_kv;
+  const int32_t* q_lens;
+  uint8_t* dst;
+  int64_t k_stride_page, k_stride_head, k_stride_token;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_shift;
+  int32_t max_pages_per_seq;
+  int32_t t_max;
+};
+
+// Compiled attention specializations.
+struct AttnConfig {
+  int dqk, dv;      // head dims
+  bool fp8;         // cache bytes are e4m3fn (else int8)
+  bool shared_kv;   // V = first dv bytes of the K row
+  int nt;           // 16-row MFMA tiles per wave
+  int nw;           // waves per workgroup (they split the rows, share KV tiles)
+  bool hilo;        // Q carries per-channel scales or is fp32: f16 hi + lo parts
+  int nstage;       // KV tiles staged in LDS
+};
+
+// Returns hipSuccess, hipErrorInvalidValue when no specialization matches.
+hipError_t launch_attention(const AttnConfig& cfg, const AttnParams& p, dim3 grid,
+                            hipStream_t stream);
+hipError_t launch_merge(int dv, const MergeParams& p, int batch, int max_q_len,
+                        hipStream_t stream);
+hipError_t launch_gather(const GatherParams& p, int batch, hipStream_t stream);
+bool attention_supported(const AttnConfig& cfg);
+
+}  // namespace pa

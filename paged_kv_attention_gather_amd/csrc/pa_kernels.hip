@@ -1,0 +1,719 @@
+// gfx950 (CDNA4) kernels for paged-KV append/decode attention.
+//
+// Work unit: (request b, KV head g, tile of GQA-packed query rows, KV chunk).
+// Packed row r of a request is token r / G of head g*G + r % G (FastDeploy
+// append_attention_c8_impl.cuh packs GROUP_SIZE heads per KV head the same way
+// in its output write).  Each workgroup has NW waves; wave w owns 16*NT rows.
+// KV is walked in 64-key tiles that all waves share:
+//
+//   HBM --(global_load_lds_dwordx4, 16 B per lane, page-table addressed)--> LDS
+//   raw int8/fp8 rows, XOR-swizzled in 16-byte chunks so that the MFMA operand
+//   reads below are free of bank conflicts.
+//
+//   S^T = K Q^T   v_mfma_f32_16x16x32_f16; A = K rows read with ds_read_b128 and
+//                 converted to f16 in registers; B = Q^T held in registers with
+//                 every scale and log2(e) folded in.
+//   online softmax in the exp2 domain (XQA mla_sm120.cu folds qScale, the KV
+//                 scale and log2e into one logit multiplier and uses exp2).
+//   O^T += V^T P^T  A = V^T fetched with ds_read_b64_tr_b8 (the gfx950 LDS
+//                 transpose read) straight from the token-major V rows, then
+//                 converted; B = P^T, taken from the S^T accumulators without
+//                 any data movement because the key order of each lane group
+//                 is chosen to match the accumulator layout.
+//
+// int8 -> f16 and e4m3fn -> f16 are exact, so the MFMA sees the cache values
+// exactly; all scales are applied in fp32 outside the MFMA (per-channel K
+// scales multiply Q, V scales multiply the final O).
+#include <hip/hip_runtime.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef int int2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
+
+constexpr int TK = 64;  // keys per KV tile
+constexpr float LN2F = 0.6931471805599453f;
+
+// ------------------------------------------------------------ small helpers --
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);                                              // round to nearest even
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+// Four int8 cache bytes -> four exact f16 values.  Each byte x becomes the f16
+// 1024 + (x + 128) by pairing (x ^ 0x80) with the exponent byte 0x64, then
+// 1152 is subtracted (exact in f16).
+__device__ __forceinline__ void i8x4_to_f16(uint32_t w, half2_t& lo, half2_t& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  const half2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  lo = __builtin_bit_cast(half2_t, a) - bias;
+  hi = __builtin_bit_cast(half2_t, b) - bias;
+}
+
+// Four e4m3fn bytes -> four exact f16 values (gfx950 OCP fp8 conversion).
+__device__ __forceinline__ void e4m3x4_to_f16(uint32_t w, half2_t& lo, half2_t& hi) {
+  lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+}
+
+template <bool FP8>
+__device__ __forceinline__ half8_t bytes8_to_f16(uint32_t w0, uint32_t w1) {
+  half2_t a, b, c, d;
+  if constexpr (FP8) {
+    e4m3x4_to_f16(w0, a, b);
+    e4m3x4_to_f16(w1, c, d);
+  } else {
+    i8x4_to_f16(w0, a, b);
+    i8x4_to_f16(w1, c, d);
+  }
+  half8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+// 16-byte-chunk XOR swizzle of a 64-row LDS tile with ROWB bytes per row.
+// For ROWB = 128 two rows span the 64 banks; keys k and k' that one 16-lane
+// MFMA operand read touches at the same chunk land on distinct bank groups.
+// For ROWB = 64 or 576 (576 = 4 mod 16 bank groups) four rows interleave and
+// only the low two chunk bits are permuted.  The map is an involution.
+template <int ROWB>
+__device__ __forceinline__ int swz(int chunk, int row) {
+  if constexpr (ROWB == 128) {
+    return chunk ^ (((row >> 1) & 7) ^ ((row >> 2) & 4));
+  } else {
+    const int qd = row >> 2;
+    return chunk ^ ((qd ^ ((qd >> 2) << 1)) & 3);
+  }
+}
+
+// Page-table address function shared by the attention loads and the debug
+// gather: key -> (physical page, slot) -> row address (FlashInfer
+// persistent.cuh prefetch_offest; XQA KVTilePartLoader::loadPages).
+__device__ __forceinline__ int page_of(const int32_t* table_row, int key, int page_shift) {
+  return table_row[key >> page_shift];
+}
+__device__ __forceinline__ const uint8_t* paged_row(const uint8_t* cache, int page, int key,
+                                                    int page_shift, int g, int64_t s_page,
+                                                    int64_t s_head, int64_t s_tok) {
+  const int slot = key & ((1 << page_shift) - 1);
+  return cache + (int64_t)page * s_page + (int64_t)g * s_head + (int64_t)slot * s_tok;
+}
+
+// Physical page of `key` among the (at most four) pages pp0..pp3 of a 64-key
+// tile whose first page index is pg0.  Plain value selects: no indexing.
+__device__ __forceinline__ int pick_page(int key, int page_shift, int pg0, int pp0, int pp1,
+                                         int pp2, int pp3) {
+  const int j = (key >> page_shift) - pg0;
+  int r = pp0;
+  r = j == 1 ? pp1 : r;
+  r = j == 2 ? pp2 : r;
+  r = j == 3 ? pp3 : r;
+  return r;
+}
+
+// 64 lanes x 16 bytes from global memory straight into LDS: lane l's bytes land
+// at lds_base + 16*l.  lds_base goes through M0 (saved and restored here, the
+// compiler treats M0 as reserved).
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
+// A global load whose completion wait is part of the same asm block, so the
+// compiler does not add a vmcnt(0) wait at some later join point.
+__device__ __forceinline__ int load_i32_sync(const int32_t* ptr) {
+  int v;
+  asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(ptr) : "memory");
+  return v;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ float row_max4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float row_sum4(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ kernel --
+//
+// Template parameters: head dims, cache format, NT 16-row MFMA tiles per wave,
+// NW waves per workgroup (they split the rows and share every KV tile), SHARED
+// (V = prefix of the K row), HILO (Q is split into f16 hi + lo parts because
+// its values carry per-channel scales or come from fp32; a bf16 query with
+// per-head or per-tensor scales is exact in f16 and needs one part), NSTAGE
+// (KV tiles staged in LDS; NSTAGE - 1 tiles are in flight while one is used).
+//
+// The LDS DMA is issued with inline assembly and its completion is tracked
+// with explicit s_waitcnt vmcnt(N): the compiler would otherwise drain every
+// outstanding DMA before each LDS access and serialize the pipeline.  No other
+// vector-memory instruction is issued inside the main loop except the rare
+// refill of the page-id window, after which the compiler drains everything.
+
+template <int DQK, int DV, bool FP8, int NT, int NW, bool SHARED, bool HILO, int NSTAGE>
+__global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
+  constexpr int ROWS_W = 16 * NT;
+  constexpr int ROWS = ROWS_W * NW;
+  constexpr int KROW = DQK;                       // bytes per K row in LDS
+  constexpr int VROW = SHARED ? DQK : DV;         // bytes per V row in LDS
+  constexpr int KTILE = TK * KROW;
+  constexpr int VTILE = SHARED ? 0 : TK * VROW;
+  constexpr int STAGE = KTILE + VTILE;
+  constexpr int KCH = KTILE / 16;                 // 16-byte chunks per K tile
+  constexpr int VCH = VTILE / 16;
+  constexpr int KCPR = KROW / 16;                 // chunks per K row
+  constexpr int VCPR = VROW / 16;
+  constexpr int KPAIRS = DQK / 64;                // pairs of 32-wide k-steps
+  constexpr int MD = DV / 16;                     // 16-dim output tiles
+  constexpr int K_DMA = (KCH + 64 * NW - 1) / (64 * NW);
+  constexpr int V_DMA = (VCH + 64 * NW - 1) / (64 * NW);
+  constexpr int DMA_PER_TILE = K_DMA + V_DMA;     // exact for NW == 1
+  static_assert(DQK % 64 == 0 && DV % 16 == 0, "head dims");
+  static_assert(KCH % 64 == 0 && VCH % 64 == 0, "tile chunks");
+  static_assert(NSTAGE == 2 || NW == 1, "deep pipelines are single-wave (per-wave DMA counts)");
+  static_assert(DMA_PER_TILE * (NSTAGE - 2) <= 63, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;
+  const int b = blockIdx.z;
+  const int g = blockIdx.y;
+  const int rt = p.row_tiles - 1 - (int)(blockIdx.x / p.max_chunks);  // long row tiles first
+  const int c = (int)(blockIdx.x % p.max_chunks);
+
+  int n, tok0;
+  if (p.cu_seqlens_q) {
+    tok0 = p.cu_seqlens_q[b];
+    n = p.cu_seqlens_q[b + 1] - tok0;
+  } else {
+    n = p.q_len_uniform;
+    tok0 = b * n;
+  }
+  const int G = p.group;
+  const int rows_total = n * G;
+  const int row0 = rt * ROWS;
+  if (row0 >= rows_total) return;
+  const int L = p.seq_lens_kv[b];
+  const int T = L + n;
+  int kv_lo = 0, kv_hi = T, n_chunks = 1;
+  if (p.chunk_size > 0) {
+    n_chunks = (T + p.chunk_size - 1) / p.chunk_size;
+    if (c >= n_chunks) return;
+    kv_lo = c * p.chunk_size;
+    kv_hi = min(T, kv_lo + p.chunk_size);
+  } else if (c > 0) {
+    return;
+  }
+  const bool split = n_chunks > 1;
+  const int last_tok = (min(rows_total, row0 + ROWS) - 1) / G;
+  const int first_tok = row0 / G;
+  const int key_end = p.causal ? min(kv_hi, L + last_tok + 1) : kv_hi;
+  const int mask_from = p.causal ? min(kv_hi, L + first_tok + 1) : kv_hi;  // keys >= this need masks
+  const int n_tiles = key_end > kv_lo ? (key_end - kv_lo + TK - 1) / TK : 0;
+
+  const int32_t* table_row = p.block_table + (int64_t)b * p.max_pages_per_seq;
+  const int H_q = p.num_q_heads;
+  const int mode = p.scale_mode;
+  const bool fold_channel = mode == PA_SCALE_PER_CHANNEL;
+  // uniform K / V scales (per head or per tensor); per-channel ones are loaded as vectors
+  const float k_uniform = fold_channel ? 1.f : p.k_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
+  const float v_uniform = fold_channel ? 1.f : p.v_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
+
+  // ---- page-id window: lane l holds the physical page of page index pw_base + l ----
+  const int page_shift = p.page_shift;
+  const int last_page = n_tiles > 0 ? (key_end - 1) >> page_shift : 0;  // never read past it
+  int pw_base = -(1 << 30);
+  int pw_val = 0;
+
+  // ---- KV tile loader: 16-byte chunks, lane-consecutive in LDS ----
+  const uint32_t smem_base = lds_addr(smem);
+  auto issue_tile = [&](int tile, int stage) {
+    const int kbase = kv_lo + tile * TK;
+    const int pg0 = kbase >> page_shift;
+    const int pg_last = min(pg0 + 3, last_page);
+    if (pg0 < pw_base || pg_last > pw_base + 63) {
+      // Refill the window (drains the DMA queue; once per 64 pages).
+      pw_base = pg0;
+      pw_val = load_i32_sync(table_row + min(pg0 + lane, last_page));
+    }
+    // up to four pages per 64-key tile (page_size >= 16); one when page_size >= 64
+    const int pp0 = __builtin_amdgcn_readlane(pw_val, pg0 - pw_base);
+    const bool one_page = page_shift >= 6;
+    int pp1 = pp0, pp2 = pp0, pp3 = pp0;
+    if (!one_page) {
+      pp1 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 1, pg_last) - pw_base);
+      pp2 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 2, pg_last) - pw_base);
+      pp3 = __builtin_amdgcn_readlane(pw_val, pg_last - pw_base);
+    }
+    const uint32_t kdst = smem_base + stage * STAGE;
+#pragma unroll
+    for (int j = 0; j < K_DMA; ++j) {
+      const int blk = j * NW + wave;
+      if (blk * 64 < KCH) {
+        const int ch = blk * 64 + lane;
+        const int row = ch / KCPR;
+        const int pos = ch % KCPR;
+        const int key = min(kbase + row, key_end - 1);
+        const uint8_t* src = paged_row(p.k_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3), key, page_shift, g, p.k_stride_page,
+                                       p.k_stride_head, p.k_stride_token) +
+                             swz<KROW>(pos, row) * 16;
+        dma16(src, kdst + blk * 1024);
+      }
+    }
+    if constexpr (!SHARED) {
+      const uint32_t vdst = kdst + KTILE;
+#pragma unroll
+      for (int j = 0; j < V_DMA; ++j) {
+        const int blk = j * NW + wave;
+        if (blk * 64 < VCH) {
+          const int ch = blk * 64 + lane;
+          const int row = ch / VCPR;
+          const int pos = ch % VCPR;
+          const int key = min(kbase + row, key_end - 1);
+          const uint8_t* src = paged_row(p.v_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3), key, page_shift, g, p.v_stride_page,
+                                         p.v_stride_head, p.v_stride_token) +
+                               swz<VROW>(pos, row) * 16;
+          dma16(src, vdst + blk * 1024);
+        }
+      }
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s)
+    if (s < n_tiles) issue_tile(s, s);
+
+  // ---- Q^T operand (B of S^T = K Q^T) ----
+  // k-step 2s covers dims 64s + 16*grp + [0,8), k-step 2s+1 dims 64s + 16*grp + [8,16).
+  // A row is multiplied by a power of two 2^k that puts its largest element in
+  // [2^14, 2^15), so f16 keeps full relative precision; per-channel K scales and
+  // sm_scale*log2(e) are folded into Q in that case (then hi + lo parts keep
+  // the products exact to ~2^-22), otherwise they multiply S^T in fp32.
+  half8_t qf[NT][2 * KPAIRS];
+  half8_t ql[HILO ? NT : 1][HILO ? 2 * KPAIRS : 1];
+  float row_mult[NT];
+  int row_tok[NT], row_head[NT];
+  bool row_ok[NT];
+  auto load_q16 = [&](int64_t qoff, int d0, float* x) {
+    if (p.q_is_f32) {
+      const float4_t* src = (const float4_t*)((const float*)p.q + qoff + d0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float4_t f = src[v];
+        x[4 * v] = f[0]; x[4 * v + 1] = f[1]; x[4 * v + 2] = f[2]; x[4 * v + 3] = f[3];
+      }
+    } else {
+      const uint4_t* src = (const uint4_t*)((const uint16_t*)p.q + qoff + d0);
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const uint4_t u = src[v];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[8 * v + 2 * e] = bf16_to_f32((uint16_t)(u[e] & 0xffffu));
+          x[8 * v + 2 * e + 1] = bf16_to_f32((uint16_t)(u[e] >> 16));
+        }
+      }
+    }
+    if (fold_channel) {
+      const float4_t* sc = (const float4_t*)(p.k_scale + (int64_t)g * DQK + d0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float4_t f = sc[v];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * v + e] *= p.qk_mult * f[e];
+      }
+    }
+  };
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = row0 + wave * ROWS_W + nt * 16 + l16;
+    row_ok[nt] = r < rows_total;
+    const int t = row_ok[nt] ? r / G : 0;
+    row_tok[nt] = t;
+    row_head[nt] = g * G + (row_ok[nt] ? r % G : 0);
+    const int64_t qoff = (int64_t)(tok0 + t) * p.q_row_stride + (int64_t)row_head[nt] * DQK;
+    float amax = 0.f;
+    if (row_ok[nt]) {
+      for (int s = 0; s < KPAIRS; ++s) {
+        float x[16];
+        load_q16(qoff, 64 * s + 16 * grp, x);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
+      }
+    }
+    amax = row_max4(amax);
+    int ex = 0;
+    if (amax > 0.f) (void)frexpf(amax, &ex);     // amax < 2^ex
+    const int k2 = min(max(15 - ex, -120), 120);
+    const float up = ldexpf(1.f, k2);
+    row_mult[nt] = ldexpf(1.f, -k2) * (fold_channel ? 1.f : p.qk_mult * k_uniform);
+#pragma unroll
+    for (int s = 0; s < KPAIRS; ++s) {
+      float x[16];
+      if (row_ok[nt]) {
+        load_q16(qoff, 64 * s + 16 * grp, x);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float v = x[e] * up;
+        const _Float16 hi = (_Float16)v;
+        qf[nt][2 * s + e / 8][e % 8] = hi;
+        if constexpr (HILO) ql[nt][2 * s + e / 8][e % 8] = (_Float16)(v - (float)hi);
+      }
+    }
+  }
+
+  // per-channel V scales of this lane's output dims (16*md + 4*grp + i)
+  float4_t vsc[MD];
+  if (fold_channel) {
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+      vsc[md] = *(const float4_t*)(p.v_scale + (int64_t)g * DV + md * 16 + grp * 4);
+  } else {
+#pragma unroll
+    for (int md = 0; md < MD; ++md) vsc[md] = float4_t{v_uniform, v_uniform, v_uniform, v_uniform};
+  }
+
+  float4_t o[MD][NT];
+  float m_run[NT], l_run[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) o[md][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const int stage = it % NSTAGE;
+    // tile `it` has landed once at most (tiles issued after it) * DMA_PER_TILE DMAs remain
+    if constexpr (NSTAGE == 2) {
+      wait_vmcnt<0>();
+    } else {
+      const int ahead = min(NSTAGE - 2, n_tiles - 1 - it);
+      if (ahead <= 0) wait_vmcnt<0>();
+      else if (ahead == 1) wait_vmcnt<DMA_PER_TILE>();
+      else if (ahead == 2) wait_vmcnt<(NSTAGE >= 4 ? 2 : 1) * DMA_PER_TILE>();
+      else wait_vmcnt<(NSTAGE >= 5 ? 3 : 1) * DMA_PER_TILE>();
+    }
+    if constexpr (NW > 1) __syncthreads();
+    if (it + NSTAGE - 1 < n_tiles) issue_tile(it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
+    const uint8_t* ks = smem + stage * STAGE;
+    const uint8_t* vs = SHARED ? ks : ks + KTILE;
+    const int kbase = kv_lo + it * TK;
+
+    // ---- S^T = K Q^T ----
+    float4_t s[4][NT];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) s[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sp = 0; sp < KPAIRS; ++sp) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int row = mt * 16 + l16;
+        const uint4_t raw =
+            *(const uint4_t*)(ks + row * KROW + swz<KROW>(4 * sp + grp, row) * 16);
+        const half8_t a0 = bytes8_to_f16<FP8>(raw[0], raw[1]);
+        const half8_t a1 = bytes8_to_f16<FP8>(raw[2], raw[3]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qf[nt][2 * sp], s[mt][nt], 0, 0, 0);
+          if constexpr (HILO)
+            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, ql[nt][2 * sp], s[mt][nt], 0, 0, 0);
+          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qf[nt][2 * sp + 1], s[mt][nt], 0, 0, 0);
+          if constexpr (HILO)
+            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, ql[nt][2 * sp + 1], s[mt][nt], 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- mask + online softmax (log2 domain) ----
+    const bool need_mask = kbase + TK > mask_from;
+    half8_t pb[2][NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if (need_mask) {
+        const int lim = p.causal ? min(kv_hi, L + row_tok[nt] + 1) : kv_hi;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kbase + mt * 16 + grp * 4 + i;
+            if (key >= lim) s[mt][nt][i] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][nt][i]);
+      mx = row_max4(mx) * row_mult[nt];
+      const float m_new = fmaxf(m_run[nt], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
+      m_run[nt] = m_new;
+      float ls = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[mt][nt][i], row_mult[nt], -m_use));
+          s[mt][nt][i] = e;
+          ls += e;
+        }
+      l_run[nt] = l_run[nt] * alpha + ls;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) o[md][nt] *= alpha;
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[ks2][nt][i] = (_Float16)s[2 * ks2][nt][i];
+          pb[ks2][nt][4 + i] = (_Float16)s[2 * ks2 + 1][nt][i];
+        }
+    }
+
+    // ---- O^T += V^T P^T ----
+    // tr8 read: lanes 2j, 2j+1 of a 16-lane group give the two 8-byte halves of key
+    // row kappa(grp, j); lane i then holds V[kappa(grp, j)][16*md + i], j = 0..7.
+    const int jr = l16 >> 1;
+    const int hlf = lane & 1;
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      const int vrow = 32 * ks2 + (jr < 4 ? 4 * grp + jr : 16 + 4 * grp + (jr - 4));
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const uint8_t* addr = vs + vrow * VROW + swz<VROW>(md, vrow) * 16 + hlf * 8;
+        const int2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) int2_t*)(addr));
+        const half8_t a = bytes8_to_f16<FP8>((uint32_t)raw[0], (uint32_t)raw[1]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[ks2][nt], o[md][nt], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: normalize, V scale, write final or partial ----
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float lt = row_sum4(l_run[nt]);
+    const bool ok = row_ok[nt];
+    const int tok = tok0 + row_tok[nt];
+    const int h = row_head[nt];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse_nat = lt > 0.f ? (m_run[nt] + __log2f(lt)) * LN2F : -INFINITY;
+    if (!ok) continue;
+    float* prow = split ? p.part_o + (((int64_t)tok * p.max_chunks + c) * H_q + h) * DV : nullptr;
+    uint16_t* orow = p.out + ((int64_t)tok * H_q + h) * DV;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      const int d = md * 16 + grp * 4;
+      const float4_t sv = vsc[md];
+      float4_t v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = o[md][nt][i] * inv * sv[i];
+      if (split) {
+        *(float4_t*)(prow + d) = v;
+      } else {
+        const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *(int2_t*)(orow + d) = int2_t{(int)w0, (int)w1};
+      }
+    }
+    if (grp == 0) {
+      if (split) p.part_lse[((int64_t)tok * p.max_chunks + c) * H_q + h] = lse_nat;
+      else if (p.lse) p.lse[(int64_t)tok * H_q + h] = lse_nat;
+    }
+  }
+}
+
+// ------------------------------------------------------------------- merge --
+// One group of DV/4 lanes per (token, head) row; each lane owns 4 channels.
+template <int DV>
+__global__ __launch_bounds__(256) void split_merge_kernel(MergeParams p) {
+  constexpr int LPR = DV / 4;
+  constexpr int RPB = 256 / LPR;
+  const int b = blockIdx.y;
+  int n, tok0;
+  if (p.cu_seqlens_q) {
+    tok0 = p.cu_seqlens_q[b];
+    n = p.cu_seqlens_q[b + 1] - tok0;
+  } else {
+    n = p.q_len_uniform;
+    tok0 = b * n;
+  }
+  const int T = p.seq_lens_kv[b] + n;
+  const int nc = min((T + p.chunk_size - 1) / p.chunk_size, p.max_chunks);
+  if (nc <= 1) return;
+  const int pair = blockIdx.x * RPB + (int)threadIdx.x / LPR;
+  if (pair >= n * p.num_q_heads) return;
+  const int t = pair / p.num_q_heads;
+  const int h = pair % p.num_q_heads;
+  const int lane = threadIdx.x % LPR;
+  const int64_t tok = tok0 + t;
+  const float* lrow = p.part_lse + tok * p.max_chunks * p.num_q_heads + h;
+  float M = -INFINITY;
+  for (int cc = 0; cc < nc; ++cc) M = fmaxf(M, lrow[(int64_t)cc * p.num_q_heads]);
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  const float* orow = p.part_o + (tok * p.max_chunks * p.num_q_heads + h) * DV + lane * 4;
+  for (int cc = 0; cc < nc; ++cc) {
+    const float lc = lrow[(int64_t)cc * p.num_q_heads];
+    if (lc == -INFINITY) continue;
+    const float w = __expf(lc - M);
+    den += w;
+    const float4_t v = *(const float4_t*)(orow + (int64_t)cc * p.num_q_heads * DV);
+    acc += w * v;
+  }
+  const float inv = 1.f / den;
+  uint16_t* dst = p.out + (tok * p.num_q_heads + h) * DV + lane * 4;
+  const uint32_t w0 = (uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16);
+  const uint32_t w1 = (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16);
+  *(int2_t*)dst = int2_t{(int)w0, (int)w1};
+  if (p.lse && lane == 0) p.lse[tok * p.num_q_heads + h] = M + __logf(den);
+}
+
+// ------------------------------------------------------------ debug gather --
+// grid (ceil(t_max / 4), H_kv, B), 64 threads: 16 lanes per key row, 4 rows.
+__global__ __launch_bounds__(64) void gather_kernel(GatherParams p) {
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int key = blockIdx.x * 4 + (threadIdx.x >> 4);
+  const int T = p.seq_lens_kv[b] + p.q_lens[b];
+  if (key >= T) return;
+  const int32_t* table_row = p.block_table + (int64_t)b * p.max_pages_per_seq;
+  const int page = page_of(table_row, key, p.page_shift);
+  const uint8_t* src = paged_row(p.k_cache, page, key, p.page_shift, g, p.k_stride_page,
+                                 p.k_stride_head, p.k_stride_token);
+  uint8_t* dst = p.dst + (((int64_t)b * p.num_kv_heads + g) * p.t_max + key) * p.head_dim;
+  for (int d = (threadIdx.x & 15) * 16; d < p.head_dim; d += 256)
+    *(uint4_t*)(dst + d) = *(const uint4_t*)(src + d);
+}
+
+// ------------------------------------------------------------------ launch --
+
+namespace {
+template <int DQK, int DV, bool FP8, int NT, int NW, bool SHARED, bool HILO, int NSTAGE>
+hipError_t launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((paged_attn_kernel<DQK, DV, FP8, NT, NW, SHARED, HILO, NSTAGE>), grid,
+                     dim3(64 * NW), 0, stream, p);
+  return hipGetLastError();
+}
+
+using LaunchFn = hipError_t (*)(const AttnParams&, dim3, hipStream_t);
+
+struct Entry {
+  AttnConfig cfg;
+  LaunchFn fn;
+};
+
+#define PA_ENTRY(DQK, DV, FP8, NT, NW, SH, HL, NS) \
+  Entry{AttnConfig{DQK, DV, FP8, SH, NT, NW, HL, NS}, &launch_one<DQK, DV, FP8, NT, NW, SH, HL, NS>}
+
+// decode-shaped (one wave, deep pipeline) and append-shaped (4 waves x 32 rows)
+#define PA_SET(DQK, DV, FP8, HL)                                                              \
+  PA_ENTRY(DQK, DV, FP8, 1, 1, false, HL, 3), PA_ENTRY(DQK, DV, FP8, 2, 1, false, HL, 3),     \
+      PA_ENTRY(DQK, DV, FP8, 3, 1, false, HL, 3), PA_ENTRY(DQK, DV, FP8, 4, 1, false, HL, 3), \
+      PA_ENTRY(DQK, DV, FP8, 2, 4, false, HL, 2)
+
+const Entry kTable[] = {
+    PA_SET(64, 64, false, false),   PA_SET(64, 64, false, true),
+    PA_SET(64, 64, true, false),    PA_SET(64, 64, true, true),
+    PA_SET(128, 128, false, false), PA_SET(128, 128, false, true),
+    PA_SET(128, 128, true, false),  PA_SET(128, 128, true, true),
+    PA_ENTRY(576, 512, true, 1, 8, true, false, 2),  PA_ENTRY(576, 512, true, 1, 8, true, true, 2),
+    PA_ENTRY(576, 512, false, 1, 8, true, false, 2), PA_ENTRY(576, 512, false, 1, 8, true, true, 2),
+};
+
+const Entry* find_entry(const AttnConfig& c) {
+  for (const Entry& e : kTable)
+    if (e.cfg.dqk == c.dqk && e.cfg.dv == c.dv && e.cfg.fp8 == c.fp8 &&
+        e.cfg.shared_kv == c.shared_kv && e.cfg.nt == c.nt && e.cfg.nw == c.nw &&
+        e.cfg.hilo == c.hilo && e.cfg.nstage == c.nstage)
+      return &e;
+  return nullptr;
+}
+}  // namespace
+
+bool attention_supported(const AttnConfig& cfg) { return find_entry(cfg) != nullptr; }
+
+hipError_t launch_attention(const AttnConfig& cfg, const AttnParams& p, dim3 grid,
+                            hipStream_t stream) {
+  const Entry* e = find_entry(cfg);
+  if (!e) return hipErrorInvalidValue;
+  return e->fn(p, grid, stream);
+}
+
+hipError_t launch_merge(int dv, const MergeParams& p, int batch, int max_q_len,
+                        hipStream_t stream) {
+  const int rows = max_q_len * p.num_q_heads;
+  switch (dv) {
+#define PA_MERGE_CASE(D)                                                                     \
+  case D: {                                                                                  \
+    constexpr int RPB = 256 / (D / 4);                                                       \
+    dim3 grid((rows + RPB - 1) / RPB, batch);                                                \
+    hipLaunchKernelGGL(split_merge_kernel<D>, grid, dim3(256), 0, stream, p);                \
+    return hipGetLastError();                                                                \
+  }
+    PA_MERGE_CASE(64)
+    PA_MERGE_CASE(128)
+    PA_MERGE_CASE(256)
+    PA_MERGE_CASE(512)
+    PA_MERGE_CASE(1024)
+#undef PA_MERGE_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gather(const GatherParams& p, int batch, hipStream_t stream) {
+  dim3 grid((p.t_max + 3) / 4, p.num_kv_heads, batch);
+  hipLaunchKernelGGL(gather_kernel, grid, dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace pa

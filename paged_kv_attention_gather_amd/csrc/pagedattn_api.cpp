@@ -1,0 +1,360 @@
+// C-ABI front end of libpagedattn.so: argument validation, specialization
+// choice, grid and workspace sizing, then launches on the caller's stream.
+// Every check runs before the first launch, so a failing call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "pa_internal.h"
+#include "pagedattn.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int32_t ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+int log2_exact(int64_t x) {
+  if (x <= 0 || (x & (x - 1)) != 0) return -1;
+  int s = 0;
+  while ((int64_t(1) << s) < x) ++s;
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kTileKeys = 64;
+
+// Shape checks shared by the workspace query and the attention calls.
+int32_t check_problem(const pa_problem* p) {
+  if (!p) return fail(PA_ERR_INVALID_ARG, "problem is NULL");
+  if (p->batch < 0) return fail(PA_ERR_INVALID_ARG, "batch %d < 0", p->batch);
+  if (p->batch > 65535) return fail(PA_ERR_UNSUPPORTED, "batch %d > 65535", p->batch);
+  if (p->num_q_heads <= 0 || p->num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID_ARG, "head counts must be positive (H_q=%d, H_kv=%d)",
+                p->num_q_heads, p->num_kv_heads);
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "H_q=%d is not a multiple of H_kv=%d", p->num_q_heads,
+                p->num_kv_heads);
+  if (p->num_kv_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "H_kv %d > 65535", p->num_kv_heads);
+  const bool dims_ok = (p->head_dim_qk == 64 && p->head_dim_v == 64) ||
+                       (p->head_dim_qk == 128 && p->head_dim_v == 128) ||
+                       (p->head_dim_qk == 576 && p->head_dim_v == 512);
+  if (p->head_dim_qk <= 0 || p->head_dim_v <= 0)
+    return fail(PA_ERR_INVALID_ARG, "head dims must be positive");
+  if (!dims_ok)
+    return fail(PA_ERR_UNSUPPORTED, "head dims (%d, %d) not compiled; supported: (64,64), (128,128), (576,512)",
+                p->head_dim_qk, p->head_dim_v);
+  if (log2_exact(p->page_size) < 0 || p->page_size < 16 || p->page_size > 1024)
+    return fail(PA_ERR_UNSUPPORTED, "page_size %d must be a power of two in [16, 1024]", p->page_size);
+  if (p->num_pages <= 0 || p->max_pages_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_pages and max_pages_per_seq must be positive");
+  if (p->max_q_len < 0 || p->max_kv_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "max_q_len / max_kv_len must be >= 0");
+  if (p->chunk_size < 0 || p->chunk_size % kTileKeys != 0)
+    return fail(PA_ERR_UNSUPPORTED, "chunk_size %d must be 0 or a positive multiple of %d",
+                p->chunk_size, kTileKeys);
+  return PA_OK;
+}
+
+int64_t max_chunks_of(const pa_problem* p) {
+  if (p->chunk_size <= 0) return 1;
+  return std::max<int64_t>(1, ceil_div((int64_t)p->max_kv_len + p->max_q_len, p->chunk_size));
+}
+
+struct WorkspaceLayout {
+  size_t part_o_bytes, part_lse_offset, part_lse_bytes, total;
+};
+
+WorkspaceLayout workspace_layout(const pa_problem* p, int64_t total_q) {
+  WorkspaceLayout w{0, 0, 0, 0};
+  if (p->chunk_size <= 0) return w;
+  const int64_t mc = max_chunks_of(p);
+  w.part_o_bytes = (size_t)total_q * mc * p->num_q_heads * p->head_dim_v * sizeof(float);
+  w.part_lse_offset = (w.part_o_bytes + 255) & ~size_t(255);
+  w.part_lse_bytes = (size_t)total_q * mc * p->num_q_heads * sizeof(float);
+  w.total = w.part_lse_offset + w.part_lse_bytes;
+  return w;
+}
+
+int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_t total_q,
+                         const void* q, const void* k_cache, const void* v_cache,
+                         const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
+                         const int32_t* seq_lens_kv, const int32_t* block_table, void* out,
+                         float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t st = check_problem(p);
+  if (st != PA_OK) return st;
+  if (decode) {
+    if (q_len < 1 || q_len > 64) return fail(PA_ERR_INVALID_ARG, "decode q_len %d not in [1, 64]", q_len);
+    if (p->max_q_len < q_len)
+      return fail(PA_ERR_INVALID_ARG, "max_q_len %d < q_len %d", p->max_q_len, q_len);
+  } else {
+    if (total_q < 0) return fail(PA_ERR_INVALID_ARG, "total_q %lld < 0", (long long)total_q);
+    if (p->batch > 0 && !cu_seqlens_q) return fail(PA_ERR_INVALID_ARG, "cu_seqlens_q is NULL");
+  }
+  if (p->batch == 0 || total_q == 0 || p->max_q_len == 0) return ok();  // nothing to compute
+  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !seq_lens_kv || !block_table || !out)
+    return fail(PA_ERR_INVALID_ARG, "a required device pointer is NULL");
+  if (p->q_dtype != PA_DTYPE_BF16 && p->q_dtype != PA_DTYPE_F32)
+    return fail(PA_ERR_UNSUPPORTED, "q_dtype %d: only BF16 and F32 queries", p->q_dtype);
+  if (p->kv_dtype != PA_DTYPE_I8 && p->kv_dtype != PA_DTYPE_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype %d: only I8 and FP8_E4M3 caches", p->kv_dtype);
+  if (p->scale_mode < PA_SCALE_PER_TENSOR || p->scale_mode > PA_SCALE_PER_CHANNEL)
+    return fail(PA_ERR_INVALID_ARG, "scale_mode %d", p->scale_mode);
+  if (p->causal != 0 && p->causal != 1) return fail(PA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!(p->sm_scale > 0.f) || !std::isfinite(p->sm_scale))
+    return fail(PA_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const int esize = p->q_dtype == PA_DTYPE_F32 ? 4 : 2;
+  if (p->q_row_stride < (int64_t)p->num_q_heads * p->head_dim_qk)
+    return fail(PA_ERR_INVALID_ARG, "q_row_stride %lld < H_q * D_qk", (long long)p->q_row_stride);
+  if ((p->q_row_stride * esize) % 16 != 0 || !aligned16(q))
+    return fail(PA_ERR_INVALID_ARG, "q and its row stride must be 16-byte aligned");
+  const int64_t ks[3] = {p->k_stride_page, p->k_stride_head, p->k_stride_token};
+  const int64_t vs[3] = {p->v_stride_page, p->v_stride_head, p->v_stride_token};
+  for (int i = 0; i < 3; ++i) {
+    if (ks[i] <= 0 || vs[i] <= 0) return fail(PA_ERR_INVALID_ARG, "cache strides must be positive");
+    if (ks[i] % 16 != 0 || vs[i] % 16 != 0)
+      return fail(PA_ERR_INVALID_ARG, "cache strides must be multiples of 16 bytes");
+  }
+  if (p->k_stride_token < p->head_dim_qk || p->v_stride_token < p->head_dim_v)
+    return fail(PA_ERR_INVALID_ARG, "token stride shorter than the head dim");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(PA_ERR_INVALID_ARG, "k_cache, v_cache and out must be 16-byte aligned");
+  const bool shared = p->head_dim_qk == 576;
+  if (shared) {
+    if (v_cache != k_cache || p->v_stride_page != p->k_stride_page ||
+        p->v_stride_head != p->k_stride_head || p->v_stride_token != p->k_stride_token)
+      return fail(PA_ERR_UNSUPPORTED,
+                  "head dims (576, 512) need the shared latent layout: v_cache == k_cache, same strides");
+  }
+  const int64_t G = p->num_q_heads / p->num_kv_heads;
+  const int64_t rows_max = (int64_t)(decode ? q_len : p->max_q_len) * G;
+
+  pa::AttnConfig cfg{};
+  cfg.dqk = p->head_dim_qk;
+  cfg.dv = p->head_dim_v;
+  cfg.fp8 = p->kv_dtype == PA_DTYPE_FP8_E4M3;
+  cfg.shared_kv = shared;
+  cfg.hilo = p->scale_mode == PA_SCALE_PER_CHANNEL || p->q_dtype == PA_DTYPE_F32;
+  if (shared) {
+    cfg.nt = 1;
+    cfg.nw = 8;
+    cfg.nstage = 2;
+  } else if (rows_max <= 64) {
+    cfg.nt = (int)ceil_div(rows_max, 16);
+    cfg.nw = 1;
+    cfg.nstage = 3;
+  } else {
+    cfg.nt = 2;
+    cfg.nw = 4;
+    cfg.nstage = 2;
+  }
+  if (!pa::attention_supported(cfg))
+    return fail(PA_ERR_UNSUPPORTED, "no compiled kernel for this configuration");
+  const int64_t rows_per_wg = 16LL * cfg.nt * cfg.nw;
+  const int64_t row_tiles = ceil_div(rows_max, rows_per_wg);
+  const int64_t max_chunks = max_chunks_of(p);
+  if (row_tiles * max_chunks > 0x7fffffffLL)
+    return fail(PA_ERR_UNSUPPORTED, "grid too large (%lld row tiles x %lld chunks)",
+                (long long)row_tiles, (long long)max_chunks);
+
+  const WorkspaceLayout wl = workspace_layout(p, total_q);
+  if (wl.total > 0) {
+    if (!workspace) return fail(PA_ERR_WORKSPACE_TOO_SMALL, "split-KV needs a workspace of %zu bytes", wl.total);
+    if (workspace_bytes < wl.total)
+      return fail(PA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, wl.total);
+    if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+
+  pa::AttnParams ap{};
+  ap.q = q;
+  ap.k_cache = static_cast<const uint8_t*>(k_cache);
+  ap.v_cache = static_cast<const uint8_t*>(v_cache);
+  ap.k_scale = k_scale;
+  ap.v_scale = v_scale;
+  ap.cu_seqlens_q = decode ? nullptr : cu_seqlens_q;
+  ap.seq_lens_kv = seq_lens_kv;
+  ap.block_table = block_table;
+  ap.out = static_cast<uint16_t*>(out);
+  ap.lse = lse;
+  ap.part_o = wl.total ? static_cast<float*>(workspace) : nullptr;
+  ap.part_lse = wl.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.part_lse_offset) : nullptr;
+  ap.q_row_stride = p->q_row_stride;
+  ap.k_stride_page = p->k_stride_page;
+  ap.k_stride_head = p->k_stride_head;
+  ap.k_stride_token = p->k_stride_token;
+  ap.v_stride_page = p->v_stride_page;
+  ap.v_stride_head = p->v_stride_head;
+  ap.v_stride_token = p->v_stride_token;
+  ap.num_q_heads = p->num_q_heads;
+  ap.group = (int32_t)G;
+  ap.page_shift = log2_exact(p->page_size);
+  ap.max_pages_per_seq = p->max_pages_per_seq;
+  ap.q_len_uniform = decode ? q_len : 0;
+  ap.chunk_size = p->chunk_size;
+  ap.max_chunks = (int32_t)max_chunks;
+  ap.row_tiles = (int32_t)row_tiles;
+  ap.q_is_f32 = p->q_dtype == PA_DTYPE_F32;
+  ap.scale_mode = p->scale_mode;
+  ap.causal = p->causal;
+  ap.qk_mult = p->sm_scale * 1.4426950408889634f;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  dim3 grid((unsigned)(row_tiles * max_chunks), (unsigned)p->num_kv_heads, (unsigned)p->batch);
+  hipError_t e = pa::launch_attention(cfg, ap, grid, s);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+  if (p->chunk_size > 0) {
+    pa::MergeParams mp{};
+    mp.part_o = ap.part_o;
+    mp.part_lse = ap.part_lse;
+    mp.cu_seqlens_q = ap.cu_seqlens_q;
+    mp.seq_lens_kv = seq_lens_kv;
+    mp.out = ap.out;
+    mp.lse = lse;
+    mp.q_len_uniform = ap.q_len_uniform;
+    mp.num_q_heads = p->num_q_heads;
+    mp.chunk_size = p->chunk_size;
+    mp.max_chunks = ap.max_chunks;
+    e = pa::launch_merge(p->head_dim_v, mp, p->batch, p->max_q_len, s);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t paged_attn_workspace_size(const pa_problem* prob, int32_t total_q) {
+  if (check_problem(prob) != PA_OK || total_q < 0) return (size_t)-1;
+  return workspace_layout(prob, total_q).total;
+}
+
+int32_t paged_attn_append(const pa_problem* prob, int32_t total_q, const void* q,
+                          const void* k_cache, const void* v_cache, const float* k_scale,
+                          const float* v_scale, const int32_t* cu_seqlens_q,
+                          const int32_t* seq_lens_kv, const int32_t* block_table, void* out,
+                          float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_common(prob, false, 0, total_q, q, k_cache, v_cache, k_scale, v_scale,
+                          cu_seqlens_q, seq_lens_kv, block_table, out, lse, workspace,
+                          workspace_bytes, stream);
+}
+
+int32_t paged_attn_decode(const pa_problem* prob, int32_t q_len, const void* q,
+                          const void* k_cache, const void* v_cache, const float* k_scale,
+                          const float* v_scale, const int32_t* seq_lens_kv,
+                          const int32_t* block_table, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!prob) return fail(PA_ERR_INVALID_ARG, "problem is NULL");
+  const int64_t total_q = (int64_t)prob->batch * q_len;
+  return attention_common(prob, true, q_len, total_q, q, k_cache, v_cache, k_scale, v_scale,
+                          nullptr, seq_lens_kv, block_table, out, lse, workspace, workspace_bytes,
+                          stream);
+}
+
+int32_t split_kv_merge(const float* partial_o, const float* partial_lse,
+                       const int32_t* cu_seqlens_q, const int32_t* seq_lens_kv,
+                       int32_t q_len_uniform, int32_t batch, int32_t total_q, int32_t max_q_len,
+                       int32_t num_q_heads, int32_t head_dim_v, int32_t chunk_size,
+                       int32_t max_chunks, void* out, float* lse, void* stream) {
+  if (batch < 0 || batch > 65535 || total_q < 0 || max_q_len < 0 || num_q_heads <= 0)
+    return fail(PA_ERR_INVALID_ARG, "bad sizes (batch=%d total_q=%d max_q_len=%d H_q=%d)", batch,
+                total_q, max_q_len, num_q_heads);
+  if (head_dim_v != 64 && head_dim_v != 128 && head_dim_v != 256 && head_dim_v != 512 &&
+      head_dim_v != 1024)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim_v %d not in {64, 128, 256, 512, 1024}", head_dim_v);
+  if (chunk_size <= 0 || max_chunks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "chunk_size and max_chunks must be positive");
+  if (!cu_seqlens_q && q_len_uniform <= 0)
+    return fail(PA_ERR_INVALID_ARG, "need cu_seqlens_q or q_len_uniform > 0");
+  if (!cu_seqlens_q && q_len_uniform > max_q_len)
+    return fail(PA_ERR_INVALID_ARG, "q_len_uniform %d > max_q_len %d", q_len_uniform, max_q_len);
+  if (batch == 0 || total_q == 0 || max_q_len == 0) return ok();
+  if (!partial_o || !partial_lse || !seq_lens_kv || !out)
+    return fail(PA_ERR_INVALID_ARG, "a required device pointer is NULL");
+  if (!aligned16(partial_o) || !aligned16(out))
+    return fail(PA_ERR_INVALID_ARG, "partial_o and out must be 16-byte aligned");
+  pa::MergeParams mp{};
+  mp.part_o = partial_o;
+  mp.part_lse = partial_lse;
+  mp.cu_seqlens_q = cu_seqlens_q;
+  mp.seq_lens_kv = seq_lens_kv;
+  mp.out = static_cast<uint16_t*>(out);
+  mp.lse = lse;
+  mp.q_len_uniform = cu_seqlens_q ? 0 : q_len_uniform;
+  mp.num_q_heads = num_q_heads;
+  mp.chunk_size = chunk_size;
+  mp.max_chunks = max_chunks;
+  hipError_t e = pa::launch_merge(head_dim_v, mp, batch, max_q_len, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t pa_gather_debug(const pa_problem* prob, const void* k_cache, const int32_t* block_table,
+                        const int32_t* seq_lens_kv, const int32_t* q_lens, int32_t t_max,
+                        uint8_t* dst, void* stream) {
+  int32_t st = check_problem(prob);
+  if (st != PA_OK) return st;
+  if (t_max < 0) return fail(PA_ERR_INVALID_ARG, "t_max %d < 0", t_max);
+  if ((int64_t)t_max > (int64_t)prob->max_pages_per_seq * prob->page_size)
+    return fail(PA_ERR_INVALID_ARG, "t_max %d exceeds the block table capacity", t_max);
+  if (prob->batch == 0 || t_max == 0) return ok();
+  if (!k_cache || !block_table || !seq_lens_kv || !q_lens || !dst)
+    return fail(PA_ERR_INVALID_ARG, "a required device pointer is NULL");
+  if (!aligned16(k_cache) || !aligned16(dst) || prob->k_stride_page % 16 || prob->k_stride_head % 16 ||
+      prob->k_stride_token % 16 || prob->k_stride_page <= 0 || prob->k_stride_head <= 0 ||
+      prob->k_stride_token <= 0)
+    return fail(PA_ERR_INVALID_ARG, "k_cache, dst and cache strides must be 16-byte aligned and positive");
+  pa::GatherParams gp{};
+  gp.k_cache = static_cast<const uint8_t*>(k_cache);
+  gp.block_table = block_table;
+  gp.seq_lens_kv = seq_lens_kv;
+  gp.q_lens = q_lens;
+  gp.dst = dst;
+  gp.k_stride_page = prob->k_stride_page;
+  gp.k_stride_head = prob->k_stride_head;
+  gp.k_stride_token = prob->k_stride_token;
+  gp.num_kv_heads = prob->num_kv_heads;
+  gp.head_dim = prob->head_dim_qk;
+  gp.page_shift = log2_exact(prob->page_size);
+  gp.max_pages_per_seq = prob->max_pages_per_seq;
+  gp.t_max = t_max;
+  hipError_t e = pa::launch_gather(gp, prob->batch, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "gather launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* pa_status_string(int32_t status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    default: return "PA_ERR_UNKNOWN";
+  }
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,205 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small workloads are compared on every output element; the full-size workloads
+(the launch configuration bench.py times) are compared on sampled requests,
+which the oracle evaluates one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import announce, compare, need_gpu, token_rows
+from workloads import config_workload, make_workload, small_variant
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, **kw):
+    from paged_kv_attention_gather_amd.harness import DeviceProblem
+    dp = DeviceProblem(w, **kw)
+    dp.run()
+    return dp, dp.outputs()
+
+
+# ------------------------------------------------------------ page gather --
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_gather_bit_exact_small(idx):
+    torch = need_gpu()
+    import paged_kv_attention_gather_amd as P
+    from paged_kv_attention_gather_amd.harness import DeviceProblem
+    w = small_variant(idx)
+    announce(f"gather small_variant({idx}) {w.name}")
+    dp = DeviceProblem(w)
+    T = w.kv_tokens()
+    t_max = int(T.max())
+    dst = torch.zeros((w.batch, w.num_kv_heads, t_max, w.head_dim_qk), dtype=torch.uint8, device="cuda")
+    P.pa_gather_debug(dp.prob, dp.k_cache, dp.block_table, dp.seq_lens_kv, dp.q_lens, t_max, dst)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy()
+    ref = oracle.gather_bytes(w)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("idx", [2, 5])
+def test_gather_bit_exact_full(idx):
+    torch = need_gpu()
+    import paged_kv_attention_gather_amd as P
+    from paged_kv_attention_gather_amd.harness import DeviceProblem
+    w = config_workload(idx)
+    announce(f"gather config_workload({idx}) {w.name}")
+    dp = DeviceProblem(w)
+    T = w.kv_tokens()
+    t_max = int(T.max())
+    dst = torch.zeros((w.batch, w.num_kv_heads, t_max, w.head_dim_qk), dtype=torch.uint8, device="cuda")
+    P.pa_gather_debug(dp.prob, dp.k_cache, dp.block_table, dp.seq_lens_kv, dp.q_lens, t_max, dst)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy()
+    for b in range(0, w.batch, max(1, w.batch // 8)):
+        for g in range(w.num_kv_heads):
+            ref = oracle.gather_rows(w.k_cache, w.block_table[b], g, int(T[b]), w.page_size, w.head_dim_qk)
+            assert np.array_equal(got[b, g, :T[b]], ref), (b, g)
+
+
+# --------------------------------------------------- attention, small sizes --
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_small_variant_parity(idx):
+    need_gpu()
+    w = small_variant(idx)
+    announce(f"attention small_variant({idx}) {w.name} chunk={w.chunk_size}")
+    _, (out, lse) = _run(w)
+    O_ref, lse_ref = oracle.attention(w)
+    compare(out, lse, O_ref, lse_ref, what=w.name)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_poisoned_tail_is_never_read(idx):
+    need_gpu()
+    w = small_variant(idx, poison_tail=True)
+    announce(f"attention poisoned tail small_variant({idx})")
+    _, (out, lse) = _run(w)
+    O_ref, lse_ref = oracle.attention(w)
+    compare(out, lse, O_ref, lse_ref, what=w.name + "+poison")
+
+
+def test_config1_tiny_append_full():
+    need_gpu()
+    w = config_workload(1)
+    announce("attention config_workload(1) tiny append")
+    _, (out, lse) = _run(w)
+    O_ref, lse_ref = oracle.attention(w)
+    compare(out, lse, O_ref, lse_ref, what=w.name)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    torch = need_gpu()
+    w = small_variant(4)
+    announce("determinism small_variant(4)")
+    from paged_kv_attention_gather_amd.harness import DeviceProblem
+    dp = DeviceProblem(w)
+    dp.run()
+    a = dp.outputs()
+    dp.out.zero_()
+    dp.run()
+    b = dp.outputs()
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ------------------------------------------------------------- edge cases --
+
+def _edge(name, **kw):
+    base = dict(name=name, seed=abs(hash(name)) % 10000, num_q_heads=8, num_kv_heads=2, head_dim_qk=128,
+                head_dim_v=128, page_size=64, q_dtype="bf16", kv_dtype="i8", scale_mode="channel",
+                causal=True, sm_scale=1 / math.sqrt(128), chunk_size=0, decode=False)
+    base.update(kw)
+    return make_workload(**base)
+
+
+EDGE_CASES = {
+    "append_zero_len_request": dict(q_lens=[5, 0, 70, 1], seq_lens_kv=[10, 33, 0, 129]),
+    "append_noncausal": dict(q_lens=[7, 90], seq_lens_kv=[100, 3], causal=False),
+    "append_chunked": dict(q_lens=[100, 37], seq_lens_kv=[300, 500], chunk_size=128),
+    "append_chunk_equals_page": dict(q_lens=[3, 80], seq_lens_kv=[200, 40], chunk_size=64),
+    "append_chunk_beyond_T": dict(q_lens=[4, 9], seq_lens_kv=[20, 70], chunk_size=4096),
+    "append_g1": dict(num_q_heads=4, num_kv_heads=4, q_lens=[33, 6], seq_lens_kv=[65, 190]),
+    "append_page16_head_scale": dict(page_size=16, scale_mode="head", q_lens=[20, 3], seq_lens_kv=[47, 100]),
+    # per-channel scales sized so |V| <= 448 * 0.008 < 4, the range where a bf16
+    # output can meet max-abs 1e-2 (half an ulp of bf16 at 4 is 7.8e-3)
+    "append_fp8_channel": dict(kv_dtype="fp8_e4m3", q_lens=[12, 80], seq_lens_kv=[64, 250],
+                               scale_range=(0.0005, 0.008)),
+    "append_f32_query": dict(q_dtype="f32", q_lens=[2, 19], seq_lens_kv=[31, 64]),
+    "decode_q8_g8": dict(num_q_heads=16, num_kv_heads=2, q_lens=[8, 8, 8], seq_lens_kv=[0, 500, 1300],
+                         decode=True, chunk_size=512),
+    "decode_page16_chunk64": dict(page_size=16, q_lens=[1, 1], seq_lens_kv=[77, 3], decode=True, chunk_size=64),
+    "decode_page256": dict(page_size=256, q_lens=[3, 3], seq_lens_kv=[700, 1], decode=True, chunk_size=256),
+    "decode_d64_fp8_tensor": dict(head_dim_qk=64, head_dim_v=64, kv_dtype="fp8_e4m3", scale_mode="tensor",
+                                  q_lens=[2, 2, 2], seq_lens_kv=[5, 140, 700], decode=True, chunk_size=256),
+    "decode_noncausal_drafts": dict(q_lens=[4, 4], seq_lens_kv=[60, 300], decode=True, causal=False,
+                                    chunk_size=128),
+    "mla_int8_g16_q2": dict(num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
+                            shared_kv=True, scale_mode="tensor", q_lens=[2, 2], seq_lens_kv=[63, 900],
+                            decode=True, chunk_size=256),
+}
+
+
+@pytest.mark.parametrize("case", sorted(EDGE_CASES))
+def test_edge_case_parity(case):
+    need_gpu()
+    w = _edge(case, **EDGE_CASES[case])
+    announce(f"edge case {case}")
+    _, (out, lse) = _run(w)
+    O_ref, lse_ref = oracle.attention(w)
+    n = int(w.q_lens.sum())
+    compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what=case)
+
+
+# ------------------------------------------------------------------ merge --
+
+def test_split_kv_merge_against_oracle_partials():
+    torch = need_gpu()
+    import paged_kv_attention_gather_amd as P
+    w = _edge("merge", q_lens=[3, 1, 6], seq_lens_kv=[700, 64, 1500], chunk_size=256)
+    announce("split_kv_merge alone")
+    C = w.chunk_size
+    T = w.kv_tokens()
+    mc = int(math.ceil((int(w.seq_lens_kv.max()) + int(w.q_lens.max())) / C))
+    po = np.zeros((w.total_q, mc, w.num_q_heads, w.head_dim_v), np.float32)
+    pl = np.full((w.total_q, mc, w.num_q_heads), -np.inf, np.float32)
+    for b in range(w.batch):
+        Oc, lc = oracle.chunk_partials(w, b, C)
+        q0, q1 = int(w.cu_seqlens_q[b]), int(w.cu_seqlens_q[b + 1])
+        po[q0:q1, :Oc.shape[1]] = Oc
+        pl[q0:q1, :lc.shape[1]] = lc
+    dev = torch.device("cuda")
+    out = torch.zeros((w.total_q, w.num_q_heads, w.head_dim_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.zeros((w.total_q, w.num_q_heads), dtype=torch.float32, device=dev)
+    P.split_kv_merge(torch.from_numpy(po).to(dev), torch.from_numpy(pl).to(dev),
+                     torch.from_numpy(w.cu_seqlens_q).to(dev), torch.from_numpy(w.seq_lens_kv).to(dev),
+                     0, w.batch, w.total_q, int(w.q_lens.max()), w.num_q_heads, w.head_dim_v, C, mc,
+                     out, lse)
+    torch.cuda.synchronize()
+    O_ref, lse_ref = oracle.attention(w)
+    rows = token_rows(w, [b for b in range(w.batch) if -(-int(T[b]) // C) > 1])
+    compare(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64),
+            O_ref, lse_ref, rows=rows, what="merge")
+
+
+# ----------------------------------------------------- full-size workloads --
+
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+def test_full_config_sampled_parity(idx):
+    need_gpu()
+    w = config_workload(idx)
+    announce(f"attention config_workload({idx}) {w.name} (sampled requests)")
+    _, (out, lse) = _run(w)
+    rng = np.random.default_rng(1000 + idx)
+    T = w.kv_tokens()
+    pick = {int(np.argmax(T)), int(np.argmin(T))}
+    pick.update(rng.choice(w.batch, size=min(w.batch, 4), replace=False).tolist())
+    reqs = sorted(pick)
+    O_ref, lse_ref = oracle.attention(w, requests=reqs)
+    rows = token_rows(w, reqs)
+    compare(out, lse, O_ref, lse_ref, rows=rows, what=f"{w.name} requests {reqs}")
