@@ -1,0 +1,164 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry
+point, and rejects invalid arguments before touching the GPU (no compute call
+is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_attention_gather_amd as P
+from paged_kv_attention_gather_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+FAKE = 0x100000  # aligned, never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from paged_kv_attention_gather_amd import build
+        build.build()
+    return P.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(L.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    names = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED",
+             3: "PA_ERR_WORKSPACE_TOO_SMALL", 4: "PA_ERR_HIP"}
+    for code, name in names.items():
+        assert lib.pa_status_string(code).decode() == name
+
+
+def base_problem(**over):
+    f = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=64,
+             num_pages=64, max_pages_per_seq=16, max_q_len=4, max_kv_len=900, q_row_stride=8 * 128,
+             k_stride_page=2 * 64 * 128, k_stride_head=64 * 128, k_stride_token=128,
+             v_stride_page=2 * 64 * 128, v_stride_head=64 * 128, v_stride_token=128,
+             q_dtype=L.DTYPE_BF16, kv_dtype=L.DTYPE_I8, scale_mode=L.SCALE_PER_CHANNEL, causal=1,
+             sm_scale=0.088, chunk_size=256)
+    f.update(over)
+    return P.make_problem(**f)
+
+
+def test_workspace_size_formula(lib):
+    prob = base_problem()
+    total_q = 8
+    mc = -(-(900 + 4) // 256)
+    po = total_q * mc * 8 * 128 * 4
+    expect = (po + 255) // 256 * 256 + total_q * mc * 8 * 4
+    assert P.workspace_size(prob, total_q) == expect
+    assert P.workspace_size(base_problem(chunk_size=0), total_q) == 0
+
+
+def _decode(prob, q_len=1, workspace=None, ws_bytes=0, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, lens=FAKE, table=FAKE, out=FAKE, lse=None)
+    p.update(ptrs)
+    return L.lib().paged_attn_decode(ctypes.byref(prob), q_len, p["q"], p["k"], p["v"], p["ks"], p["vs"],
+                                     p["lens"], p["table"], p["out"], p["lse"], workspace, ws_bytes, None)
+
+
+def _append(prob, total_q=8, workspace=None, ws_bytes=0, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, cu=FAKE, lens=FAKE, table=FAKE, out=FAKE, lse=None)
+    p.update(ptrs)
+    return L.lib().paged_attn_append(ctypes.byref(prob), total_q, p["q"], p["k"], p["v"], p["ks"], p["vs"],
+                                     p["cu"], p["lens"], p["table"], p["out"], p["lse"], workspace, ws_bytes,
+                                     None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(num_kv_heads=3), L.PA_ERR_INVALID_ARG),                 # H_q % H_kv != 0
+    (dict(num_q_heads=0), L.PA_ERR_INVALID_ARG),
+    (dict(head_dim_qk=96, head_dim_v=96), L.PA_ERR_UNSUPPORTED),
+    (dict(page_size=48), L.PA_ERR_UNSUPPORTED),                   # not a power of two
+    (dict(page_size=8), L.PA_ERR_UNSUPPORTED),                    # below 16
+    (dict(chunk_size=100), L.PA_ERR_UNSUPPORTED),                 # not a multiple of 64
+    (dict(q_dtype=7), L.PA_ERR_UNSUPPORTED),
+    (dict(kv_dtype=L.DTYPE_BF16), L.PA_ERR_UNSUPPORTED),
+    (dict(scale_mode=5), L.PA_ERR_INVALID_ARG),
+    (dict(sm_scale=0.0), L.PA_ERR_INVALID_ARG),
+    (dict(sm_scale=float("nan")), L.PA_ERR_INVALID_ARG),
+    (dict(causal=2), L.PA_ERR_INVALID_ARG),
+    (dict(q_row_stride=100), L.PA_ERR_INVALID_ARG),               # < H_q * D and misaligned
+    (dict(k_stride_token=120), L.PA_ERR_INVALID_ARG),             # not 16-byte multiple
+    (dict(batch=-1), L.PA_ERR_INVALID_ARG),
+    (dict(batch=70000), L.PA_ERR_UNSUPPORTED),
+])
+def test_invalid_problems_are_rejected(lib, over, status):
+    assert _decode(base_problem(**over)) == status
+    assert lib.pa_last_error().decode()
+
+
+def test_null_and_misaligned_pointers(lib):
+    prob = base_problem(chunk_size=0)
+    assert _decode(prob, q=None) == L.PA_ERR_INVALID_ARG
+    assert _decode(prob, out=FAKE + 2) == L.PA_ERR_INVALID_ARG
+    assert _append(prob, cu=None) == L.PA_ERR_INVALID_ARG
+    assert lib.paged_attn_decode(None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0,
+                                 None) == L.PA_ERR_INVALID_ARG
+
+
+def test_decode_q_len_bounds(lib):
+    assert _decode(base_problem(max_q_len=80), q_len=65) == L.PA_ERR_INVALID_ARG
+    assert _decode(base_problem(), q_len=0) == L.PA_ERR_INVALID_ARG
+    assert _decode(base_problem(max_q_len=1), q_len=2) == L.PA_ERR_INVALID_ARG
+
+
+def test_workspace_too_small(lib):
+    prob = base_problem()
+    need = P.workspace_size(prob, 2)
+    assert _decode(prob, q_len=1) == L.PA_ERR_WORKSPACE_TOO_SMALL
+    assert _decode(prob, q_len=1, workspace=FAKE, ws_bytes=need - 1) == L.PA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_mla_layout_requires_shared_rows(lib):
+    prob = base_problem(head_dim_qk=576, head_dim_v=512, num_q_heads=16, num_kv_heads=1,
+                        q_row_stride=16 * 576, k_stride_page=64 * 576, k_stride_head=64 * 576,
+                        k_stride_token=576, v_stride_page=64 * 576, v_stride_head=64 * 576,
+                        v_stride_token=576, chunk_size=0)
+    assert _decode(prob, v=FAKE + 4096) == L.PA_ERR_UNSUPPORTED
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert _decode(base_problem(batch=0)) == L.PA_OK
+    assert _append(base_problem(batch=0), total_q=0) == L.PA_OK
+
+
+def test_merge_validation(lib):
+    m = lib.split_kv_merge
+    assert m(FAKE, FAKE, None, FAKE, 0, 2, 2, 1, 8, 128, 256, 4, FAKE, None, None) == L.PA_ERR_INVALID_ARG
+    assert m(FAKE, FAKE, None, FAKE, 1, 2, 2, 1, 8, 96, 256, 4, FAKE, None, None) == L.PA_ERR_UNSUPPORTED
+    assert m(FAKE, FAKE, None, FAKE, 1, 2, 2, 1, 8, 128, 0, 4, FAKE, None, None) == L.PA_ERR_INVALID_ARG
+    assert m(FAKE, FAKE, None, FAKE, 1, 0, 0, 1, 8, 128, 256, 4, FAKE, None, None) == L.PA_OK
+
+
+def test_gather_validation(lib):
+    prob = base_problem()
+    g = lib.pa_gather_debug
+    assert g(ctypes.byref(prob), FAKE, FAKE, FAKE, FAKE, -1, FAKE, None) == L.PA_ERR_INVALID_ARG
+    assert g(ctypes.byref(prob), None, FAKE, FAKE, FAKE, 64, FAKE, None) == L.PA_ERR_INVALID_ARG
+    assert g(ctypes.byref(prob), FAKE, FAKE, FAKE, FAKE, 16 * 64 + 1, FAKE, None) == L.PA_ERR_INVALID_ARG
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        L.lib()
