@@ -71,6 +71,37 @@ __device__ __forceinline__ void e4m3x4_to_f16(uint32_t w, half2_t& lo, half2_t& 
   hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
 }
 
+// Four int8 cache bytes -> four f16 values 1152 + x (exact): (x ^ 0x80) = x + 128
+// paired with the exponent byte 0x64 reads as 1024 + (x + 128).  The constant
+// offset is removed exactly after the MFMA (a per-row logit bias for K, a
+// per-channel shift of the normalized output for V).
+__device__ __forceinline__ void i8x4_to_f16_off(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+}
+
+// Eight cache bytes -> eight f16 MFMA operand values: e4m3fn exactly, or int8
+// as 1152 + x.
+template <bool FP8>
+__device__ __forceinline__ half8_t bytes8_to_op(uint32_t w0, uint32_t w1) {
+  if constexpr (FP8) {
+    half2_t a, b, c, d;
+    e4m3x4_to_f16(w0, a, b);
+    e4m3x4_to_f16(w1, c, d);
+    half8_t r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+  } else {
+    uint32_t a, b, c, d;
+    i8x4_to_f16_off(w0, a, b);
+    i8x4_to_f16_off(w1, c, d);
+    const uint4_t u = {a, b, c, d};
+    return __builtin_bit_cast(half8_t, u);
+  }
+}
+
 template <bool FP8>
 __device__ __forceinline__ half8_t bytes8_to_f16(uint32_t w0, uint32_t w1) {
   half2_t a, b, c, d;
@@ -140,6 +171,17 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
       : "memory");
 }
 
+// Same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
+__device__ __forceinline__ void dma16_s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
 // A global load whose completion wait is part of the same asm block, so the
 // compiler does not add a vmcnt(0) wait at some later join point.
 __device__ __forceinline__ int load_i32_sync(const int32_t* ptr) {
@@ -203,6 +245,8 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
   constexpr int K_DMA = (KCH + 64 * NW - 1) / (64 * NW);
   constexpr int V_DMA = (VCH + 64 * NW - 1) / (64 * NW);
   constexpr int DMA_PER_TILE = K_DMA + V_DMA;     // exact for NW == 1
+  // int8 operands reach the MFMA as 1152 + x (see i8x4_to_f16_off)
+  constexpr float KV_OFF = FP8 ? 0.f : 1152.f;
   static_assert(DQK % 64 == 0 && DV % 16 == 0, "head dims");
   static_assert(KCH % 64 == 0 && VCH % 64 == 0, "tile chunks");
   static_assert(NSTAGE == 2 || NW == 1, "deep pipelines are single-wave (per-wave DMA counts)");
@@ -253,18 +297,33 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
   const int H_q = p.num_q_heads;
   const int mode = p.scale_mode;
   const bool fold_channel = mode == PA_SCALE_PER_CHANNEL;
-  // uniform K / V scales (per head or per tensor); per-channel ones are loaded as vectors
-  const float k_uniform = fold_channel ? 1.f : p.k_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
-  const float v_uniform = fold_channel ? 1.f : p.v_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
 
-  // ---- page-id window: lane l holds the physical page of page index pw_base + l ----
+  // ---- KV tile loader ----
+  // Page-id window: lane l holds the physical page of page index pw_base + l.
   const int page_shift = p.page_shift;
   const int last_page = n_tiles > 0 ? (key_end - 1) >> page_shift : 0;  // never read past it
   int pw_base = -(1 << 30);
   int pw_val = 0;
-
-  // ---- KV tile loader: 16-byte chunks, lane-consecutive in LDS ----
+  // With pages of >= 64 keys a tile lies in one page: the page base is a scalar
+  // and every lane's source offset inside it is fixed (unless the tile is clamped).
+  const bool one_page = page_shift >= 6;
+  const bool fast_addr = one_page && (int64_t)TK * p.k_stride_token < (1LL << 30) &&
+                         (int64_t)TK * p.v_stride_token < (1LL << 30);
+  uint32_t koff[K_DMA], voff[V_DMA > 0 ? V_DMA : 1];
+#pragma unroll
+  for (int j = 0; j < K_DMA; ++j) {
+    const int ch = (j * NW + wave) * 64 + lane;
+    const int row = ch / KCPR;
+    koff[j] = (uint32_t)(row * p.k_stride_token + swz<KROW>(ch % KCPR, row) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < V_DMA; ++j) {
+    const int ch = (j * NW + wave) * 64 + lane;
+    const int row = ch / VCPR;
+    voff[j] = (uint32_t)(row * p.v_stride_token + swz<VROW>(ch % VCPR, row) * 16);
+  }
   const uint32_t smem_base = lds_addr(smem);
+
   auto issue_tile = [&](int tile, int stage) {
     const int kbase = kv_lo + tile * TK;
     const int pg0 = kbase >> page_shift;
@@ -274,16 +333,32 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
       pw_base = pg0;
       pw_val = load_i32_sync(table_row + min(pg0 + lane, last_page));
     }
-    // up to four pages per 64-key tile (page_size >= 16); one when page_size >= 64
     const int pp0 = __builtin_amdgcn_readlane(pw_val, pg0 - pw_base);
-    const bool one_page = page_shift >= 6;
+    const uint32_t kdst = smem_base + stage * STAGE;
+    const uint32_t vdst = kdst + KTILE;
+    if (fast_addr && kbase + TK <= key_end) {
+      const int slot0 = kbase & ((1 << page_shift) - 1);
+      const uint8_t* kb = p.k_cache + (int64_t)pp0 * p.k_stride_page + (int64_t)g * p.k_stride_head +
+                          (int64_t)slot0 * p.k_stride_token;
+#pragma unroll
+      for (int j = 0; j < K_DMA; ++j)
+        if ((j * NW + wave) * 64 < KCH) dma16_s(koff[j], kb, kdst + (j * NW + wave) * 1024);
+      if constexpr (!SHARED) {
+        const uint8_t* vb = p.v_cache + (int64_t)pp0 * p.v_stride_page +
+                            (int64_t)g * p.v_stride_head + (int64_t)slot0 * p.v_stride_token;
+#pragma unroll
+        for (int j = 0; j < V_DMA; ++j)
+          if ((j * NW + wave) * 64 < VCH) dma16_s(voff[j], vb, vdst + (j * NW + wave) * 1024);
+      }
+      return;
+    }
+    // general path: up to four pages per tile (page_size >= 16), clamped rows
     int pp1 = pp0, pp2 = pp0, pp3 = pp0;
     if (!one_page) {
       pp1 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 1, pg_last) - pw_base);
       pp2 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 2, pg_last) - pw_base);
       pp3 = __builtin_amdgcn_readlane(pw_val, pg_last - pw_base);
     }
-    const uint32_t kdst = smem_base + stage * STAGE;
 #pragma unroll
     for (int j = 0; j < K_DMA; ++j) {
       const int blk = j * NW + wave;
@@ -292,14 +367,14 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
         const int row = ch / KCPR;
         const int pos = ch % KCPR;
         const int key = min(kbase + row, key_end - 1);
-        const uint8_t* src = paged_row(p.k_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3), key, page_shift, g, p.k_stride_page,
-                                       p.k_stride_head, p.k_stride_token) +
+        const uint8_t* src = paged_row(p.k_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3),
+                                       key, page_shift, g, p.k_stride_page, p.k_stride_head,
+                                       p.k_stride_token) +
                              swz<KROW>(pos, row) * 16;
         dma16(src, kdst + blk * 1024);
       }
     }
     if constexpr (!SHARED) {
-      const uint32_t vdst = kdst + KTILE;
 #pragma unroll
       for (int j = 0; j < V_DMA; ++j) {
         const int blk = j * NW + wave;
@@ -308,8 +383,9 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
           const int row = ch / VCPR;
           const int pos = ch % VCPR;
           const int key = min(kbase + row, key_end - 1);
-          const uint8_t* src = paged_row(p.v_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3), key, page_shift, g, p.v_stride_page,
-                                         p.v_stride_head, p.v_stride_token) +
+          const uint8_t* src = paged_row(p.v_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3),
+                                         key, page_shift, g, p.v_stride_page, p.v_stride_head,
+                                         p.v_stride_token) +
                                swz<VROW>(pos, row) * 16;
           dma16(src, vdst + blk * 1024);
         }
@@ -317,19 +393,23 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
     }
   };
 
+  // First tiles go out before the query prologue so both latencies overlap.
 #pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < n_tiles) issue_tile(s, s);
+  for (int st = 0; st < NSTAGE - 1; ++st)
+    if (st < n_tiles) issue_tile(st, st);
 
   // ---- Q^T operand (B of S^T = K Q^T) ----
   // k-step 2s covers dims 64s + 16*grp + [0,8), k-step 2s+1 dims 64s + 16*grp + [8,16).
   // A row is multiplied by a power of two 2^k that puts its largest element in
-  // [2^14, 2^15), so f16 keeps full relative precision; per-channel K scales and
-  // sm_scale*log2(e) are folded into Q in that case (then hi + lo parts keep
-  // the products exact to ~2^-22), otherwise they multiply S^T in fp32.
+  // [2^14, 2^15), so f16 keeps full relative precision.  Per-channel K scales
+  // and sm_scale*log2(e) are folded into Q in that case (then hi + lo parts keep
+  // the products exact to ~2^-22); otherwise they multiply S^T in fp32.
+  const float k_uniform = fold_channel ? 1.f : p.k_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
+  const float v_uniform = fold_channel ? 1.f : p.v_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
   half8_t qf[NT][2 * KPAIRS];
   half8_t ql[HILO ? NT : 1][HILO ? 2 * KPAIRS : 1];
-  float row_mult[NT];
+  float row_mult[NT];  // raw S^T -> log2-domain logits
+  float kbias[NT];     // log2-domain logit offset from the int8 operand offset
   int row_tok[NT], row_head[NT];
   bool row_ok[NT];
   auto load_q16 = [&](int64_t qoff, int d0, float* x) {
@@ -372,9 +452,9 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
     const int64_t qoff = (int64_t)(tok0 + t) * p.q_row_stride + (int64_t)row_head[nt] * DQK;
     float amax = 0.f;
     if (row_ok[nt]) {
-      for (int s = 0; s < KPAIRS; ++s) {
+      for (int sp = 0; sp < KPAIRS; ++sp) {
         float x[16];
-        load_q16(qoff, 64 * s + 16 * grp, x);
+        load_q16(qoff, 64 * sp + 16 * grp, x);
 #pragma unroll
         for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
       }
@@ -385,11 +465,12 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
     const int k2 = min(max(15 - ex, -120), 120);
     const float up = ldexpf(1.f, k2);
     row_mult[nt] = ldexpf(1.f, -k2) * (fold_channel ? 1.f : p.qk_mult * k_uniform);
+    float qsum = 0.f;
 #pragma unroll
-    for (int s = 0; s < KPAIRS; ++s) {
+    for (int sp = 0; sp < KPAIRS; ++sp) {
       float x[16];
       if (row_ok[nt]) {
-        load_q16(qoff, 64 * s + 16 * grp, x);
+        load_q16(qoff, 64 * sp + 16 * grp, x);
       } else {
 #pragma unroll
         for (int e = 0; e < 16; ++e) x[e] = 0.f;
@@ -398,21 +479,16 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
       for (int e = 0; e < 16; ++e) {
         const float v = x[e] * up;
         const _Float16 hi = (_Float16)v;
-        qf[nt][2 * s + e / 8][e % 8] = hi;
-        if constexpr (HILO) ql[nt][2 * s + e / 8][e % 8] = (_Float16)(v - (float)hi);
+        qf[nt][2 * sp + e / 8][e % 8] = hi;
+        qsum += (float)hi;
+        if constexpr (HILO) {
+          const _Float16 lo = (_Float16)(v - (float)hi);
+          ql[nt][2 * sp + e / 8][e % 8] = lo;
+          qsum += (float)lo;
+        }
       }
     }
-  }
-
-  // per-channel V scales of this lane's output dims (16*md + 4*grp + i)
-  float4_t vsc[MD];
-  if (fold_channel) {
-#pragma unroll
-    for (int md = 0; md < MD; ++md)
-      vsc[md] = *(const float4_t*)(p.v_scale + (int64_t)g * DV + md * 16 + grp * 4);
-  } else {
-#pragma unroll
-    for (int md = 0; md < MD; ++md) vsc[md] = float4_t{v_uniform, v_uniform, v_uniform, v_uniform};
+    kbias[nt] = KV_OFF * row_sum4(qsum) * row_mult[nt];
   }
 
   float4_t o[MD][NT];
@@ -424,7 +500,7 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
 #pragma unroll
     for (int md = 0; md < MD; ++md) o[md][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
-
+  const half2_t ones2 = {(_Float16)1.0f, (_Float16)1.0f};
 
   for (int it = 0; it < n_tiles; ++it) {
     const int stage = it % NSTAGE;
@@ -444,7 +520,7 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
     const uint8_t* vs = SHARED ? ks : ks + KTILE;
     const int kbase = kv_lo + it * TK;
 
-    // ---- S^T = K Q^T ----
+    // ---- S^T = K Q^T: 4 x NT independent accumulator chains ----
     float4_t s[4][NT];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -452,21 +528,28 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
       for (int nt = 0; nt < NT; ++nt) s[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sp = 0; sp < KPAIRS; ++sp) {
+      uint4_t raw[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const int row = mt * 16 + l16;
-        const uint4_t raw =
-            *(const uint4_t*)(ks + row * KROW + swz<KROW>(4 * sp + grp, row) * 16);
-        const half8_t a0 = bytes8_to_f16<FP8>(raw[0], raw[1]);
-        const half8_t a1 = bytes8_to_f16<FP8>(raw[2], raw[3]);
+        raw[mt] = *(const uint4_t*)(ks + row * KROW + swz<KROW>(4 * sp + grp, row) * 16);
+      }
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qf[nt][2 * sp], s[mt][nt], 0, 0, 0);
-          if constexpr (HILO)
-            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, ql[nt][2 * sp], s[mt][nt], 0, 0, 0);
-          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qf[nt][2 * sp + 1], s[mt][nt], 0, 0, 0);
-          if constexpr (HILO)
-            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, ql[nt][2 * sp + 1], s[mt][nt], 0, 0, 0);
+      for (int hk = 0; hk < 2; ++hk) {
+        half8_t a[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) a[mt] = bytes8_to_op<FP8>(raw[mt][2 * hk], raw[mt][2 * hk + 1]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], qf[nt][2 * sp + hk], s[mt][nt], 0, 0, 0);
+        if constexpr (HILO) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], ql[nt][2 * sp + hk], s[mt][nt], 0, 0, 0);
         }
       }
     }
@@ -474,6 +557,7 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
     // ---- mask + online softmax (log2 domain) ----
     const bool need_mask = kbase + TK > mask_from;
     half8_t pb[2][NT];
+    float alpha[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       if (need_mask) {
@@ -491,30 +575,41 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][nt][i]);
-      mx = row_max4(mx) * row_mult[nt];
+      mx = row_max4(mx) * row_mult[nt] - kbias[nt];
       const float m_new = fmaxf(m_run[nt], mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
+      alpha[nt] = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
       m_run[nt] = m_new;
-      float ls = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[mt][nt][i], row_mult[nt], -m_use));
-          s[mt][nt][i] = e;
-          ls += e;
-        }
-      l_run[nt] = l_run[nt] * alpha + ls;
-#pragma unroll
-      for (int md = 0; md < MD; ++md) o[md][nt] *= alpha;
+      const float nb = -(kbias[nt] + m_use);
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pb[ks2][nt][i] = (_Float16)s[2 * ks2][nt][i];
-          pb[ks2][nt][4 + i] = (_Float16)s[2 * ks2 + 1][nt][i];
+          pb[ks2][nt][i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[2 * ks2][nt][i], row_mult[nt], nb));
+          pb[ks2][nt][4 + i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[2 * ks2 + 1][nt][i], row_mult[nt], nb));
         }
+      // row sum of the f16 weights the MFMA actually sees.  (The pairs are built
+      // from vector elements: bit-casting uint4 lanes to half2 here makes this
+      // compiler reuse one register for all four dot products.)
+      float ls = 0.f;
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const half2_t pr = {pb[ks2][nt][2 * e], pb[ks2][nt][2 * e + 1]};
+          ls = __builtin_amdgcn_fdot2(pr, ones2, ls, false);
+        }
+      l_run[nt] = l_run[nt] * alpha[nt] + ls;
+    }
+    // rescale O only when some row maximum grew
+    bool grew = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) grew |= alpha[nt] != 1.f;
+    if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int md = 0; md < MD; ++md) o[md][nt] *= alpha[nt];
     }
 
     // ---- O^T += V^T P^T ----
@@ -530,7 +625,7 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
         const uint8_t* addr = vs + vrow * VROW + swz<VROW>(md, vrow) * 16 + hlf * 8;
         const int2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (__attribute__((address_space(3))) int2_t*)(addr));
-        const half8_t a = bytes8_to_f16<FP8>((uint32_t)raw[0], (uint32_t)raw[1]);
+        const half8_t a = bytes8_to_op<FP8>((uint32_t)raw[0], (uint32_t)raw[1]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[ks2][nt], o[md][nt], 0, 0, 0);
@@ -538,7 +633,17 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
     }
   }
 
-  // ---- epilogue: normalize, V scale, write final or partial ----
+  // ---- epilogue: normalize, remove the operand offset, V scale, write ----
+  // per-channel V scales of this lane's output dims (16*md + 4*grp + i)
+  float4_t vsc[MD];
+  if (fold_channel) {
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+      vsc[md] = *(const float4_t*)(p.v_scale + (int64_t)g * DV + md * 16 + grp * 4);
+  } else {
+#pragma unroll
+    for (int md = 0; md < MD; ++md) vsc[md] = float4_t{v_uniform, v_uniform, v_uniform, v_uniform};
+  }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float lt = row_sum4(l_run[nt]);
@@ -546,6 +651,7 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
     const int tok = tok0 + row_tok[nt];
     const int h = row_head[nt];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float off = lt > 0.f ? KV_OFF : 0.f;
     const float lse_nat = lt > 0.f ? (m_run[nt] + __log2f(lt)) * LN2F : -INFINITY;
     if (!ok) continue;
     float* prow = split ? p.part_o + (((int64_t)tok * p.max_chunks + c) * H_q + h) * DV : nullptr;
@@ -556,7 +662,7 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
       const float4_t sv = vsc[md];
       float4_t v;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = o[md][nt][i] * inv * sv[i];
+      for (int i = 0; i < 4; ++i) v[i] = fmaf(o[md][nt][i], inv, -off) * sv[i];
       if (split) {
         *(float4_t*)(prow + d) = v;
       } else {
@@ -655,10 +761,14 @@ struct Entry {
   Entry{AttnConfig{DQK, DV, FP8, SH, NT, NW, HL, NS}, &launch_one<DQK, DV, FP8, NT, NW, SH, HL, NS>}
 
 // decode-shaped (one wave, deep pipeline) and append-shaped (4 waves x 32 rows)
-#define PA_SET(DQK, DV, FP8, HL)                                                              \
-  PA_ENTRY(DQK, DV, FP8, 1, 1, false, HL, 3), PA_ENTRY(DQK, DV, FP8, 2, 1, false, HL, 3),     \
-      PA_ENTRY(DQK, DV, FP8, 3, 1, false, HL, 3), PA_ENTRY(DQK, DV, FP8, 4, 1, false, HL, 3), \
-      PA_ENTRY(DQK, DV, FP8, 2, 4, false, HL, 2)
+#ifndef PA_DECODE_NSTAGE
+#define PA_DECODE_NSTAGE 2
+#endif
+#define PA_DS PA_DECODE_NSTAGE
+#define PA_SET(DQK, DV, FP8, HL)                                                                  \
+  PA_ENTRY(DQK, DV, FP8, 1, 1, false, HL, PA_DS), PA_ENTRY(DQK, DV, FP8, 2, 1, false, HL, PA_DS), \
+      PA_ENTRY(DQK, DV, FP8, 3, 1, false, HL, PA_DS),                                             \
+      PA_ENTRY(DQK, DV, FP8, 4, 1, false, HL, PA_DS), PA_ENTRY(DQK, DV, FP8, 2, 4, false, HL, 2)
 
 const Entry kTable[] = {
     PA_SET(64, 64, false, false),   PA_SET(64, 64, false, true),
