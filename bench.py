@@ -3,8 +3,10 @@
 
 A step is one call of the C ABI (attention kernel + split-KV merge) over one
 batch of the synthetic workload, inputs resident in HBM.  Before every timed
-step the L2 and the 256 MB last-level cache are flushed (outside the events),
-so the KV bytes really come from HBM.  The default workload is the int8 decode
+step the L2 and the 256 MB last-level cache are flushed (outside the events)
+by READING a 1 GiB buffer, so the KV bytes really come from HBM and no dirty
+flush data is left to be written back while the step runs (a write-based
+flush costs a read kernel about a third of its bandwidth).  The default workload is the int8 decode
 case (B=64, q_len 1, 32/8 heads, D=128, page 64, KV lens U[512, 4096],
 per-channel scales, chunk 512): the one the decode KV-bandwidth metric is
 quoted on.  --config 1..5 selects another workload.
@@ -103,7 +105,20 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="skip the per-step cache flush")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
+
+    if args.copy_probe_mib:
+        import torch
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3}))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
@@ -123,11 +138,11 @@ def main():
     chunk = dp.prob.chunk_size
     kv_bytes, alg_bytes, flops = work_figures(w)
     stream = torch.cuda.current_stream()
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB
 
     def do_flush():
         if not args.no_flush:
-            flush.add_(1)
+            flush.max()  # read-only pass over 1 GiB
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

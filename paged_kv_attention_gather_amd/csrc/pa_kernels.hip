@@ -412,7 +412,26 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
   float kbias[NT];     // log2-domain logit offset from the int8 operand offset
   int row_tok[NT], row_head[NT];
   bool row_ok[NT];
-  auto load_q16 = [&](int64_t qoff, int d0, float* x) {
+  // Short heads keep the row and its per-channel scales in registers (one pass
+  // over global memory); long ones re-read the row after finding its maximum.
+  constexpr bool ONE_PASS = KPAIRS <= 2;
+  float ksc[ONE_PASS ? KPAIRS : 1][16];
+  if constexpr (ONE_PASS) {
+    if (fold_channel) {
+#pragma unroll
+      for (int sp = 0; sp < KPAIRS; ++sp) {
+        const float4_t* sc = (const float4_t*)(p.k_scale + (int64_t)g * DQK + 64 * sp + 16 * grp);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float4_t f = sc[v];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ksc[sp][4 * v + e] = p.qk_mult * f[e];
+        }
+      }
+    }
+  }
+  auto load_q16 = [&](int64_t qoff, int sp, float* x) {
+    const int d0 = 64 * sp + 16 * grp;
     if (p.q_is_f32) {
       const float4_t* src = (const float4_t*)((const float*)p.q + qoff + d0);
 #pragma unroll
@@ -433,12 +452,17 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
       }
     }
     if (fold_channel) {
-      const float4_t* sc = (const float4_t*)(p.k_scale + (int64_t)g * DQK + d0);
+      if constexpr (ONE_PASS) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float4_t f = sc[v];
+        for (int e = 0; e < 16; ++e) x[e] *= ksc[sp][e];
+      } else {
+        const float4_t* sc = (const float4_t*)(p.k_scale + (int64_t)g * DQK + d0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * v + e] *= p.qk_mult * f[e];
+        for (int v = 0; v < 4; ++v) {
+          const float4_t f = sc[v];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * v + e] *= p.qk_mult * f[e];
+        }
       }
     }
   };
@@ -450,13 +474,21 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
     row_tok[nt] = t;
     row_head[nt] = g * G + (row_ok[nt] ? r % G : 0);
     const int64_t qoff = (int64_t)(tok0 + t) * p.q_row_stride + (int64_t)row_head[nt] * DQK;
+    float xq[ONE_PASS ? KPAIRS : 1][16];
     float amax = 0.f;
-    if (row_ok[nt]) {
-      for (int sp = 0; sp < KPAIRS; ++sp) {
-        float x[16];
-        load_q16(qoff, 64 * sp + 16 * grp, x);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    for (int sp = 0; sp < KPAIRS; ++sp) {
+      float x[16];
+      if (row_ok[nt]) {
+        load_q16(qoff, sp, x);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        amax = fmaxf(amax, fabsf(x[e]));
+        if constexpr (ONE_PASS) xq[sp][e] = x[e];
       }
     }
     amax = row_max4(amax);
@@ -469,8 +501,11 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
 #pragma unroll
     for (int sp = 0; sp < KPAIRS; ++sp) {
       float x[16];
-      if (row_ok[nt]) {
-        load_q16(qoff, 64 * sp + 16 * grp, x);
+      if constexpr (ONE_PASS) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = xq[sp][e];
+      } else if (row_ok[nt]) {
+        load_q16(qoff, sp, x);
       } else {
 #pragma unroll
         for (int e = 0; e < 16; ++e) x[e] = 0.f;
@@ -490,6 +525,23 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
     }
     kbias[nt] = KV_OFF * row_sum4(qsum) * row_mult[nt];
   }
+
+  // Per-channel V scales of this lane's output dims (16*md + 4*grp + i).  With
+  // one row tile they are fetched now, so their latency overlaps the query's;
+  // larger tiles fetch them in the epilogue to keep registers for the loop.
+  constexpr bool VSC_EARLY = NT == 1 && MD <= 8;
+  float4_t vsc[MD];
+  auto load_vsc = [&]() {
+    if (fold_channel) {
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+        vsc[md] = *(const float4_t*)(p.v_scale + (int64_t)g * DV + md * 16 + grp * 4);
+    } else {
+#pragma unroll
+      for (int md = 0; md < MD; ++md) vsc[md] = float4_t{v_uniform, v_uniform, v_uniform, v_uniform};
+    }
+  };
+  if constexpr (VSC_EARLY) load_vsc();
 
   float4_t o[MD][NT];
   float m_run[NT], l_run[NT];
@@ -634,16 +686,7 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
   }
 
   // ---- epilogue: normalize, remove the operand offset, V scale, write ----
-  // per-channel V scales of this lane's output dims (16*md + 4*grp + i)
-  float4_t vsc[MD];
-  if (fold_channel) {
-#pragma unroll
-    for (int md = 0; md < MD; ++md)
-      vsc[md] = *(const float4_t*)(p.v_scale + (int64_t)g * DV + md * 16 + grp * 4);
-  } else {
-#pragma unroll
-    for (int md = 0; md < MD; ++md) vsc[md] = float4_t{v_uniform, v_uniform, v_uniform, v_uniform};
-  }
+  if constexpr (!VSC_EARLY) load_vsc();
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float lt = row_sum4(l_run[nt]);
