@@ -212,7 +212,367 @@ __device__ __forceinline__ float row_sum4(float v) {
 
 }  // namespace
 
-// ------------------------------------------------------------------ kernel --
+// ------------------------------------------------------ shared kernel parts --
+//
+// A work unit is (request b, KV head g, tile of GQA-packed query rows, KV
+// chunk c).  Both attention kernels below share its geometry, the query
+// prologue, the online softmax, the PV step and the epilogue; they differ in
+// how KV tiles travel from HBM (LDS DMA shared by several waves, or register
+// staging in a single wave).
+
+struct Unit {
+  int n, tok0, G, rows_total, row0, L, T;
+  int kv_lo, kv_hi, n_chunks, key_end, mask_from, n_tiles;
+  bool split;
+};
+
+// Fills `u` for row tile rt and chunk c of request b; false when the unit is empty.
+template <int ROWS>
+__device__ __forceinline__ bool unit_setup(const AttnParams& p, int b, int rt, int c, Unit& u) {
+  if (p.cu_seqlens_q) {
+    u.tok0 = p.cu_seqlens_q[b];
+    u.n = p.cu_seqlens_q[b + 1] - u.tok0;
+  } else {
+    u.n = p.q_len_uniform;
+    u.tok0 = b * u.n;
+  }
+  u.G = p.group;
+  u.rows_total = u.n * u.G;
+  u.row0 = rt * ROWS;
+  if (u.row0 >= u.rows_total) return false;
+  u.L = p.seq_lens_kv[b];
+  u.T = u.L + u.n;
+  u.kv_lo = 0;
+  u.kv_hi = u.T;
+  u.n_chunks = 1;
+  if (p.chunk_size > 0) {
+    u.n_chunks = (u.T + p.chunk_size - 1) / p.chunk_size;
+    if (c >= u.n_chunks) return false;
+    u.kv_lo = c * p.chunk_size;
+    u.kv_hi = min(u.T, u.kv_lo + p.chunk_size);
+  } else if (c > 0) {
+    return false;
+  }
+  u.split = u.n_chunks > 1;
+  const int last_tok = (min(u.rows_total, u.row0 + ROWS) - 1) / u.G;
+  const int first_tok = u.row0 / u.G;
+  // Bottom-right causal: token t sees keys j <= L + t.
+  u.key_end = p.causal ? min(u.kv_hi, u.L + last_tok + 1) : u.kv_hi;
+  u.mask_from = p.causal ? min(u.kv_hi, u.L + first_tok + 1) : u.kv_hi;  // keys >= this need masks
+  u.n_tiles = u.key_end > u.kv_lo ? (u.key_end - u.kv_lo + TK - 1) / TK : 0;
+  return true;
+}
+
+// Query rows of one wave as the B operand of S^T = K Q^T.
+// k-step 2s covers dims 64s + 16*grp + [0,8), k-step 2s+1 dims 64s + 16*grp + [8,16).
+// A row is multiplied by a power of two 2^k that puts its largest element in
+// [2^14, 2^15), so f16 keeps full relative precision.  Per-channel K scales and
+// sm_scale*log2(e) are folded into Q in that case (then hi + lo parts keep the
+// products exact to ~2^-22); otherwise they multiply S^T in fp32 (row_mult).
+// kbias is the log2-domain logit offset that the int8 operand offset adds.
+template <int DQK, int NT, bool HILO>
+struct QRows {
+  static constexpr int KPAIRS = DQK / 64;
+  half8_t hi[NT][2 * KPAIRS];
+  half8_t lo[HILO ? NT : 1][HILO ? 2 * KPAIRS : 1];
+  float row_mult[NT];
+  float kbias[NT];
+  int tok[NT], head[NT];
+  bool ok[NT];
+};
+
+template <int DQK, int NT, bool HILO>
+__device__ __forceinline__ void load_query(const AttnParams& p, const Unit& u, int g, int row_base,
+                                           int lane, float kv_off, QRows<DQK, NT, HILO>& q) {
+  constexpr int KPAIRS = DQK / 64;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int mode = p.scale_mode;
+  const bool fold_channel = mode == PA_SCALE_PER_CHANNEL;
+  const float k_uniform = fold_channel ? 1.f : p.k_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
+  // Short heads keep the row and its per-channel scales in registers (one pass
+  // over global memory); long ones re-read the row after finding its maximum.
+  constexpr bool ONE_PASS = KPAIRS <= 2;
+  float ksc[ONE_PASS ? KPAIRS : 1][16];
+  if constexpr (ONE_PASS) {
+    if (fold_channel) {
+#pragma unroll
+      for (int sp = 0; sp < KPAIRS; ++sp) {
+        const float4_t* sc = (const float4_t*)(p.k_scale + (int64_t)g * DQK + 64 * sp + 16 * grp);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float4_t f = sc[v];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ksc[sp][4 * v + e] = p.qk_mult * f[e];
+        }
+      }
+    }
+  }
+  auto load_q16 = [&](int64_t qoff, int sp, float* x) {
+    const int d0 = 64 * sp + 16 * grp;
+    if (p.q_is_f32) {
+      const float4_t* src = (const float4_t*)((const float*)p.q + qoff + d0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float4_t f = src[v];
+        x[4 * v] = f[0]; x[4 * v + 1] = f[1]; x[4 * v + 2] = f[2]; x[4 * v + 3] = f[3];
+      }
+    } else {
+      const uint4_t* src = (const uint4_t*)((const uint16_t*)p.q + qoff + d0);
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const uint4_t w = src[v];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[8 * v + 2 * e] = bf16_to_f32((uint16_t)(w[e] & 0xffffu));
+          x[8 * v + 2 * e + 1] = bf16_to_f32((uint16_t)(w[e] >> 16));
+        }
+      }
+    }
+    if (fold_channel) {
+      if constexpr (ONE_PASS) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] *= ksc[sp][e];
+      } else {
+        const float4_t* sc = (const float4_t*)(p.k_scale + (int64_t)g * DQK + d0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float4_t f = sc[v];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * v + e] *= p.qk_mult * f[e];
+        }
+      }
+    }
+  };
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = row_base + nt * 16 + l16;
+    q.ok[nt] = r < u.rows_total;
+    const int t = q.ok[nt] ? r / u.G : 0;
+    q.tok[nt] = t;
+    q.head[nt] = g * u.G + (q.ok[nt] ? r % u.G : 0);
+    const int64_t qoff = (int64_t)(u.tok0 + t) * p.q_row_stride + (int64_t)q.head[nt] * DQK;
+    float xq[ONE_PASS ? KPAIRS : 1][16];
+    float amax = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < KPAIRS; ++sp) {
+      float x[16];
+      if (q.ok[nt]) {
+        load_q16(qoff, sp, x);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        amax = fmaxf(amax, fabsf(x[e]));
+        if constexpr (ONE_PASS) xq[sp][e] = x[e];
+      }
+    }
+    amax = row_max4(amax);
+    int ex = 0;
+    if (amax > 0.f) (void)frexpf(amax, &ex);     // amax < 2^ex
+    const int k2 = min(max(15 - ex, -120), 120);
+    const float up = ldexpf(1.f, k2);
+    q.row_mult[nt] = ldexpf(1.f, -k2) * (fold_channel ? 1.f : p.qk_mult * k_uniform);
+    float qsum = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < KPAIRS; ++sp) {
+      float x[16];
+      if constexpr (ONE_PASS) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = xq[sp][e];
+      } else if (q.ok[nt]) {
+        load_q16(qoff, sp, x);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float v = x[e] * up;
+        const _Float16 h = (_Float16)v;
+        q.hi[nt][2 * sp + e / 8][e % 8] = h;
+        qsum += (float)h;
+        if constexpr (HILO) {
+          const _Float16 l = (_Float16)(v - (float)h);
+          q.lo[nt][2 * sp + e / 8][e % 8] = l;
+          qsum += (float)l;
+        }
+      }
+    }
+    q.kbias[nt] = kv_off * row_sum4(qsum) * q.row_mult[nt];
+  }
+}
+
+// Online-softmax state of one wave: O^T accumulators (lane holds dims
+// 16*md + 4*grp + i of row l16), running max (log2 units) and denominator.
+template <int NT, int MD>
+struct SoftmaxState {
+  float4_t o[MD][NT];
+  float m[NT], l[NT];
+};
+
+template <int NT, int MD>
+__device__ __forceinline__ void softmax_init(SoftmaxState<NT, MD>& st) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    st.m[nt] = -INFINITY;
+    st.l[nt] = 0.f;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) st.o[md][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Masks one 64-key tile of S^T, updates the running max/denominator, rescales
+// O when a row maximum grows, and returns P^T (f16) in the B-operand layout of
+// the PV MFMA: pb[ks][nt] holds keys {32ks + 4grp + i, 32ks + 16 + 4grp + i}.
+template <int DQK, int NT, int MD, bool HILO>
+__device__ __forceinline__ void softmax_tile(const AttnParams& p, const Unit& u, int kbase, int grp,
+                                             const QRows<DQK, NT, HILO>& q, float4_t (&s)[4][NT],
+                                             SoftmaxState<NT, MD>& st, half8_t (&pb)[2][NT]) {
+  const bool need_mask = kbase + TK > u.mask_from;
+  const half2_t ones2 = {(_Float16)1.0f, (_Float16)1.0f};
+  float alpha[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    if (need_mask) {
+      const int lim = p.causal ? min(u.kv_hi, u.L + q.tok[nt] + 1) : u.kv_hi;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kbase + mt * 16 + grp * 4 + i;
+          if (key >= lim) s[mt][nt][i] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][nt][i]);
+    mx = row_max4(mx) * q.row_mult[nt] - q.kbias[nt];
+    const float m_new = fmaxf(st.m[nt], mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    alpha[nt] = __builtin_amdgcn_exp2f(st.m[nt] - m_use);
+    st.m[nt] = m_new;
+    const float nb = -(q.kbias[nt] + m_use);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb[ks][nt][i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[2 * ks][nt][i], q.row_mult[nt], nb));
+        pb[ks][nt][4 + i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[2 * ks + 1][nt][i], q.row_mult[nt], nb));
+      }
+    // Row sum of the f16 weights the MFMA actually sees.  (The pairs are built
+    // from vector elements: bit-casting uint4 lanes to half2 here made this
+    // compiler reuse one register for all four dot products.)
+    float ls = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const half2_t pr = {pb[ks][nt][2 * e], pb[ks][nt][2 * e + 1]};
+        ls = __builtin_amdgcn_fdot2(pr, ones2, ls, false);
+      }
+    st.l[nt] = st.l[nt] * alpha[nt] + ls;
+  }
+  bool grew = false;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) grew |= alpha[nt] != 1.f;
+  if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int md = 0; md < MD; ++md) st.o[md][nt] *= alpha[nt];
+  }
+}
+
+// O^T += V^T P^T for one 64-key tile whose V rows sit in LDS (VROW bytes per
+// row, XOR-swizzled chunks).  tr8 read: lanes 2j, 2j+1 of a 16-lane group give
+// the two 8-byte halves of key row kappa(grp, j); lane i then holds
+// V[kappa(grp, j)][16*md + i], j = 0..7.
+template <bool FP8, int NT, int MD, int VROW>
+__device__ __forceinline__ void pv_tile(const uint8_t* vs, int lane, const half8_t (&pb)[2][NT],
+                                        SoftmaxState<NT, MD>& st) {
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int jr = l16 >> 1;
+  const int hlf = lane & 1;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int vrow = 32 * ks + (jr < 4 ? 4 * grp + jr : 16 + 4 * grp + (jr - 4));
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      const uint8_t* addr = vs + vrow * VROW + swz<VROW>(md, vrow) * 16 + hlf * 8;
+      const int2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) int2_t*)(addr));
+      const half8_t a = bytes8_to_op<FP8>((uint32_t)raw[0], (uint32_t)raw[1]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        st.o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[ks][nt], st.o[md][nt], 0, 0, 0);
+    }
+  }
+}
+
+// Normalize, remove the int8 operand offset, apply V scales and write the final
+// bf16 row + natural lse, or the chunk's fp32 partial + lse.
+template <int DQK, int DV, int NT, bool HILO>
+__device__ __forceinline__ void write_rows(const AttnParams& p, const Unit& u, int g, int c, int lane,
+                                           float kv_off, const QRows<DQK, NT, HILO>& q,
+                                           const SoftmaxState<NT, DV / 16>& st,
+                                           const float4_t (&vsc)[DV / 16]) {
+  constexpr int MD = DV / 16;
+  const int grp = lane >> 4;
+  const int H_q = p.num_q_heads;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float lt = row_sum4(st.l[nt]);
+    const int tok = u.tok0 + q.tok[nt];
+    const int h = q.head[nt];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float off = lt > 0.f ? kv_off : 0.f;
+    const float lse_nat = lt > 0.f ? (st.m[nt] + __log2f(lt)) * LN2F : -INFINITY;
+    if (!q.ok[nt]) continue;
+    float* prow = u.split ? p.part_o + (((int64_t)tok * p.max_chunks + c) * H_q + h) * DV : nullptr;
+    uint16_t* orow = p.out + ((int64_t)tok * H_q + h) * DV;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      const int d = md * 16 + grp * 4;
+      float4_t v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = fmaf(st.o[md][nt][i], inv, -off) * vsc[md][i];
+      if (u.split) {
+        *(float4_t*)(prow + d) = v;
+      } else {
+        const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *(int2_t*)(orow + d) = int2_t{(int)w0, (int)w1};
+      }
+    }
+    if (grp == 0) {
+      if (u.split) p.part_lse[((int64_t)tok * p.max_chunks + c) * H_q + h] = lse_nat;
+      else if (p.lse) p.lse[(int64_t)tok * H_q + h] = lse_nat;
+    }
+  }
+}
+
+// Per-channel V scales of this lane's output dims (16*md + 4*grp + i).
+template <int DV>
+__device__ __forceinline__ void load_v_scales(const AttnParams& p, int g, int lane, float4_t (&vsc)[DV / 16]) {
+  constexpr int MD = DV / 16;
+  const int grp = lane >> 4;
+  const int mode = p.scale_mode;
+  if (mode == PA_SCALE_PER_CHANNEL) {
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+      vsc[md] = *(const float4_t*)(p.v_scale + (int64_t)g * DV + md * 16 + grp * 4);
+  } else {
+    const float v = p.v_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
+#pragma unroll
+    for (int md = 0; md < MD; ++md) vsc[md] = float4_t{v, v, v, v};
+  }
+}
+
+// ----------------------------------------------- shared-tile attention kernel --
 //
 // Template parameters: head dims, cache format, NT 16-row MFMA tiles per wave,
 // NW waves per workgroup (they split the rows and share every KV tile), SHARED
@@ -221,11 +581,11 @@ __device__ __forceinline__ float row_sum4(float v) {
 // per-head or per-tensor scales is exact in f16 and needs one part), NSTAGE
 // (KV tiles staged in LDS; NSTAGE - 1 tiles are in flight while one is used).
 //
-// The LDS DMA is issued with inline assembly and its completion is tracked
-// with explicit s_waitcnt vmcnt(N): the compiler would otherwise drain every
-// outstanding DMA before each LDS access and serialize the pipeline.  No other
-// vector-memory instruction is issued inside the main loop except the rare
-// refill of the page-id window, after which the compiler drains everything.
+// KV tiles travel by LDS DMA (global_load_lds_dwordx4, 16 B per lane), issued
+// with inline assembly and tracked with explicit s_waitcnt vmcnt(N): the
+// compiler would otherwise drain every outstanding DMA before each LDS access.
+// No other vector-memory instruction is issued inside the main loop except the
+// rare refill of the page-id window, which waits for itself.
 
 template <int DQK, int DV, bool FP8, int NT, int NW, bool SHARED, bool HILO, int NSTAGE>
 __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
@@ -263,40 +623,10 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
   const int rt = p.row_tiles - 1 - (int)(blockIdx.x / p.max_chunks);  // long row tiles first
   const int c = (int)(blockIdx.x % p.max_chunks);
 
-  int n, tok0;
-  if (p.cu_seqlens_q) {
-    tok0 = p.cu_seqlens_q[b];
-    n = p.cu_seqlens_q[b + 1] - tok0;
-  } else {
-    n = p.q_len_uniform;
-    tok0 = b * n;
-  }
-  const int G = p.group;
-  const int rows_total = n * G;
-  const int row0 = rt * ROWS;
-  if (row0 >= rows_total) return;
-  const int L = p.seq_lens_kv[b];
-  const int T = L + n;
-  int kv_lo = 0, kv_hi = T, n_chunks = 1;
-  if (p.chunk_size > 0) {
-    n_chunks = (T + p.chunk_size - 1) / p.chunk_size;
-    if (c >= n_chunks) return;
-    kv_lo = c * p.chunk_size;
-    kv_hi = min(T, kv_lo + p.chunk_size);
-  } else if (c > 0) {
-    return;
-  }
-  const bool split = n_chunks > 1;
-  const int last_tok = (min(rows_total, row0 + ROWS) - 1) / G;
-  const int first_tok = row0 / G;
-  const int key_end = p.causal ? min(kv_hi, L + last_tok + 1) : kv_hi;
-  const int mask_from = p.causal ? min(kv_hi, L + first_tok + 1) : kv_hi;  // keys >= this need masks
-  const int n_tiles = key_end > kv_lo ? (key_end - kv_lo + TK - 1) / TK : 0;
-
+  Unit u;
+  if (!unit_setup<ROWS>(p, b, rt, c, u)) return;
   const int32_t* table_row = p.block_table + (int64_t)b * p.max_pages_per_seq;
-  const int H_q = p.num_q_heads;
-  const int mode = p.scale_mode;
-  const bool fold_channel = mode == PA_SCALE_PER_CHANNEL;
+  const int key_end = u.key_end, kv_lo = u.kv_lo, n_tiles = u.n_tiles;
 
   // ---- KV tile loader ----
   // Page-id window: lane l holds the physical page of page index pw_base + l.
@@ -398,161 +728,10 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
   for (int st = 0; st < NSTAGE - 1; ++st)
     if (st < n_tiles) issue_tile(st, st);
 
-  // ---- Q^T operand (B of S^T = K Q^T) ----
-  // k-step 2s covers dims 64s + 16*grp + [0,8), k-step 2s+1 dims 64s + 16*grp + [8,16).
-  // A row is multiplied by a power of two 2^k that puts its largest element in
-  // [2^14, 2^15), so f16 keeps full relative precision.  Per-channel K scales
-  // and sm_scale*log2(e) are folded into Q in that case (then hi + lo parts keep
-  // the products exact to ~2^-22); otherwise they multiply S^T in fp32.
-  const float k_uniform = fold_channel ? 1.f : p.k_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
-  const float v_uniform = fold_channel ? 1.f : p.v_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
-  half8_t qf[NT][2 * KPAIRS];
-  half8_t ql[HILO ? NT : 1][HILO ? 2 * KPAIRS : 1];
-  float row_mult[NT];  // raw S^T -> log2-domain logits
-  float kbias[NT];     // log2-domain logit offset from the int8 operand offset
-  int row_tok[NT], row_head[NT];
-  bool row_ok[NT];
-  // Short heads keep the row and its per-channel scales in registers (one pass
-  // over global memory); long ones re-read the row after finding its maximum.
-  constexpr bool ONE_PASS = KPAIRS <= 2;
-  float ksc[ONE_PASS ? KPAIRS : 1][16];
-  if constexpr (ONE_PASS) {
-    if (fold_channel) {
-#pragma unroll
-      for (int sp = 0; sp < KPAIRS; ++sp) {
-        const float4_t* sc = (const float4_t*)(p.k_scale + (int64_t)g * DQK + 64 * sp + 16 * grp);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float4_t f = sc[v];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ksc[sp][4 * v + e] = p.qk_mult * f[e];
-        }
-      }
-    }
-  }
-  auto load_q16 = [&](int64_t qoff, int sp, float* x) {
-    const int d0 = 64 * sp + 16 * grp;
-    if (p.q_is_f32) {
-      const float4_t* src = (const float4_t*)((const float*)p.q + qoff + d0);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float4_t f = src[v];
-        x[4 * v] = f[0]; x[4 * v + 1] = f[1]; x[4 * v + 2] = f[2]; x[4 * v + 3] = f[3];
-      }
-    } else {
-      const uint4_t* src = (const uint4_t*)((const uint16_t*)p.q + qoff + d0);
-#pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        const uint4_t u = src[v];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[8 * v + 2 * e] = bf16_to_f32((uint16_t)(u[e] & 0xffffu));
-          x[8 * v + 2 * e + 1] = bf16_to_f32((uint16_t)(u[e] >> 16));
-        }
-      }
-    }
-    if (fold_channel) {
-      if constexpr (ONE_PASS) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] *= ksc[sp][e];
-      } else {
-        const float4_t* sc = (const float4_t*)(p.k_scale + (int64_t)g * DQK + d0);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float4_t f = sc[v];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[4 * v + e] *= p.qk_mult * f[e];
-        }
-      }
-    }
-  };
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = row0 + wave * ROWS_W + nt * 16 + l16;
-    row_ok[nt] = r < rows_total;
-    const int t = row_ok[nt] ? r / G : 0;
-    row_tok[nt] = t;
-    row_head[nt] = g * G + (row_ok[nt] ? r % G : 0);
-    const int64_t qoff = (int64_t)(tok0 + t) * p.q_row_stride + (int64_t)row_head[nt] * DQK;
-    float xq[ONE_PASS ? KPAIRS : 1][16];
-    float amax = 0.f;
-#pragma unroll
-    for (int sp = 0; sp < KPAIRS; ++sp) {
-      float x[16];
-      if (row_ok[nt]) {
-        load_q16(qoff, sp, x);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        amax = fmaxf(amax, fabsf(x[e]));
-        if constexpr (ONE_PASS) xq[sp][e] = x[e];
-      }
-    }
-    amax = row_max4(amax);
-    int ex = 0;
-    if (amax > 0.f) (void)frexpf(amax, &ex);     // amax < 2^ex
-    const int k2 = min(max(15 - ex, -120), 120);
-    const float up = ldexpf(1.f, k2);
-    row_mult[nt] = ldexpf(1.f, -k2) * (fold_channel ? 1.f : p.qk_mult * k_uniform);
-    float qsum = 0.f;
-#pragma unroll
-    for (int sp = 0; sp < KPAIRS; ++sp) {
-      float x[16];
-      if constexpr (ONE_PASS) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = xq[sp][e];
-      } else if (row_ok[nt]) {
-        load_q16(qoff, sp, x);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float v = x[e] * up;
-        const _Float16 hi = (_Float16)v;
-        qf[nt][2 * sp + e / 8][e % 8] = hi;
-        qsum += (float)hi;
-        if constexpr (HILO) {
-          const _Float16 lo = (_Float16)(v - (float)hi);
-          ql[nt][2 * sp + e / 8][e % 8] = lo;
-          qsum += (float)lo;
-        }
-      }
-    }
-    kbias[nt] = KV_OFF * row_sum4(qsum) * row_mult[nt];
-  }
-
-  // Per-channel V scales of this lane's output dims (16*md + 4*grp + i).  With
-  // one row tile they are fetched now, so their latency overlaps the query's;
-  // larger tiles fetch them in the epilogue to keep registers for the loop.
-  constexpr bool VSC_EARLY = NT == 1 && MD <= 8;
-  float4_t vsc[MD];
-  auto load_vsc = [&]() {
-    if (fold_channel) {
-#pragma unroll
-      for (int md = 0; md < MD; ++md)
-        vsc[md] = *(const float4_t*)(p.v_scale + (int64_t)g * DV + md * 16 + grp * 4);
-    } else {
-#pragma unroll
-      for (int md = 0; md < MD; ++md) vsc[md] = float4_t{v_uniform, v_uniform, v_uniform, v_uniform};
-    }
-  };
-  if constexpr (VSC_EARLY) load_vsc();
-
-  float4_t o[MD][NT];
-  float m_run[NT], l_run[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
-#pragma unroll
-    for (int md = 0; md < MD; ++md) o[md][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  const half2_t ones2 = {(_Float16)1.0f, (_Float16)1.0f};
+  QRows<DQK, NT, HILO> q;
+  load_query<DQK, NT, HILO>(p, u, g, u.row0 + wave * ROWS_W, lane, KV_OFF, q);
+  SoftmaxState<NT, MD> st;
+  softmax_init(st);
 
   for (int it = 0; it < n_tiles; ++it) {
     const int stage = it % NSTAGE;
@@ -595,130 +774,192 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
-            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], qf[nt][2 * sp + hk], s[mt][nt], 0, 0, 0);
+            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], q.hi[nt][2 * sp + hk], s[mt][nt], 0, 0, 0);
         if constexpr (HILO) {
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
-              s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], ql[nt][2 * sp + hk], s[mt][nt], 0, 0, 0);
+              s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], q.lo[nt][2 * sp + hk], s[mt][nt], 0, 0, 0);
         }
       }
     }
 
-    // ---- mask + online softmax (log2 domain) ----
-    const bool need_mask = kbase + TK > mask_from;
     half8_t pb[2][NT];
-    float alpha[NT];
+    softmax_tile<DQK, NT, MD, HILO>(p, u, kbase, grp, q, s, st, pb);
+    pv_tile<FP8, NT, MD, VROW>(vs, lane, pb, st);
+  }
+
+  float4_t vsc[MD];
+  load_v_scales<DV>(p, g, lane, vsc);
+  write_rows<DQK, DV, NT, HILO>(p, u, g, c, lane, KV_OFF, q, st, vsc);
+}
+
+// -------------------------------------------------------- decode attention --
+//
+// One wave per unit, KV tiles staged in registers with plain global loads
+// (the compiler tracks their completion): K goes straight from registers into
+// the QK^T MFMA (each lane loads the 16 bytes it feeds as the A operand), V is
+// written to a small per-wave LDS tile right after it arrives, so its
+// registers can take the next tile's V while this tile is computed, and read
+// back transposed for PV.  One tile stays in flight per wave while the
+// register file, not LDS, holds it: about twice the bytes in flight per CU of
+// LDS staging at the same occupancy.
+
+template <int D, bool FP8, int NT, bool HILO>
+__global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnParams p) {
+  constexpr int KPAIRS = D / 64;
+  constexpr int MD = D / 16;
+  constexpr int CPR = D / 16;            // 16-byte chunks per row
+  constexpr int RPL = 64 / CPR;          // V rows per 1 KB load
+  constexpr int VLD = TK / RPL;          // V loads per tile
+  constexpr float KV_OFF = FP8 ? 0.f : 1152.f;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t vtile[TK * D];
+
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;
+  const int b = blockIdx.z;
+  const int g = blockIdx.y;
+  const int rt = p.row_tiles - 1 - (int)(blockIdx.x / p.max_chunks);
+  const int c = (int)(blockIdx.x % p.max_chunks);
+
+  Unit u;
+  if (!unit_setup<16 * NT>(p, b, rt, c, u)) return;
+  const int32_t* table_row = p.block_table + (int64_t)b * p.max_pages_per_seq;
+  const int key_end = u.key_end, kv_lo = u.kv_lo, n_tiles = u.n_tiles;
+  const int page_shift = p.page_shift;
+  const int last_page = n_tiles > 0 ? (key_end - 1) >> page_shift : 0;  // never read past it
+
+  // Page-id window: lane l holds the physical page of page index pw_base + l.
+  int pw_base = -(1 << 30);
+  int pw_val = 0;
+  const bool one_page = page_shift >= 6;
+  // lane-constant parts of the K (A-operand) and V (row-coalesced) offsets
+  const int64_t k_lane = (int64_t)l16 * p.k_stride_token + 16 * grp;
+  const int v_row = lane / CPR, v_chunk = lane % CPR;
+  const int64_t v_lane = (int64_t)v_row * p.v_stride_token + 16 * v_chunk;
+
+  uint4_t kr[KPAIRS][4];   // K rows 16mt + l16, dims 64sp + 16grp .. +16
+  uint4_t vr[VLD];         // V row RPL*j + v_row, chunk v_chunk
+
+  auto tile_pages = [&](int kbase, int& pg0, int& pp0, int& pp1, int& pp2, int& pp3) {
+    pg0 = kbase >> page_shift;
+    const int pg_last = min(pg0 + 3, last_page);
+    if (pg0 < pw_base || pg_last > pw_base + 63) {
+      pw_base = pg0;
+      pw_val = table_row[min(pg0 + lane, last_page)];
+    }
+    pp0 = __builtin_amdgcn_readlane(pw_val, pg0 - pw_base);
+    pp1 = pp2 = pp3 = pp0;
+    if (!one_page) {
+      pp1 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 1, pg_last) - pw_base);
+      pp2 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 2, pg_last) - pw_base);
+      pp3 = __builtin_amdgcn_readlane(pw_val, pg_last - pw_base);
+    }
+  };
+  auto load_k = [&](int tile) {
+    const int kbase = kv_lo + tile * TK;
+    int pg0, pp0, pp1, pp2, pp3;
+    tile_pages(kbase, pg0, pp0, pp1, pp2, pp3);
+    if (one_page && kbase + TK <= key_end) {
+      const uint8_t* base = p.k_cache + (int64_t)pp0 * p.k_stride_page + (int64_t)g * p.k_stride_head +
+                            (int64_t)(kbase & ((1 << page_shift) - 1)) * p.k_stride_token;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      if (need_mask) {
-        const int lim = p.causal ? min(kv_hi, L + row_tok[nt] + 1) : kv_hi;
+      for (int sp = 0; sp < KPAIRS; ++sp)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          kr[sp][mt] = *(const uint4_t*)(base + (int64_t)(16 * mt) * p.k_stride_token + 64 * sp + k_lane);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int key = min(kbase + 16 * mt + l16, key_end - 1);
+        const uint8_t* row = paged_row(p.k_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3), key,
+                                       page_shift, g, p.k_stride_page, p.k_stride_head, p.k_stride_token);
+#pragma unroll
+        for (int sp = 0; sp < KPAIRS; ++sp) kr[sp][mt] = *(const uint4_t*)(row + 64 * sp + 16 * grp);
+      }
+    }
+  };
+  auto load_v = [&](int tile) {
+    const int kbase = kv_lo + tile * TK;
+    int pg0, pp0, pp1, pp2, pp3;
+    tile_pages(kbase, pg0, pp0, pp1, pp2, pp3);
+    if (one_page && kbase + TK <= key_end) {
+      const uint8_t* base = p.v_cache + (int64_t)pp0 * p.v_stride_page + (int64_t)g * p.v_stride_head +
+                            (int64_t)(kbase & ((1 << page_shift) - 1)) * p.v_stride_token;
+#pragma unroll
+      for (int j = 0; j < VLD; ++j)
+        vr[j] = *(const uint4_t*)(base + (int64_t)(RPL * j) * p.v_stride_token + v_lane);
+    } else {
+#pragma unroll
+      for (int j = 0; j < VLD; ++j) {
+        const int key = min(kbase + RPL * j + v_row, key_end - 1);
+        const uint8_t* row = paged_row(p.v_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3), key,
+                                       page_shift, g, p.v_stride_page, p.v_stride_head, p.v_stride_token);
+        vr[j] = *(const uint4_t*)(row + 16 * v_chunk);
+      }
+    }
+  };
+
+  if (n_tiles > 0) {
+    load_k(0);
+    load_v(0);
+  }
+  QRows<D, NT, HILO> q;
+  load_query<D, NT, HILO>(p, u, g, u.row0, lane, KV_OFF, q);
+  float4_t vsc[MD];
+  SoftmaxState<NT, MD> st;
+  softmax_init(st);
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const int kbase = kv_lo + it * TK;
+    const bool more = it + 1 < n_tiles;
+    // V(it) -> LDS (swizzled rows), then its registers take V(it + 1)
+#pragma unroll
+    for (int j = 0; j < VLD; ++j) {
+      const int row = RPL * j + v_row;
+      *(uint4_t*)(vtile + row * D + swz<D>(v_chunk, row) * 16) = vr[j];
+    }
+    if (more) load_v(it + 1);
+
+    // ---- S^T = K Q^T from the registers ----
+    float4_t s[4][NT];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) s[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sp = 0; sp < KPAIRS; ++sp) {
+#pragma unroll
+      for (int hk = 0; hk < 2; ++hk) {
+        half8_t a[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) a[mt] = bytes8_to_op<FP8>(kr[sp][mt][2 * hk], kr[sp][mt][2 * hk + 1]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kbase + mt * 16 + grp * 4 + i;
-            if (key >= lim) s[mt][nt][i] = -INFINITY;
-          }
+          for (int nt = 0; nt < NT; ++nt)
+            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], q.hi[nt][2 * sp + hk], s[mt][nt], 0, 0, 0);
+        if constexpr (HILO) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], q.lo[nt][2 * sp + hk], s[mt][nt], 0, 0, 0);
+        }
       }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][nt][i]);
-      mx = row_max4(mx) * row_mult[nt] - kbias[nt];
-      const float m_new = fmaxf(m_run[nt], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      alpha[nt] = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
-      m_run[nt] = m_new;
-      const float nb = -(kbias[nt] + m_use);
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[ks2][nt][i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[2 * ks2][nt][i], row_mult[nt], nb));
-          pb[ks2][nt][4 + i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[2 * ks2 + 1][nt][i], row_mult[nt], nb));
-        }
-      // row sum of the f16 weights the MFMA actually sees.  (The pairs are built
-      // from vector elements: bit-casting uint4 lanes to half2 here makes this
-      // compiler reuse one register for all four dot products.)
-      float ls = 0.f;
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const half2_t pr = {pb[ks2][nt][2 * e], pb[ks2][nt][2 * e + 1]};
-          ls = __builtin_amdgcn_fdot2(pr, ones2, ls, false);
-        }
-      l_run[nt] = l_run[nt] * alpha[nt] + ls;
     }
-    // rescale O only when some row maximum grew
-    bool grew = false;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) grew |= alpha[nt] != 1.f;
-    if (__builtin_amdgcn_ballot_w64(grew) != 0) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int md = 0; md < MD; ++md) o[md][nt] *= alpha[nt];
-    }
+    if (more) load_k(it + 1);
 
-    // ---- O^T += V^T P^T ----
-    // tr8 read: lanes 2j, 2j+1 of a 16-lane group give the two 8-byte halves of key
-    // row kappa(grp, j); lane i then holds V[kappa(grp, j)][16*md + i], j = 0..7.
-    const int jr = l16 >> 1;
-    const int hlf = lane & 1;
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      const int vrow = 32 * ks2 + (jr < 4 ? 4 * grp + jr : 16 + 4 * grp + (jr - 4));
-#pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        const uint8_t* addr = vs + vrow * VROW + swz<VROW>(md, vrow) * 16 + hlf * 8;
-        const int2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) int2_t*)(addr));
-        const half8_t a = bytes8_to_op<FP8>((uint32_t)raw[0], (uint32_t)raw[1]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[ks2][nt], o[md][nt], 0, 0, 0);
-      }
-    }
+    half8_t pb[2][NT];
+    softmax_tile<D, NT, MD, HILO>(p, u, kbase, grp, q, s, st, pb);
+    pv_tile<FP8, NT, MD, D>(vtile, lane, pb, st);
   }
 
-  // ---- epilogue: normalize, remove the operand offset, V scale, write ----
-  if constexpr (!VSC_EARLY) load_vsc();
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const float lt = row_sum4(l_run[nt]);
-    const bool ok = row_ok[nt];
-    const int tok = tok0 + row_tok[nt];
-    const int h = row_head[nt];
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float off = lt > 0.f ? KV_OFF : 0.f;
-    const float lse_nat = lt > 0.f ? (m_run[nt] + __log2f(lt)) * LN2F : -INFINITY;
-    if (!ok) continue;
-    float* prow = split ? p.part_o + (((int64_t)tok * p.max_chunks + c) * H_q + h) * DV : nullptr;
-    uint16_t* orow = p.out + ((int64_t)tok * H_q + h) * DV;
-#pragma unroll
-    for (int md = 0; md < MD; ++md) {
-      const int d = md * 16 + grp * 4;
-      const float4_t sv = vsc[md];
-      float4_t v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = fmaf(o[md][nt][i], inv, -off) * sv[i];
-      if (split) {
-        *(float4_t*)(prow + d) = v;
-      } else {
-        const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        const uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-        *(int2_t*)(orow + d) = int2_t{(int)w0, (int)w1};
-      }
-    }
-    if (grp == 0) {
-      if (split) p.part_lse[((int64_t)tok * p.max_chunks + c) * H_q + h] = lse_nat;
-      else if (p.lse) p.lse[(int64_t)tok * H_q + h] = lse_nat;
-    }
-  }
+  load_v_scales<D>(p, g, lane, vsc);
+  write_rows<D, D, NT, HILO>(p, u, g, c, lane, KV_OFF, q, st, vsc);
 }
 
 // ------------------------------------------------------------------- merge --
@@ -793,6 +1034,12 @@ hipError_t launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, bool FP8, int NT, bool HILO>
+hipError_t launch_decode(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((paged_decode_kernel<D, FP8, NT, HILO>), grid, dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
 using LaunchFn = hipError_t (*)(const AttnParams&, dim3, hipStream_t);
 
 struct Entry {
@@ -800,24 +1047,20 @@ struct Entry {
   LaunchFn fn;
 };
 
+// nstage == 0 marks the register-staged single-wave decode kernel.
 #define PA_ENTRY(DQK, DV, FP8, NT, NW, SH, HL, NS) \
   Entry{AttnConfig{DQK, DV, FP8, SH, NT, NW, HL, NS}, &launch_one<DQK, DV, FP8, NT, NW, SH, HL, NS>}
+#define PA_DEC(D, FP8, NT, HL) Entry{AttnConfig{D, D, FP8, false, NT, 1, HL, 0}, &launch_decode<D, FP8, NT, HL>}
 
-// decode-shaped (one wave, deep pipeline) and append-shaped (4 waves x 32 rows)
-#ifndef PA_DECODE_NSTAGE
-#define PA_DECODE_NSTAGE 2
-#endif
-#define PA_DS PA_DECODE_NSTAGE
-#define PA_SET(DQK, DV, FP8, HL)                                                                  \
-  PA_ENTRY(DQK, DV, FP8, 1, 1, false, HL, PA_DS), PA_ENTRY(DQK, DV, FP8, 2, 1, false, HL, PA_DS), \
-      PA_ENTRY(DQK, DV, FP8, 3, 1, false, HL, PA_DS),                                             \
-      PA_ENTRY(DQK, DV, FP8, 4, 1, false, HL, PA_DS), PA_ENTRY(DQK, DV, FP8, 2, 4, false, HL, 2)
+#define PA_SET(D, FP8, HL)                                                                       \
+  PA_DEC(D, FP8, 1, HL), PA_DEC(D, FP8, 2, HL), PA_ENTRY(D, D, FP8, 3, 1, false, HL, 2),            \
+      PA_ENTRY(D, D, FP8, 4, 1, false, HL, 2), PA_ENTRY(D, D, FP8, 2, 4, false, HL, 2)
 
 const Entry kTable[] = {
-    PA_SET(64, 64, false, false),   PA_SET(64, 64, false, true),
-    PA_SET(64, 64, true, false),    PA_SET(64, 64, true, true),
-    PA_SET(128, 128, false, false), PA_SET(128, 128, false, true),
-    PA_SET(128, 128, true, false),  PA_SET(128, 128, true, true),
+    PA_SET(64, false, false),   PA_SET(64, false, true),
+    PA_SET(64, true, false),    PA_SET(64, true, true),
+    PA_SET(128, false, false), PA_SET(128, false, true),
+    PA_SET(128, true, false),  PA_SET(128, true, true),
     PA_ENTRY(576, 512, true, 1, 8, true, false, 2),  PA_ENTRY(576, 512, true, 1, 8, true, true, 2),
     PA_ENTRY(576, 512, false, 1, 8, true, false, 2), PA_ENTRY(576, 512, false, 1, 8, true, true, 2),
 };

@@ -13,10 +13,6 @@
 #include "pa_internal.h"
 #include "pagedattn.h"
 
-#ifndef PA_DECODE_NSTAGE
-#define PA_DECODE_NSTAGE 2  // KV tiles staged per single-wave decode workgroup
-#endif
-
 namespace {
 
 thread_local std::string g_last_error;
@@ -167,7 +163,8 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   } else if (rows_max <= 64) {
     cfg.nt = (int)ceil_div(rows_max, 16);
     cfg.nw = 1;
-    cfg.nstage = PA_DECODE_NSTAGE;
+    // up to 32 rows: register-staged decode kernel; more rows: LDS-staged
+    cfg.nstage = cfg.nt <= 2 ? 0 : 2;
   } else {
     cfg.nt = 2;
     cfg.nw = 4;
