@@ -12,7 +12,9 @@
 namespace pa {
 
 // One launch of the paged attention kernel.  A work unit is (request b, KV
-// head g, packed-row tile, KV chunk); grid = (row_tiles * chunk_slots, H_kv, B).
+// head g, packed-row tile, KV chunk); the decode kernel's grid is
+// (B * H_kv, row_tiles, chunk_slots), the shared-tile kernel's
+// (row_tiles * chunk_slots, H_kv, B).
 struct AttnParams {
   const void* q;
   const uint8_t* k_cache;
@@ -30,6 +32,7 @@ struct AttnParams {
   int64_t k_stride_page, k_stride_head, k_stride_token;
   int64_t v_stride_page, v_stride_head, v_stride_token;
   int32_t num_q_heads;
+  int32_t num_kv_heads;
   int32_t group;                // G = H_q / H_kv
   int32_t page_shift;           // log2(page_size)
   int32_t max_pages_per_seq;

@@ -618,9 +618,11 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15;
   const int grp = lane >> 4;
-  const int b = blockIdx.z;
-  const int g = blockIdx.y;
-  const int rt = p.row_tiles - 1 - (int)(blockIdx.x / p.max_chunks);  // long row tiles first
+  // grid = (row tiles * chunks, H_kv, B): the row tiles of one request and head
+  // are dispatched next to each other (they read the same KV), longest first
+  const int b = (int)blockIdx.z;
+  const int g = (int)blockIdx.y;
+  const int rt = p.row_tiles - 1 - (int)(blockIdx.x / p.max_chunks);
   const int c = (int)(blockIdx.x % p.max_chunks);
 
   Unit u;
@@ -797,33 +799,35 @@ __global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
 
 // -------------------------------------------------------- decode attention --
 //
-// One wave per unit, KV tiles staged in registers with plain global loads
-// (the compiler tracks their completion): K goes straight from registers into
-// the QK^T MFMA (each lane loads the 16 bytes it feeds as the A operand), V is
-// written to a small per-wave LDS tile right after it arrives, so its
-// registers can take the next tile's V while this tile is computed, and read
-// back transposed for PV.  One tile stays in flight per wave while the
-// register file, not LDS, holds it: about twice the bytes in flight per CU of
-// LDS staging at the same occupancy.
+// One wave per unit; KV tiles are staged in registers with plain, row-coalesced
+// global loads (the compiler tracks their completion).  At the top of each
+// iteration the arrived tile is written to a per-wave LDS tile and the same
+// registers immediately take the next tile, so every load has a whole
+// iteration to arrive while the register file, not LDS, holds the bytes in
+// flight.  K is then read back in the MFMA A-operand layout, V transposed.
 
 template <int D, bool FP8, int NT, bool HILO>
 __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnParams p) {
   constexpr int KPAIRS = D / 64;
   constexpr int MD = D / 16;
   constexpr int CPR = D / 16;            // 16-byte chunks per row
-  constexpr int RPL = 64 / CPR;          // V rows per 1 KB load
-  constexpr int VLD = TK / RPL;          // V loads per tile
+  constexpr int RPL = 64 / CPR;          // rows per 1 KB wave load
+  constexpr int NLD = TK / RPL;          // loads per tile (K or V)
   constexpr float KV_OFF = FP8 ? 0.f : 1152.f;
 
+  __shared__ __attribute__((aligned(1024))) uint8_t ktile[TK * D];
   __shared__ __attribute__((aligned(1024))) uint8_t vtile[TK * D];
+  __shared__ float vscale_lds[D];
 
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15;
   const int grp = lane >> 4;
-  const int b = blockIdx.z;
-  const int g = blockIdx.y;
-  const int rt = p.row_tiles - 1 - (int)(blockIdx.x / p.max_chunks);
-  const int c = (int)(blockIdx.x % p.max_chunks);
+  // grid = (B * H_kv, row tiles, chunks): chunk-major, so the empty units of
+  // short requests (chunks past their length) are dispatched last
+  const int b = (int)blockIdx.x / p.num_kv_heads;
+  const int g = (int)blockIdx.x % p.num_kv_heads;
+  const int rt = p.row_tiles - 1 - (int)blockIdx.y;  // long (late-token) row tiles first
+  const int c = (int)blockIdx.z;
 
   Unit u;
   if (!unit_setup<16 * NT>(p, b, rt, c, u)) return;
@@ -836,95 +840,81 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnP
   int pw_base = -(1 << 30);
   int pw_val = 0;
   const bool one_page = page_shift >= 6;
-  // lane-constant parts of the K (A-operand) and V (row-coalesced) offsets
-  const int64_t k_lane = (int64_t)l16 * p.k_stride_token + 16 * grp;
-  const int v_row = lane / CPR, v_chunk = lane % CPR;
-  const int64_t v_lane = (int64_t)v_row * p.v_stride_token + 16 * v_chunk;
+  const int ld_row = lane / CPR, ld_chunk = lane % CPR;
+  const int64_t k_lane = (int64_t)ld_row * p.k_stride_token + 16 * ld_chunk;
+  const int64_t v_lane = (int64_t)ld_row * p.v_stride_token + 16 * ld_chunk;
 
-  uint4_t kr[KPAIRS][4];   // K rows 16mt + l16, dims 64sp + 16grp .. +16
-  uint4_t vr[VLD];         // V row RPL*j + v_row, chunk v_chunk
+  uint4_t kr[NLD];   // K row RPL*j + ld_row, chunk ld_chunk
+  uint4_t vr[NLD];   // V row RPL*j + ld_row, chunk ld_chunk
 
-  auto tile_pages = [&](int kbase, int& pg0, int& pp0, int& pp1, int& pp2, int& pp3) {
-    pg0 = kbase >> page_shift;
+  auto load_tile = [&](int tile) {
+    const int kbase = kv_lo + tile * TK;
+    const int pg0 = kbase >> page_shift;
     const int pg_last = min(pg0 + 3, last_page);
     if (pg0 < pw_base || pg_last > pw_base + 63) {
       pw_base = pg0;
       pw_val = table_row[min(pg0 + lane, last_page)];
     }
-    pp0 = __builtin_amdgcn_readlane(pw_val, pg0 - pw_base);
-    pp1 = pp2 = pp3 = pp0;
-    if (!one_page) {
-      pp1 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 1, pg_last) - pw_base);
-      pp2 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 2, pg_last) - pw_base);
-      pp3 = __builtin_amdgcn_readlane(pw_val, pg_last - pw_base);
-    }
-  };
-  auto load_k = [&](int tile) {
-    const int kbase = kv_lo + tile * TK;
-    int pg0, pp0, pp1, pp2, pp3;
-    tile_pages(kbase, pg0, pp0, pp1, pp2, pp3);
+    const int pp0 = __builtin_amdgcn_readlane(pw_val, pg0 - pw_base);
     if (one_page && kbase + TK <= key_end) {
-      const uint8_t* base = p.k_cache + (int64_t)pp0 * p.k_stride_page + (int64_t)g * p.k_stride_head +
-                            (int64_t)(kbase & ((1 << page_shift) - 1)) * p.k_stride_token;
+      const int64_t slot0 = kbase & ((1 << page_shift) - 1);
+      const uint8_t* kb = p.k_cache + (int64_t)pp0 * p.k_stride_page + (int64_t)g * p.k_stride_head +
+                          slot0 * p.k_stride_token;
+      const uint8_t* vb = p.v_cache + (int64_t)pp0 * p.v_stride_page + (int64_t)g * p.v_stride_head +
+                          slot0 * p.v_stride_token;
 #pragma unroll
-      for (int sp = 0; sp < KPAIRS; ++sp)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          kr[sp][mt] = *(const uint4_t*)(base + (int64_t)(16 * mt) * p.k_stride_token + 64 * sp + k_lane);
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int key = min(kbase + 16 * mt + l16, key_end - 1);
-        const uint8_t* row = paged_row(p.k_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3), key,
-                                       page_shift, g, p.k_stride_page, p.k_stride_head, p.k_stride_token);
-#pragma unroll
-        for (int sp = 0; sp < KPAIRS; ++sp) kr[sp][mt] = *(const uint4_t*)(row + 64 * sp + 16 * grp);
+      for (int j = 0; j < NLD; ++j) {
+        kr[j] = *(const uint4_t*)(kb + (int64_t)(RPL * j) * p.k_stride_token + k_lane);
+        vr[j] = *(const uint4_t*)(vb + (int64_t)(RPL * j) * p.v_stride_token + v_lane);
       }
-    }
-  };
-  auto load_v = [&](int tile) {
-    const int kbase = kv_lo + tile * TK;
-    int pg0, pp0, pp1, pp2, pp3;
-    tile_pages(kbase, pg0, pp0, pp1, pp2, pp3);
-    if (one_page && kbase + TK <= key_end) {
-      const uint8_t* base = p.v_cache + (int64_t)pp0 * p.v_stride_page + (int64_t)g * p.v_stride_head +
-                            (int64_t)(kbase & ((1 << page_shift) - 1)) * p.v_stride_token;
-#pragma unroll
-      for (int j = 0; j < VLD; ++j)
-        vr[j] = *(const uint4_t*)(base + (int64_t)(RPL * j) * p.v_stride_token + v_lane);
     } else {
+      int pp1 = pp0, pp2 = pp0, pp3 = pp0;
+      if (!one_page) {
+        pp1 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 1, pg_last) - pw_base);
+        pp2 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 2, pg_last) - pw_base);
+        pp3 = __builtin_amdgcn_readlane(pw_val, pg_last - pw_base);
+      }
 #pragma unroll
-      for (int j = 0; j < VLD; ++j) {
-        const int key = min(kbase + RPL * j + v_row, key_end - 1);
-        const uint8_t* row = paged_row(p.v_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3), key,
-                                       page_shift, g, p.v_stride_page, p.v_stride_head, p.v_stride_token);
-        vr[j] = *(const uint4_t*)(row + 16 * v_chunk);
+      for (int j = 0; j < NLD; ++j) {
+        const int key = min(kbase + RPL * j + ld_row, key_end - 1);
+        const int page = pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3);
+        kr[j] = *(const uint4_t*)(paged_row(p.k_cache, page, key, page_shift, g, p.k_stride_page,
+                                            p.k_stride_head, p.k_stride_token) + 16 * ld_chunk);
+        vr[j] = *(const uint4_t*)(paged_row(p.v_cache, page, key, page_shift, g, p.v_stride_page,
+                                            p.v_stride_head, p.v_stride_token) + 16 * ld_chunk);
       }
     }
   };
 
-  if (n_tiles > 0) {
-    load_k(0);
-    load_v(0);
+  if (n_tiles > 0) load_tile(0);
+  // V scales go to LDS while the first tile and the query are in flight.
+  const bool fold_channel = p.scale_mode == PA_SCALE_PER_CHANNEL;
+  float vs_lane[D / 64];
+  if (fold_channel) {
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) vs_lane[i] = p.v_scale[(int64_t)g * D + lane + 64 * i];
   }
   QRows<D, NT, HILO> q;
   load_query<D, NT, HILO>(p, u, g, u.row0, lane, KV_OFF, q);
-  float4_t vsc[MD];
+  if (fold_channel) {
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) vscale_lds[lane + 64 * i] = vs_lane[i];
+  }
   SoftmaxState<NT, MD> st;
   softmax_init(st);
 
   for (int it = 0; it < n_tiles; ++it) {
     const int kbase = kv_lo + it * TK;
-    const bool more = it + 1 < n_tiles;
-    // V(it) -> LDS (swizzled rows), then its registers take V(it + 1)
+    // tile `it` -> LDS (swizzled rows); its registers take tile it + 1
 #pragma unroll
-    for (int j = 0; j < VLD; ++j) {
-      const int row = RPL * j + v_row;
-      *(uint4_t*)(vtile + row * D + swz<D>(v_chunk, row) * 16) = vr[j];
+    for (int j = 0; j < NLD; ++j) {
+      const int row = RPL * j + ld_row;
+      *(uint4_t*)(ktile + row * D + swz<D>(ld_chunk, row) * 16) = kr[j];
+      *(uint4_t*)(vtile + row * D + swz<D>(ld_chunk, row) * 16) = vr[j];
     }
-    if (more) load_v(it + 1);
+    if (it + 1 < n_tiles) load_tile(it + 1);
 
-    // ---- S^T = K Q^T from the registers ----
+    // ---- S^T = K Q^T: 4 x NT independent accumulator chains ----
     float4_t s[4][NT];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -932,11 +922,17 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnP
       for (int nt = 0; nt < NT; ++nt) s[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int sp = 0; sp < KPAIRS; ++sp) {
+      uint4_t raw[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int row = mt * 16 + l16;
+        raw[mt] = *(const uint4_t*)(ktile + row * D + swz<D>(4 * sp + grp, row) * 16);
+      }
 #pragma unroll
       for (int hk = 0; hk < 2; ++hk) {
         half8_t a[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) a[mt] = bytes8_to_op<FP8>(kr[sp][mt][2 * hk], kr[sp][mt][2 * hk + 1]);
+        for (int mt = 0; mt < 4; ++mt) a[mt] = bytes8_to_op<FP8>(raw[mt][2 * hk], raw[mt][2 * hk + 1]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -951,14 +947,19 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnP
         }
       }
     }
-    if (more) load_k(it + 1);
 
     half8_t pb[2][NT];
     softmax_tile<D, NT, MD, HILO>(p, u, kbase, grp, q, s, st, pb);
     pv_tile<FP8, NT, MD, D>(vtile, lane, pb, st);
   }
 
-  load_v_scales<D>(p, g, lane, vsc);
+  float4_t vsc[MD];
+  if (fold_channel) {
+#pragma unroll
+    for (int md = 0; md < MD; ++md) vsc[md] = *(const float4_t*)(vscale_lds + md * 16 + grp * 4);
+  } else {
+    load_v_scales<D>(p, g, lane, vsc);
+  }
   write_rows<D, D, NT, HILO>(p, u, g, c, lane, KV_OFF, q, st, vsc);
 }
 
@@ -986,26 +987,31 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MergeParams p) {
   const int h = pair % p.num_q_heads;
   const int lane = threadIdx.x % LPR;
   const int64_t tok = tok0 + t;
-  const float* lrow = p.part_lse + tok * p.max_chunks * p.num_q_heads + h;
+  const int64_t H = p.num_q_heads;
+  const float* lrow = p.part_lse + tok * p.max_chunks * H + h;
+  const float* orow = p.part_o + (tok * p.max_chunks * H + h) * DV + lane * 4;
+  // Every lane of the row reads the (few, cached) lse values itself: no
+  // cross-lane step, and the loads of both passes are independent of each
+  // other so they are issued back to back.
   float M = -INFINITY;
-  for (int cc = 0; cc < nc; ++cc) M = fmaxf(M, lrow[(int64_t)cc * p.num_q_heads]);
+#pragma unroll 8
+  for (int cc = 0; cc < nc; ++cc) M = fmaxf(M, lrow[(int64_t)cc * H]);
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  const float* orow = p.part_o + (tok * p.max_chunks * p.num_q_heads + h) * DV + lane * 4;
+#pragma unroll 4
   for (int cc = 0; cc < nc; ++cc) {
-    const float lc = lrow[(int64_t)cc * p.num_q_heads];
-    if (lc == -INFINITY) continue;
-    const float w = __expf(lc - M);
+    const float lc = lrow[(int64_t)cc * H];
+    const float4_t v = *(const float4_t*)(orow + (int64_t)cc * H * DV);
+    const float w = lc == -INFINITY ? 0.f : __expf(lc - M);
     den += w;
-    const float4_t v = *(const float4_t*)(orow + (int64_t)cc * p.num_q_heads * DV);
     acc += w * v;
   }
   const float inv = 1.f / den;
-  uint16_t* dst = p.out + (tok * p.num_q_heads + h) * DV + lane * 4;
+  uint16_t* dst = p.out + (tok * H + h) * DV + lane * 4;
   const uint32_t w0 = (uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16);
   const uint32_t w1 = (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16);
   *(int2_t*)dst = int2_t{(int)w0, (int)w1};
-  if (p.lse && lane == 0) p.lse[tok * p.num_q_heads + h] = M + __logf(den);
+  if (p.lse && lane == 0) p.lse[tok * H + h] = M + __logf(den);
 }
 
 // ------------------------------------------------------------ debug gather --

@@ -175,9 +175,10 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   const int64_t rows_per_wg = 16LL * cfg.nt * cfg.nw;
   const int64_t row_tiles = ceil_div(rows_max, rows_per_wg);
   const int64_t max_chunks = max_chunks_of(p);
-  if (row_tiles * max_chunks > 0x7fffffffLL)
-    return fail(PA_ERR_UNSUPPORTED, "grid too large (%lld row tiles x %lld chunks)",
-                (long long)row_tiles, (long long)max_chunks);
+  if (row_tiles > 65535 || max_chunks > 65535 || row_tiles * max_chunks > 0x7fffffffLL)
+    return fail(PA_ERR_UNSUPPORTED, "grid too large (%lld row tiles, %lld chunks, %lld request-heads)",
+                (long long)row_tiles, (long long)max_chunks,
+                (long long)p->batch * p->num_kv_heads);
 
   const WorkspaceLayout wl = workspace_layout(p, total_q);
   if (wl.total > 0) {
@@ -208,6 +209,7 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   ap.v_stride_head = p->v_stride_head;
   ap.v_stride_token = p->v_stride_token;
   ap.num_q_heads = p->num_q_heads;
+  ap.num_kv_heads = p->num_kv_heads;
   ap.group = (int32_t)G;
   ap.page_shift = log2_exact(p->page_size);
   ap.max_pages_per_seq = p->max_pages_per_seq;
@@ -221,7 +223,13 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   ap.qk_mult = p->sm_scale * 1.4426950408889634f;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid((unsigned)(row_tiles * max_chunks), (unsigned)p->num_kv_heads, (unsigned)p->batch);
+  // The single-wave decode kernel runs chunk-major (empty chunks of short
+  // requests dispatch last); the shared-tile kernel keeps one request-head's
+  // row tiles adjacent.
+  const bool decode_kernel = cfg.nstage == 0;
+  dim3 grid = decode_kernel
+                  ? dim3((unsigned)(p->batch * p->num_kv_heads), (unsigned)row_tiles, (unsigned)max_chunks)
+                  : dim3((unsigned)(row_tiles * max_chunks), (unsigned)p->num_kv_heads, (unsigned)p->batch);
   hipError_t e = pa::launch_attention(cfg, ap, grid, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (p->chunk_size > 0) {
