@@ -38,6 +38,7 @@ typedef int int2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
 
 constexpr int TK = 64;  // keys per KV tile
+constexpr float LAZY_LOG2 = 8.f;  // softmax reference-max slack (log2 units)
 constexpr float LN2F = 0.6931471805599453f;
 
 // ------------------------------------------------------------ small helpers --
@@ -451,7 +452,11 @@ __device__ __forceinline__ void softmax_tile(const AttnParams& p, const Unit& u,
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mt][nt][i]);
     mx = row_max4(mx) * q.row_mult[nt] - q.kbias[nt];
-    const float m_new = fmaxf(st.m[nt], mx);
+    // Lazy rescaling: the reference maximum only moves when the row maximum
+    // exceeds it by more than 2^LAZY_LOG2; weights then stay <= 256 (exact
+    // enough in f16 and fp32) and O is rescaled rarely.  lse = m + log2(l)
+    // holds for any reference m.
+    const float m_new = mx > st.m[nt] + LAZY_LOG2 ? mx : st.m[nt];
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     alpha[nt] = __builtin_amdgcn_exp2f(st.m[nt] - m_use);
     st.m[nt] = m_new;
@@ -588,7 +593,7 @@ __device__ __forceinline__ void load_v_scales(const AttnParams& p, int g, int la
 // rare refill of the page-id window, which waits for itself.
 
 template <int DQK, int DV, bool FP8, int NT, int NW, bool SHARED, bool HILO, int NSTAGE>
-__global__ __launch_bounds__(64 * NW) void paged_attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void paged_attn_kernel(AttnParams p) {
   constexpr int ROWS_W = 16 * NT;
   constexpr int ROWS = ROWS_W * NW;
   constexpr int KROW = DQK;                       // bytes per K row in LDS
