@@ -81,7 +81,7 @@ struct AttnConfig {
   int nt;           // 16-row MFMA tiles per wave
   int nw;           // waves per workgroup (they split the rows, share KV tiles)
   bool hilo;        // Q carries per-channel scales or is fp32: f16 hi + lo parts
-  int nstage;       // KV tiles staged in LDS (0: register-staged decode kernel)
+  int nstage;       // KV tiles staged in LDS (0: register-staged decode kernel, 1: MLA kernel)
 };
 
 // Returns hipSuccess, hipErrorInvalidValue when no specialization matches.

@@ -968,6 +968,248 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnP
   write_rows<D, D, NT, HILO>(p, u, g, c, lane, KV_OFF, q, st, vsc);
 }
 
+// ------------------------------------------------------- MLA latent decode --
+//
+// Shared 576/512 latent rows (V = first 512 bytes of each K row), one KV head,
+// 128 packed query rows per workgroup of 8 waves.  The per-wave state is kept
+// small by splitting the two contractions differently:
+//   phase A  wave w computes S^T = K Q^T and the online softmax for rows
+//            16w..16w+15 (its query rows stay in registers), and writes P^T to
+//            LDS already in the B-operand layout of the PV MFMA;
+//   phase B  wave w accumulates O^T for output dims 64w..64w+63 of all 128
+//            rows, reading every wave's P^T and per-row rescale factors.
+// KV tiles (64 keys x 576 bytes) travel by LDS DMA as in the shared-tile kernel.
+
+template <bool FP8, bool HILO>
+__global__ __launch_bounds__(512, 1) void paged_mla_kernel(AttnParams p) {
+  constexpr int DQK = 576, DV = 512, NW = 8, ROWS = 128;
+  constexpr int KROW = DQK;
+  constexpr int KTILE = TK * KROW;                // 36 KB
+  constexpr int KCH = KTILE / 16;
+  constexpr int KCPR = KROW / 16;
+  constexpr int KPAIRS = DQK / 64;                // 9
+  constexpr int K_DMA = (KCH + 64 * NW - 1) / (64 * NW);
+  constexpr int MDW = DV / 16 / NW;               // 4 output-dim tiles per wave
+  constexpr int NTB = ROWS / 16;                  // 8 row tiles in phase B
+  constexpr float KV_OFF = FP8 ? 0.f : 1152.f;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * KTILE];
+  __shared__ __attribute__((aligned(16))) half8_t pt_lds[NTB * 2 * 64];   // P^T operands
+  __shared__ float alpha_lds[ROWS];
+  __shared__ float lrow_lds[ROWS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;
+  const int b = (int)blockIdx.z;
+  const int g = (int)blockIdx.y;
+  const int rt = p.row_tiles - 1 - (int)(blockIdx.x / p.max_chunks);
+  const int c = (int)(blockIdx.x % p.max_chunks);
+
+  Unit u;
+  if (!unit_setup<ROWS>(p, b, rt, c, u)) return;
+  const int32_t* table_row = p.block_table + (int64_t)b * p.max_pages_per_seq;
+  const int key_end = u.key_end, kv_lo = u.kv_lo, n_tiles = u.n_tiles;
+  const int page_shift = p.page_shift;
+  const int last_page = n_tiles > 0 ? (key_end - 1) >> page_shift : 0;
+  int pw_base = -(1 << 30);
+  int pw_val = 0;
+  const bool one_page = page_shift >= 6;
+  const bool fast_addr = one_page && (int64_t)TK * p.k_stride_token < (1LL << 30);
+  uint32_t koff[K_DMA];
+#pragma unroll
+  for (int j = 0; j < K_DMA; ++j) {
+    const int ch = (j * NW + wave) * 64 + lane;
+    const int row = ch / KCPR;
+    koff[j] = (uint32_t)(row * p.k_stride_token + swz<KROW>(ch % KCPR, row) * 16);
+  }
+  const uint32_t smem_base = lds_addr(smem);
+
+  auto issue_tile = [&](int tile, int stage) {
+    const int kbase = kv_lo + tile * TK;
+    const int pg0 = kbase >> page_shift;
+    const int pg_last = min(pg0 + 3, last_page);
+    if (pg0 < pw_base || pg_last > pw_base + 63) {
+      pw_base = pg0;
+      pw_val = load_i32_sync(table_row + min(pg0 + lane, last_page));
+    }
+    const int pp0 = __builtin_amdgcn_readlane(pw_val, pg0 - pw_base);
+    const uint32_t kdst = smem_base + stage * KTILE;
+    if (fast_addr && kbase + TK <= key_end) {
+      const uint8_t* kb = p.k_cache + (int64_t)pp0 * p.k_stride_page + (int64_t)g * p.k_stride_head +
+                          (int64_t)(kbase & ((1 << page_shift) - 1)) * p.k_stride_token;
+#pragma unroll
+      for (int j = 0; j < K_DMA; ++j)
+        if ((j * NW + wave) * 64 < KCH) dma16_s(koff[j], kb, kdst + (j * NW + wave) * 1024);
+      return;
+    }
+    int pp1 = pp0, pp2 = pp0, pp3 = pp0;
+    if (!one_page) {
+      pp1 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 1, pg_last) - pw_base);
+      pp2 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 2, pg_last) - pw_base);
+      pp3 = __builtin_amdgcn_readlane(pw_val, pg_last - pw_base);
+    }
+#pragma unroll
+    for (int j = 0; j < K_DMA; ++j) {
+      const int blk = j * NW + wave;
+      if (blk * 64 < KCH) {
+        const int ch = blk * 64 + lane;
+        const int row = ch / KCPR;
+        const int key = min(kbase + row, key_end - 1);
+        const uint8_t* src = paged_row(p.k_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3), key,
+                                       page_shift, g, p.k_stride_page, p.k_stride_head, p.k_stride_token) +
+                             swz<KROW>(ch % KCPR, row) * 16;
+        dma16(src, kdst + blk * 1024);
+      }
+    }
+  };
+
+  if (n_tiles > 0) issue_tile(0, 0);
+
+  QRows<DQK, 1, HILO> q;
+  load_query<DQK, 1, HILO>(p, u, g, u.row0 + wave * 16, lane, KV_OFF, q);
+  SoftmaxState<1, 1> sa;   // phase-A row state (m, l); its o is unused
+  softmax_init(sa);
+  float4_t o[MDW][NTB];    // phase-B accumulators: dims 64*wave + 16*md + 4*grp + i, row 16*nt + l16
+#pragma unroll
+  for (int md = 0; md < MDW; ++md)
+#pragma unroll
+    for (int nt = 0; nt < NTB; ++nt) o[md][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const int stage = it & 1;
+    wait_vmcnt<0>();
+    __syncthreads();  // tile landed everywhere; phase B of it - 1 is done with P^T and the stage
+    if (it + 1 < n_tiles) issue_tile(it + 1, stage ^ 1);
+    const uint8_t* ks = smem + stage * KTILE;
+    const int kbase = kv_lo + it * TK;
+
+    // ---- phase A: S^T = K Q^T for this wave's 16 rows, softmax, P^T -> LDS ----
+    float4_t s[4][1];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) s[mt][0] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sp = 0; sp < KPAIRS; ++sp) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int row = mt * 16 + l16;
+        const uint4_t raw = *(const uint4_t*)(ks + row * KROW + swz<KROW>(4 * sp + grp, row) * 16);
+        const half8_t a0 = bytes8_to_op<FP8>(raw[0], raw[1]);
+        const half8_t a1 = bytes8_to_op<FP8>(raw[2], raw[3]);
+        s[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, q.hi[0][2 * sp], s[mt][0], 0, 0, 0);
+        s[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.hi[0][2 * sp + 1], s[mt][0], 0, 0, 0);
+        if constexpr (HILO) {
+          s[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, q.lo[0][2 * sp], s[mt][0], 0, 0, 0);
+          s[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.lo[0][2 * sp + 1], s[mt][0], 0, 0, 0);
+        }
+      }
+    }
+    half8_t pb[2][1];
+    {
+      // softmax_tile rescales sa.o (one dummy tile); the real O lives in phase B,
+      // which applies the per-row factor published below.
+      const float m_before = sa.m[0];
+      softmax_tile<DQK, 1, 1, HILO>(p, u, kbase, grp, q, s, sa, pb);
+      const float m_use = sa.m[0] == -INFINITY ? 0.f : sa.m[0];
+      if (grp == 0) alpha_lds[wave * 16 + l16] = __builtin_amdgcn_exp2f(m_before - m_use);
+    }
+    pt_lds[(wave * 2 + 0) * 64 + lane] = pb[0][0];
+    pt_lds[(wave * 2 + 1) * 64 + lane] = pb[1][0];
+    __syncthreads();
+
+    // ---- phase B: O^T[64 dims of this wave][all rows] += V^T P^T ----
+    {
+      float al[NTB];
+      bool grew = false;
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt) {
+        al[nt] = alpha_lds[nt * 16 + l16];
+        grew |= al[nt] != 1.f;
+      }
+      if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+#pragma unroll
+        for (int md = 0; md < MDW; ++md)
+#pragma unroll
+          for (int nt = 0; nt < NTB; ++nt) o[md][nt] *= al[nt];
+      }
+    }
+    const int jr = l16 >> 1;
+    const int hlf = lane & 1;
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      const int vrow = 32 * ks2 + (jr < 4 ? 4 * grp + jr : 16 + 4 * grp + (jr - 4));
+      half8_t va[MDW];
+#pragma unroll
+      for (int md = 0; md < MDW; ++md) {
+        const int chunk = wave * MDW + md;   // 16-byte chunk = 16 output dims
+        const uint8_t* addr = ks + vrow * KROW + swz<KROW>(chunk, vrow) * 16 + hlf * 8;
+        const int2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) int2_t*)(addr));
+        va[md] = bytes8_to_op<FP8>((uint32_t)raw[0], (uint32_t)raw[1]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt) {
+        const half8_t pbn = pt_lds[(nt * 2 + ks2) * 64 + lane];
+#pragma unroll
+        for (int md = 0; md < MDW; ++md)
+          o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[md], pbn, o[md][nt], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: row sums and lse from the owner waves, outputs per dim slice ----
+  const int H_q = p.num_q_heads;
+  {
+    const float lt = row_sum4(sa.l[0]);
+    const float lse_nat = lt > 0.f ? (sa.m[0] + __log2f(lt)) * LN2F : -INFINITY;
+    if (grp == 0) lrow_lds[wave * 16 + l16] = lt;
+    if (grp == 0 && q.ok[0]) {
+      const int tok = u.tok0 + q.tok[0];
+      if (u.split) p.part_lse[((int64_t)tok * p.max_chunks + c) * H_q + q.head[0]] = lse_nat;
+      else if (p.lse) p.lse[(int64_t)tok * H_q + q.head[0]] = lse_nat;
+    }
+  }
+  __syncthreads();
+  const int mode = p.scale_mode;
+  float4_t vsc[MDW];
+  if (mode == PA_SCALE_PER_CHANNEL) {
+#pragma unroll
+    for (int md = 0; md < MDW; ++md)
+      vsc[md] = *(const float4_t*)(p.v_scale + (int64_t)g * DV + (wave * MDW + md) * 16 + grp * 4);
+  } else {
+    const float v = p.v_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
+#pragma unroll
+    for (int md = 0; md < MDW; ++md) vsc[md] = float4_t{v, v, v, v};
+  }
+#pragma unroll
+  for (int nt = 0; nt < NTB; ++nt) {
+    const int r = u.row0 + nt * 16 + l16;
+    if (r >= u.rows_total) continue;
+    const float lt = lrow_lds[nt * 16 + l16];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float off = lt > 0.f ? KV_OFF : 0.f;
+    const int tok = u.tok0 + r / u.G;
+    const int h = g * u.G + r % u.G;
+    float* prow = u.split ? p.part_o + (((int64_t)tok * p.max_chunks + c) * H_q + h) * DV : nullptr;
+    uint16_t* orow = p.out + ((int64_t)tok * H_q + h) * DV;
+#pragma unroll
+    for (int md = 0; md < MDW; ++md) {
+      const int d = (wave * MDW + md) * 16 + grp * 4;
+      float4_t v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = fmaf(o[md][nt][i], inv, -off) * vsc[md][i];
+      if (u.split) {
+        *(float4_t*)(prow + d) = v;
+      } else {
+        const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *(int2_t*)(orow + d) = int2_t{(int)w0, (int)w1};
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------- merge --
 // One group of DV/4 lanes per (token, head) row; each lane owns 4 channels.
 template <int DV>
@@ -1045,6 +1287,12 @@ hipError_t launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <bool FP8, bool HILO>
+hipError_t launch_mla(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((paged_mla_kernel<FP8, HILO>), grid, dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int D, bool FP8, int NT, bool HILO>
 hipError_t launch_decode(const AttnParams& p, dim3 grid, hipStream_t stream) {
   hipLaunchKernelGGL((paged_decode_kernel<D, FP8, NT, HILO>), grid, dim3(64), 0, stream, p);
@@ -1062,6 +1310,8 @@ struct Entry {
 #define PA_ENTRY(DQK, DV, FP8, NT, NW, SH, HL, NS) \
   Entry{AttnConfig{DQK, DV, FP8, SH, NT, NW, HL, NS}, &launch_one<DQK, DV, FP8, NT, NW, SH, HL, NS>}
 #define PA_DEC(D, FP8, NT, HL) Entry{AttnConfig{D, D, FP8, false, NT, 1, HL, 0}, &launch_decode<D, FP8, NT, HL>}
+// the split-phase MLA kernel (128 rows, 8 waves) is marked nstage == 1
+#define PA_MLA(FP8, HL) Entry{AttnConfig{576, 512, FP8, true, 1, 8, HL, 1}, &launch_mla<FP8, HL>}
 
 #define PA_SET(D, FP8, HL)                                                                       \
   PA_DEC(D, FP8, 1, HL), PA_DEC(D, FP8, 2, HL), PA_ENTRY(D, D, FP8, 3, 1, false, HL, 2),            \
@@ -1072,8 +1322,7 @@ const Entry kTable[] = {
     PA_SET(64, true, false),    PA_SET(64, true, true),
     PA_SET(128, false, false), PA_SET(128, false, true),
     PA_SET(128, true, false),  PA_SET(128, true, true),
-    PA_ENTRY(576, 512, true, 1, 8, true, false, 2),  PA_ENTRY(576, 512, true, 1, 8, true, true, 2),
-    PA_ENTRY(576, 512, false, 1, 8, true, false, 2), PA_ENTRY(576, 512, false, 1, 8, true, true, 2),
+    PA_MLA(true, false), PA_MLA(true, true), PA_MLA(false, false), PA_MLA(false, true),
 };
 
 const Entry* find_entry(const AttnConfig& c) {

@@ -159,7 +159,7 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   if (shared) {
     cfg.nt = 1;
     cfg.nw = 8;
-    cfg.nstage = 2;
+    cfg.nstage = 1;  // split-phase MLA kernel
   } else if (rows_max <= 64) {
     cfg.nt = (int)ceil_div(rows_max, 16);
     cfg.nw = 1;
