@@ -405,6 +405,122 @@ __device__ __forceinline__ void load_query(const AttnParams& p, const Unit& u, i
   }
 }
 
+// Split form of load_query for short heads (D <= 128), used where the first KV
+// tile should be in flight while the query is processed: query_fetch issues
+// every query and scale load, then the caller issues its tile loads, and
+// query_finish does the arithmetic once the query bytes are in.  Loads of one
+// wave complete in order, so the query is waited for without waiting for the
+// tile.  The fetch is branch-free (rows past the unit re-read the unit's first
+// row, bf16 rows re-read their first 32 bytes where fp32 rows read 64, scale
+// loads that the mode does not use re-read the query) so that the compiler's
+// wait counts stay exact.  The result equals load_query's.
+template <int DQK, int NT>
+struct QRaw {
+  static constexpr int KPAIRS = DQK / 64;
+  uint4_t x[NT][KPAIRS][4];   // 16 bf16 (first two vectors) or 16 fp32 per (row, pair)
+  float4_t ksc[KPAIRS][4];    // per-channel K scales of this lane's 16 dims per pair
+  float k_uniform;            // per-tensor or per-head K scale
+};
+
+template <int DQK, int NT>
+__device__ __forceinline__ void query_fetch(const AttnParams& p, const Unit& u, int g, int row_base,
+                                            int lane, QRaw<DQK, NT>& raw) {
+  constexpr int KPAIRS = DQK / 64;
+  static_assert(KPAIRS <= 2, "query_fetch holds the whole row in registers");
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int mode = p.scale_mode;
+  const bool f32 = p.q_is_f32;
+  const int esize = f32 ? 4 : 2;
+  const uint8_t* qrow[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r0 = row_base + nt * 16 + l16;
+    const int r = r0 < u.rows_total ? r0 : u.row0;
+    const int64_t qoff = (int64_t)(u.tok0 + r / u.G) * p.q_row_stride + (int64_t)(g * u.G + r % u.G) * DQK;
+    qrow[nt] = (const uint8_t*)p.q + qoff * esize;
+  }
+#pragma unroll
+  for (int sp = 0; sp < KPAIRS; ++sp) {
+    const uint8_t* sc = mode == PA_SCALE_PER_CHANNEL
+                            ? (const uint8_t*)(p.k_scale + (int64_t)g * DQK + 64 * sp + 16 * grp)
+                            : qrow[0];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) raw.ksc[sp][v] = *(const float4_t*)(sc + 16 * v);
+  }
+  raw.k_uniform = p.k_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int sp = 0; sp < KPAIRS; ++sp) {
+      const uint8_t* src = qrow[nt] + (64 * sp + 16 * grp) * esize;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) raw.x[nt][sp][v] = *(const uint4_t*)(src + 16 * (f32 ? v : (v & 1)));
+    }
+}
+
+template <int DQK, int NT, bool HILO>
+__device__ __forceinline__ void query_finish(const AttnParams& p, const Unit& u, int g, int row_base,
+                                             int lane, float kv_off, const QRaw<DQK, NT>& raw,
+                                             QRows<DQK, NT, HILO>& q) {
+  constexpr int KPAIRS = DQK / 64;
+  const int l16 = lane & 15;
+  const int mode = p.scale_mode;
+  const bool fold_channel = mode == PA_SCALE_PER_CHANNEL;
+  const float k_uniform = fold_channel ? 1.f : raw.k_uniform;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = row_base + nt * 16 + l16;
+    q.ok[nt] = r < u.rows_total;
+    const int t = q.ok[nt] ? r / u.G : 0;
+    q.tok[nt] = t;
+    q.head[nt] = g * u.G + (q.ok[nt] ? r % u.G : 0);
+    float xq[KPAIRS][16];
+    float amax = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < KPAIRS; ++sp) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float x;
+        if (p.q_is_f32) {
+          // (the element goes through a scalar: bit-casting a vector element
+          // in place made this compiler read lane 0 of the vector)
+          const uint32_t bits = raw.x[nt][sp][e / 4][e % 4];
+          x = __builtin_bit_cast(float, bits);
+        } else {
+          const uint32_t w = raw.x[nt][sp][e / 8][(e % 8) / 2];
+          x = bf16_to_f32((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
+        }
+        if (fold_channel) x *= p.qk_mult * raw.ksc[sp][e / 4][e % 4];
+        x = q.ok[nt] ? x : 0.f;
+        xq[sp][e] = x;
+        amax = fmaxf(amax, fabsf(x));
+      }
+    }
+    amax = row_max4(amax);
+    int ex = 0;
+    if (amax > 0.f) (void)frexpf(amax, &ex);     // amax < 2^ex
+    const int k2 = min(max(15 - ex, -120), 120);
+    const float up = ldexpf(1.f, k2);
+    q.row_mult[nt] = ldexpf(1.f, -k2) * (fold_channel ? 1.f : p.qk_mult * k_uniform);
+    float qsum = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < KPAIRS; ++sp)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float v = xq[sp][e] * up;
+        const _Float16 h = (_Float16)v;
+        q.hi[nt][2 * sp + e / 8][e % 8] = h;
+        qsum += (float)h;
+        if constexpr (HILO) {
+          const _Float16 l = (_Float16)(v - (float)h);
+          q.lo[nt][2 * sp + e / 8][e % 8] = l;
+          qsum += (float)l;
+        }
+      }
+    q.kbias[nt] = kv_off * row_sum4(qsum) * q.row_mult[nt];
+  }
+}
+
 // Online-softmax state of one wave: O^T accumulators (lane holds dims
 // 16*md + 4*grp + i of row l16), running max (log2 units) and denominator.
 template <int NT, int MD>
@@ -804,15 +920,18 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void paged_attn_kernel(At
 
 // -------------------------------------------------------- decode attention --
 //
-// One wave per unit; KV tiles are staged in registers with plain, row-coalesced
+// KS waves per unit: wave w takes tiles w, w + KS, ... of the unit's key range
+// and the waves merge their softmax states through LDS at the end, so a unit
+// of n tiles finishes in about n / KS tile times (short units fill the tail of
+// the dispatch).  KV tiles are staged in registers with plain, row-coalesced
 // global loads (the compiler tracks their completion).  At the top of each
-// iteration the arrived tile is written to a per-wave LDS tile and the same
+// iteration the arrived tile is written to the wave's LDS tile and the same
 // registers immediately take the next tile, so every load has a whole
 // iteration to arrive while the register file, not LDS, holds the bytes in
 // flight.  K is then read back in the MFMA A-operand layout, V transposed.
 
-template <int D, bool FP8, int NT, bool HILO>
-__global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnParams p) {
+template <int D, bool FP8, int NT, bool HILO, int KS>
+__global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnParams p) {
   constexpr int KPAIRS = D / 64;
   constexpr int MD = D / 16;
   constexpr int CPR = D / 16;            // 16-byte chunks per row
@@ -820,11 +939,14 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnP
   constexpr int NLD = TK / RPL;          // loads per tile (K or V)
   constexpr float KV_OFF = FP8 ? 0.f : 1152.f;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t ktile[TK * D];
-  __shared__ __attribute__((aligned(1024))) uint8_t vtile[TK * D];
+  __shared__ __attribute__((aligned(1024))) uint8_t kvlds[KS][2][TK * D];   // per wave: K tile, V tile
   __shared__ float vscale_lds[D];
+  __shared__ float mrg_m[KS][16 * NT], mrg_l[KS][16 * NT];
 
   const int lane = threadIdx.x & 63;
+  const int wv = KS > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
+  uint8_t* const ktile = kvlds[wv][0];
+  uint8_t* const vtile = kvlds[wv][1];
   const int l16 = lane & 15;
   const int grp = lane >> 4;
   // grid = (B * H_kv, row tiles, chunks): chunk-major, so the empty units of
@@ -833,17 +955,20 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnP
   const int g = (int)blockIdx.x % p.num_kv_heads;
   const int rt = p.row_tiles - 1 - (int)blockIdx.y;  // long (late-token) row tiles first
   const int c = (int)blockIdx.z;
+  const int32_t* table_row = p.block_table + (int64_t)b * p.max_pages_per_seq;
+  const int page_shift = p.page_shift;
+
+  // Page-id window: lane l holds the physical page of page index pw_base + l.
+  // The first window is read before the request length is known, in parallel
+  // with it (entries past the request's last page are read, from within its
+  // block-table row, but never used as addresses).
+  int pw_base = (p.chunk_size > 0 ? c * p.chunk_size : 0) >> page_shift;
+  int pw_val = table_row[min(pw_base + lane, p.max_pages_per_seq - 1)];
 
   Unit u;
   if (!unit_setup<16 * NT>(p, b, rt, c, u)) return;
-  const int32_t* table_row = p.block_table + (int64_t)b * p.max_pages_per_seq;
   const int key_end = u.key_end, kv_lo = u.kv_lo, n_tiles = u.n_tiles;
-  const int page_shift = p.page_shift;
-  const int last_page = n_tiles > 0 ? (key_end - 1) >> page_shift : 0;  // never read past it
-
-  // Page-id window: lane l holds the physical page of page index pw_base + l.
-  int pw_base = -(1 << 30);
-  int pw_val = 0;
+  const int last_page = n_tiles > 0 ? (key_end - 1) >> page_shift : 0;  // never used past it
   const bool one_page = page_shift >= 6;
   const int ld_row = lane / CPR, ld_chunk = lane % CPR;
   const int64_t k_lane = (int64_t)ld_row * p.k_stride_token + 16 * ld_chunk;
@@ -858,7 +983,7 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnP
     const int pg_last = min(pg0 + 3, last_page);
     if (pg0 < pw_base || pg_last > pw_base + 63) {
       pw_base = pg0;
-      pw_val = table_row[min(pg0 + lane, last_page)];
+      pw_val = load_i32_sync(table_row + min(pg0 + lane, last_page));  // waits here, not at a join
     }
     const int pp0 = __builtin_amdgcn_readlane(pw_val, pg0 - pw_base);
     if (one_page && kbase + TK <= key_end) {
@@ -891,24 +1016,41 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnP
     }
   };
 
-  if (n_tiles > 0) load_tile(0);
-  // V scales go to LDS while the first tile and the query are in flight.
-  const bool fold_channel = p.scale_mode == PA_SCALE_PER_CHANNEL;
-  float vs_lane[D / 64];
-  if (fold_channel) {
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) vs_lane[i] = p.v_scale[(int64_t)g * D + lane + 64 * i];
-  }
-  QRows<D, NT, HILO> q;
-  load_query<D, NT, HILO>(p, u, g, u.row0, lane, KV_OFF, q);
-  if (fold_channel) {
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) vscale_lds[lane + 64 * i] = vs_lane[i];
-  }
   SoftmaxState<NT, MD> st;
   softmax_init(st);
+  if (n_tiles == 0) {
+    // No visible key in this unit: (0, -inf) rows, written by wave 0.
+    if (wv > 0) return;
+    QRows<D, NT, HILO> q;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int r = u.row0 + nt * 16 + l16;
+      q.ok[nt] = r < u.rows_total;
+      q.tok[nt] = q.ok[nt] ? r / u.G : 0;
+      q.head[nt] = g * u.G + (q.ok[nt] ? r % u.G : 0);
+    }
+    float4_t vsc[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md) vsc[md] = float4_t{0.f, 0.f, 0.f, 0.f};
+    write_rows<D, D, NT, HILO>(p, u, g, c, lane, KV_OFF, q, st, vsc);
+    return;
+  }
 
-  for (int it = 0; it < n_tiles; ++it) {
+  // Query (and its scales) first: it arrives before the first tile, so it is
+  // processed while that tile is still in flight.  Every wave loads a valid
+  // first tile (a surplus wave of a short unit loads the last one and skips
+  // it), so no path skips the load and the wait counts stay exact.
+  QRaw<D, NT> qraw;
+  query_fetch<D, NT>(p, u, g, u.row0, lane, qraw);
+  const bool fold_channel = p.scale_mode == PA_SCALE_PER_CHANNEL;
+  float vs_lane[D / 64];   // per-channel V scales (other modes re-read the first one)
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) vs_lane[i] = p.v_scale[fold_channel ? (int64_t)g * D + lane + 64 * i : 0];
+  load_tile(min(wv, n_tiles - 1));
+  QRows<D, NT, HILO> q;
+  query_finish<D, NT, HILO>(p, u, g, u.row0, lane, KV_OFF, qraw, q);
+
+  for (int it = wv; it < n_tiles; it += KS) {
     const int kbase = kv_lo + it * TK;
     // tile `it` -> LDS (swizzled rows); its registers take tile it + 1
 #pragma unroll
@@ -917,7 +1059,7 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnP
       *(uint4_t*)(ktile + row * D + swz<D>(ld_chunk, row) * 16) = kr[j];
       *(uint4_t*)(vtile + row * D + swz<D>(ld_chunk, row) * 16) = vr[j];
     }
-    if (it + 1 < n_tiles) load_tile(it + 1);
+    if (it + KS < n_tiles) load_tile(it + KS);
 
     // ---- S^T = K Q^T: 4 x NT independent accumulator chains ----
     float4_t s[4][NT];
@@ -956,6 +1098,61 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnP
     half8_t pb[2][NT];
     softmax_tile<D, NT, MD, HILO>(p, u, kbase, grp, q, s, st, pb);
     pv_tile<FP8, NT, MD, D>(vtile, lane, pb, st);
+  }
+
+  if (fold_channel && wv == 0) {
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) vscale_lds[lane + 64 * i] = vs_lane[i];
+  }
+
+  if constexpr (KS > 1) {
+    // Merge the KS partial states of the unit: common reference max M per row,
+    // each wave's (O, l) weighted by 2^(m_w - M); wave 0 sums and writes.
+    float lt[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      lt[nt] = row_sum4(st.l[nt]);
+      if (grp == 0) {
+        mrg_m[wv][nt * 16 + l16] = st.m[nt];
+        mrg_l[wv][nt * 16 + l16] = lt[nt];
+      }
+    }
+    __syncthreads();  // also: every wave is done with its K/V tiles
+    float f[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float mm = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < KS; ++w) mm = fmaxf(mm, mrg_m[w][nt * 16 + l16]);
+      float lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < KS; ++w) {
+        const float mw = mrg_m[w][nt * 16 + l16];
+        lsum += mw == -INFINITY ? 0.f : mrg_l[w][nt * 16 + l16] * __builtin_amdgcn_exp2f(mw - mm);
+      }
+      f[nt] = st.m[nt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m[nt] - mm);
+      st.m[nt] = mm;
+      st.l[nt] = grp == 0 ? lsum : 0.f;   // write_rows sums the four lane groups
+    }
+    // O of wave w > 0 -> its own K/V tile area (lane-major float4s)
+    float4_t* obuf = (float4_t*)kvlds[wv][0];
+    if (wv > 0) {
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) obuf[(md * NT + nt) * 64 + lane] = st.o[md][nt] * f[nt];
+    }
+    __syncthreads();
+    if (wv > 0) return;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float4_t acc = st.o[md][nt] * f[nt];
+#pragma unroll
+        for (int w = 1; w < KS; ++w) acc += ((const float4_t*)kvlds[w][0])[(md * NT + nt) * 64 + lane];
+        st.o[md][nt] = acc;
+      }
   }
 
   float4_t vsc[MD];
@@ -1293,9 +1490,9 @@ hipError_t launch_mla(const AttnParams& p, dim3 grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool FP8, int NT, bool HILO>
+template <int D, bool FP8, int NT, bool HILO, int KS>
 hipError_t launch_decode(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((paged_decode_kernel<D, FP8, NT, HILO>), grid, dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((paged_decode_kernel<D, FP8, NT, HILO, KS>), grid, dim3(64 * KS), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1309,12 +1506,16 @@ struct Entry {
 // nstage == 0 marks the register-staged single-wave decode kernel.
 #define PA_ENTRY(DQK, DV, FP8, NT, NW, SH, HL, NS) \
   Entry{AttnConfig{DQK, DV, FP8, SH, NT, NW, HL, NS}, &launch_one<DQK, DV, FP8, NT, NW, SH, HL, NS>}
-#define PA_DEC(D, FP8, NT, HL) Entry{AttnConfig{D, D, FP8, false, NT, 1, HL, 0}, &launch_decode<D, FP8, NT, HL>}
+// (for it, nw counts the waves that split one unit's key range)
+#define PA_DEC(D, FP8, NT, HL, KS) \
+  Entry{AttnConfig{D, D, FP8, false, NT, KS, HL, 0}, &launch_decode<D, FP8, NT, HL, KS>}
 // the split-phase MLA kernel (128 rows, 8 waves) is marked nstage == 1
 #define PA_MLA(FP8, HL) Entry{AttnConfig{576, 512, FP8, true, 1, 8, HL, 1}, &launch_mla<FP8, HL>}
 
 #define PA_SET(D, FP8, HL)                                                                       \
-  PA_DEC(D, FP8, 1, HL), PA_DEC(D, FP8, 2, HL), PA_ENTRY(D, D, FP8, 3, 1, false, HL, 2),            \
+  PA_DEC(D, FP8, 1, HL, 1), PA_DEC(D, FP8, 1, HL, 2), PA_DEC(D, FP8, 1, HL, 4),                    \
+      PA_DEC(D, FP8, 2, HL, 1), PA_DEC(D, FP8, 2, HL, 2), PA_DEC(D, FP8, 2, HL, 4),                 \
+      PA_ENTRY(D, D, FP8, 3, 1, false, HL, 2),                                                      \
       PA_ENTRY(D, D, FP8, 4, 1, false, HL, 2), PA_ENTRY(D, D, FP8, 2, 4, false, HL, 2)
 
 const Entry kTable[] = {

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "pa_internal.h"
@@ -80,6 +81,26 @@ int32_t check_problem(const pa_problem* p) {
 int64_t max_chunks_of(const pa_problem* p) {
   if (p->chunk_size <= 0) return 1;
   return std::max<int64_t>(1, ceil_div((int64_t)p->max_kv_len + p->max_q_len, p->chunk_size));
+}
+
+// Waves that split one unit's key range in the register-staged decode kernel.
+// Units are (request, KV head, row tile, chunk).  Each wave of a unit pays
+// the unit's start-up latency (lengths, page ids, first tile), so a unit is
+// split only when the units cannot fill the 2048 (NT = 1) or 1024 (NT = 2)
+// resident waves, and while every wave keeps at least four tiles.
+// PAGEDATTN_DECODE_WAVES (1, 2 or 4) overrides the choice, for tuning.
+int decode_split_waves(const pa_problem* p, int nt) {
+  if (const char* env = std::getenv("PAGEDATTN_DECODE_WAVES")) {
+    const int v = std::atoi(env);
+    if (v == 1 || v == 2 || v == 4) return v;
+  }
+  const int64_t keys = p->chunk_size > 0 ? p->chunk_size : (int64_t)p->max_kv_len + p->max_q_len;
+  const int64_t tiles = ceil_div(keys, 64);
+  const int64_t units = (int64_t)p->batch * p->num_kv_heads * max_chunks_of(p);
+  const int64_t slots = nt == 1 ? 2048 : 1024;
+  int ks = 1;
+  while (ks < 4 && tiles >= 8 * ks && units * ks * 2 <= slots) ks *= 2;
+  return ks;
 }
 
 struct WorkspaceLayout {
@@ -165,6 +186,7 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
     cfg.nw = 1;
     // up to 32 rows: register-staged decode kernel; more rows: LDS-staged
     cfg.nstage = cfg.nt <= 2 ? 0 : 2;
+    if (cfg.nstage == 0) cfg.nw = decode_split_waves(p, cfg.nt);
   } else {
     cfg.nt = 2;
     cfg.nw = 4;
@@ -172,7 +194,7 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   }
   if (!pa::attention_supported(cfg))
     return fail(PA_ERR_UNSUPPORTED, "no compiled kernel for this configuration");
-  const int64_t rows_per_wg = 16LL * cfg.nt * cfg.nw;
+  const int64_t rows_per_wg = 16LL * cfg.nt * (cfg.nstage == 0 ? 1 : cfg.nw);  // decode: nw splits keys
   const int64_t row_tiles = ceil_div(rows_max, rows_per_wg);
   const int64_t max_chunks = max_chunks_of(p);
   if (row_tiles > 65535 || max_chunks > 65535 || row_tiles * max_chunks > 0x7fffffffLL)

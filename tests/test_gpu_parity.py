@@ -156,6 +156,32 @@ def test_edge_case_parity(case):
     compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what=case)
 
 
+# Decode units whose key range is split across 2 or 4 waves of a workgroup
+# (states merged in LDS), forced through the tuning override; a request with
+# fewer tiles than waves leaves some waves empty.
+SPLIT_WAVE_CASES = {
+    "g4_q1_chunk512": dict(num_q_heads=8, num_kv_heads=2, q_lens=[1, 1, 1], seq_lens_kv=[1000, 64, 2],
+                           decode=True, chunk_size=512),
+    "g8_q3_nochunk": dict(num_q_heads=16, num_kv_heads=2, q_lens=[3, 3], seq_lens_kv=[900, 130],
+                          decode=True, chunk_size=0),
+    "d64_fp8_chunk256": dict(head_dim_qk=64, head_dim_v=64, kv_dtype="fp8_e4m3", scale_mode="tensor",
+                             q_lens=[2, 2], seq_lens_kv=[700, 40], decode=True, chunk_size=256),
+}
+
+
+@pytest.mark.parametrize("waves", [2, 4])
+@pytest.mark.parametrize("case", sorted(SPLIT_WAVE_CASES))
+def test_decode_split_waves_parity(case, waves, monkeypatch):
+    need_gpu()
+    monkeypatch.setenv("PAGEDATTN_DECODE_WAVES", str(waves))
+    w = _edge("split_" + case, **SPLIT_WAVE_CASES[case])
+    announce(f"decode split waves={waves} {case}")
+    _, (out, lse) = _run(w)
+    O_ref, lse_ref = oracle.attention(w)
+    n = int(w.q_lens.sum())
+    compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what=f"{case} waves={waves}")
+
+
 # ------------------------------------------------------------------ merge --
 
 def test_split_kv_merge_against_oracle_partials():
