@@ -36,6 +36,8 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef int int2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
 
 constexpr int TK = 64;  // keys per KV tile
 constexpr float LAZY_LOG2 = 8.f;  // softmax reference-max slack (log2 units)
@@ -525,7 +527,7 @@ __device__ __forceinline__ void query_finish(const AttnParams& p, const Unit& u,
 // 16*md + 4*grp + i of row l16), running max (log2 units) and denominator.
 template <int NT, int MD>
 struct SoftmaxState {
-  float4_t o[MD][NT];
+  float4_t o[MD > 0 ? MD : 1][NT];   // MD == 0: no O here (the caller keeps it elsewhere)
   float m[NT], l[NT];
 };
 
@@ -597,14 +599,16 @@ __device__ __forceinline__ void softmax_tile(const AttnParams& p, const Unit& u,
       }
     st.l[nt] = st.l[nt] * alpha[nt] + ls;
   }
-  bool grew = false;
+  if constexpr (MD > 0) {
+    bool grew = false;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) grew |= alpha[nt] != 1.f;
-  if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+    for (int nt = 0; nt < NT; ++nt) grew |= alpha[nt] != 1.f;
+    if (__builtin_amdgcn_ballot_w64(grew) != 0) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int md = 0; md < MD; ++md) st.o[md][nt] *= alpha[nt];
+        for (int md = 0; md < MD; ++md) st.o[md][nt] *= alpha[nt];
+    }
   }
 }
 
@@ -1168,41 +1172,61 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
 // ------------------------------------------------------- MLA latent decode --
 //
 // Shared 576/512 latent rows (V = first 512 bytes of each K row), one KV head,
-// 128 packed query rows per workgroup of 8 waves.  The per-wave state is kept
-// small by splitting the two contractions differently:
-//   phase A  wave w computes S^T = K Q^T and the online softmax for rows
-//            16w..16w+15 (its query rows stay in registers), and writes P^T to
-//            LDS already in the B-operand layout of the PV MFMA;
-//   phase B  wave w accumulates O^T for output dims 64w..64w+63 of all 128
-//            rows, reading every wave's P^T and per-row rescale factors.
-// KV tiles (64 keys x 576 bytes) travel by LDS DMA as in the shared-tile kernel.
+// NW waves and 16 * NW packed query rows per workgroup (8 waves and 128 rows;
+// 4 and 64 when Q needs hi + lo parts).  Per 64-key tile:
+//   staging  the raw tile (64 x 576 bytes) arrives by LDS DMA, two tiles ahead;
+//   convert  the waves turn its first 512 dims into an f16 tile in LDS once
+//            (each wave an equal share), instead of every wave converting the
+//            whole tile for its own rows;
+//   phase A  wave w computes S^T = K Q^T for rows 16w..16w+15 (its query rows
+//            stay in registers; K read as f16 from the converted tile, the 64
+//            rope dims converted from the raw tile), runs the online softmax
+//            and writes P^T to LDS in the B-operand layout of the PV MFMA;
+//   phase B  wave w accumulates O^T for output dims (512 / NW) * w onwards of
+//            all rows: V^T comes from the f16 tile by the 16-bit LDS transpose
+//            read, P^T and the per-row rescale factors from phase A.
+
+// XOR swizzle of the 16-byte chunks of a 1024-byte f16 key row: the 16 keys of
+// an MFMA operand read land on 16 distinct bank groups, and the 8 keys that a
+// transposed read pairs up land on 8 distinct 32-byte groups.
+__device__ __forceinline__ int kf_swz(int chunk, int key) {
+  return chunk ^ (((key & 7) << 1) | ((key >> 3) & 1));
+}
+
+constexpr int MLA_WAVES = 4;  // waves (= 16-row tiles) per MLA workgroup
 
 template <bool FP8, bool HILO>
-__global__ __launch_bounds__(512, 1) void paged_mla_kernel(AttnParams p) {
-  constexpr int DQK = 576, DV = 512, NW = 8, ROWS = 128;
+__global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams p) {
+  constexpr int DQK = 576, DV = 512, NW = MLA_WAVES;
+  constexpr int NTA = 1;                          // 16-row tiles per wave in phase A
+  constexpr int ROWS = 16 * NTA * NW;             // 128 (64 with hi + lo query parts)
+  constexpr int NTB = ROWS / 16;                  // row tiles in phase B
+  constexpr int MDW = DV / 16 / NW;               // output-dim tiles per wave
   constexpr int KROW = DQK;
-  constexpr int KTILE = TK * KROW;                // 36 KB
-  constexpr int KCH = KTILE / 16;
-  constexpr int KCPR = KROW / 16;
-  constexpr int KPAIRS = DQK / 64;                // 9
-  constexpr int K_DMA = (KCH + 64 * NW - 1) / (64 * NW);
-  constexpr int MDW = DV / 16 / NW;               // 4 output-dim tiles per wave
-  constexpr int NTB = ROWS / 16;                  // 8 row tiles in phase B
+  constexpr int KTILE = TK * KROW;                // 36 KB raw tile
+  constexpr int KCPR = KROW / 16;                 // 36 chunks per raw row
+  constexpr int K_BLK = TK * KCPR / 64;           // 36 DMA instructions per tile
+  constexpr int K_DMA = (K_BLK + NW - 1) / NW;    // per wave (waves below K_BLK % NW issue one more)
+  constexpr int FROW = DV * 2;                    // 1024-byte f16 row
   constexpr float KV_OFF = FP8 ? 0.f : 1152.f;
+  static_assert(K_BLK * 64 == TK * KCPR, "raw tile is whole DMA blocks");
+  static_assert(K_BLK % NW == 0 || K_BLK % NW == NW / 2, "per-wave DMA count is K_DMA or K_DMA - 1");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * KTILE];
-  __shared__ __attribute__((aligned(16))) half8_t pt_lds[NTB * 2 * 64];   // P^T operands
+  __shared__ __attribute__((aligned(1024))) uint8_t kst[2 * KTILE];      // raw tiles
+  __shared__ __attribute__((aligned(1024))) uint8_t kf[TK * FROW];       // f16 dims 0..511
+  __shared__ __attribute__((aligned(16))) half8_t pt_lds[NTB * 2 * 64];  // P^T operands
   __shared__ float alpha_lds[ROWS];
   __shared__ float lrow_lds[ROWS];
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int l16 = lane & 15;
   const int grp = lane >> 4;
   const int b = (int)blockIdx.z;
   const int g = (int)blockIdx.y;
-  const int rt = p.row_tiles - 1 - (int)(blockIdx.x / p.max_chunks);
-  const int c = (int)(blockIdx.x % p.max_chunks);
+  // the row tiles of one chunk are adjacent, so they share its KV tiles in L2
+  const int rt = p.row_tiles - 1 - (int)(blockIdx.x % p.row_tiles);
+  const int c = (int)(blockIdx.x / p.row_tiles);
 
   Unit u;
   if (!unit_setup<ROWS>(p, b, rt, c, u)) return;
@@ -1214,15 +1238,9 @@ __global__ __launch_bounds__(512, 1) void paged_mla_kernel(AttnParams p) {
   int pw_val = 0;
   const bool one_page = page_shift >= 6;
   const bool fast_addr = one_page && (int64_t)TK * p.k_stride_token < (1LL << 30);
-  uint32_t koff[K_DMA];
-#pragma unroll
-  for (int j = 0; j < K_DMA; ++j) {
-    const int ch = (j * NW + wave) * 64 + lane;
-    const int row = ch / KCPR;
-    koff[j] = (uint32_t)(row * p.k_stride_token + swz<KROW>(ch % KCPR, row) * 16);
-  }
-  const uint32_t smem_base = lds_addr(smem);
+  const uint32_t kst_base = lds_addr(kst);
 
+  // Raw tile `tile` -> stage `stage` (this wave's K_DMA instructions).
   auto issue_tile = [&](int tile, int stage) {
     const int kbase = kv_lo + tile * TK;
     const int pg0 = kbase >> page_shift;
@@ -1232,13 +1250,19 @@ __global__ __launch_bounds__(512, 1) void paged_mla_kernel(AttnParams p) {
       pw_val = load_i32_sync(table_row + min(pg0 + lane, last_page));
     }
     const int pp0 = __builtin_amdgcn_readlane(pw_val, pg0 - pw_base);
-    const uint32_t kdst = smem_base + stage * KTILE;
+    const uint32_t kdst = kst_base + stage * KTILE;
     if (fast_addr && kbase + TK <= key_end) {
       const uint8_t* kb = p.k_cache + (int64_t)pp0 * p.k_stride_page + (int64_t)g * p.k_stride_head +
                           (int64_t)(kbase & ((1 << page_shift) - 1)) * p.k_stride_token;
 #pragma unroll
-      for (int j = 0; j < K_DMA; ++j)
-        if ((j * NW + wave) * 64 < KCH) dma16_s(koff[j], kb, kdst + (j * NW + wave) * 1024);
+      for (int j = 0; j < K_DMA; ++j) {
+        const int blk = j * NW + wave;
+        if (blk >= K_BLK) break;
+        const int ch = blk * 64 + lane;
+        const int row = ch / KCPR;
+        dma16_s((uint32_t)(row * p.k_stride_token + swz<KROW>(ch - row * KCPR, row) * 16), kb,
+                kdst + blk * 1024);
+      }
       return;
     }
     int pp1 = pp0, pp2 = pp0, pp3 = pp0;
@@ -1250,72 +1274,170 @@ __global__ __launch_bounds__(512, 1) void paged_mla_kernel(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < K_DMA; ++j) {
       const int blk = j * NW + wave;
-      if (blk * 64 < KCH) {
-        const int ch = blk * 64 + lane;
-        const int row = ch / KCPR;
-        const int key = min(kbase + row, key_end - 1);
-        const uint8_t* src = paged_row(p.k_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3), key,
-                                       page_shift, g, p.k_stride_page, p.k_stride_head, p.k_stride_token) +
-                             swz<KROW>(ch % KCPR, row) * 16;
-        dma16(src, kdst + blk * 1024);
-      }
+      if (blk >= K_BLK) break;
+      const int ch = blk * 64 + lane;
+      const int row = ch / KCPR;
+      const int key = min(kbase + row, key_end - 1);
+      const uint8_t* src = paged_row(p.k_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3), key,
+                                     page_shift, g, p.k_stride_page, p.k_stride_head, p.k_stride_token) +
+                           swz<KROW>(ch % KCPR, row) * 16;
+      dma16(src, kdst + blk * 1024);
     }
   };
 
   if (n_tiles > 0) issue_tile(0, 0);
+  if (n_tiles > 1) issue_tile(1, 1);
 
-  QRows<DQK, 1, HILO> q;
-  load_query<DQK, 1, HILO>(p, u, g, u.row0 + wave * 16, lane, KV_OFF, q);
-  SoftmaxState<1, 1> sa;   // phase-A row state (m, l); its o is unused
+  QRows<DQK, NTA, HILO> q;
+  load_query<DQK, NTA, HILO>(p, u, g, u.row0 + wave * 16 * NTA, lane, KV_OFF, q);
+  SoftmaxState<NTA, 0> sa;   // phase-A row state (m, l); O lives in phase B
   softmax_init(sa);
-  float4_t o[MDW][NTB];    // phase-B accumulators: dims 64*wave + 16*md + 4*grp + i, row 16*nt + l16
+  float4_t o[MDW][NTB];      // dims 16*(MDW*wave + md) + 4*grp + i, row 16*nt + l16
 #pragma unroll
   for (int md = 0; md < MDW; ++md)
 #pragma unroll
     for (int nt = 0; nt < NTB; ++nt) o[md][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Per-lane LDS offsets, hoisted so that each access below is a base plus a
+  // compile-time offset (kf_swz only permutes the low four chunk bits).
+  //  convert: raw read of key NW*i + wave, chunk lane/2 (swz<576> depends on
+  //           key % 32, so on i % CV_RP); f16 write of chunk lane (kf_swz
+  //           depends on key % 16, so on i % CV_WP)
+  constexpr int CV_RP = 32 / NW, CV_WP = 16 / NW;
+  int cv_rd[CV_RP], cv_wr[CV_WP];
+#pragma unroll
+  for (int i = 0; i < CV_RP; ++i) {
+    const int key = i * NW + wave;
+    cv_rd[i] = key * KROW + swz<KROW>(lane >> 1, key) * 16 + (lane & 1) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < CV_WP; ++i) {
+    const int key = i * NW + wave;
+    cv_wr[i] = key * FROW + kf_swz(lane, key) * 16;
+  }
+  //  phase A: key l16 (+16mt), f16 chunk 8*(sp & 1) + 2grp + h (+16 * (sp >> 1))
+  int qa_off[2][2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) qa_off[par][h] = l16 * FROW + kf_swz(8 * par + 2 * grp + h, l16) * 16;
+  //  phase B: transposed reads; lanes 4j..4j+3 of a 16-lane group give key j
+  int vb_off[MDW];
+  {
+    const int tr_j = l16 >> 2, tr_q = l16 & 3;
+    const int kA = 4 * grp + tr_j;   // kf_swz depends on the key's low four bits only
+#pragma unroll
+    for (int md = 0; md < MDW; ++md)
+      vb_off[md] = kA * FROW + kf_swz(2 * (wave * MDW + md) + (tr_q >> 1), kA) * 16 + (tr_q & 1) * 8;
+  }
+
   for (int it = 0; it < n_tiles; ++it) {
     const int stage = it & 1;
-    wait_vmcnt<0>();
-    __syncthreads();  // tile landed everywhere; phase B of it - 1 is done with P^T and the stage
-    if (it + 1 < n_tiles) issue_tile(it + 1, stage ^ 1);
-    const uint8_t* ks = smem + stage * KTILE;
+    // this wave's DMA of tile it + 1 (K_DMA or K_DMA - 1 instructions) may stay in flight
+    if (it + 1 >= n_tiles) wait_vmcnt<0>();
+    else if ((K_DMA - 1) * NW + wave < K_BLK) wait_vmcnt<K_DMA>();
+    else wait_vmcnt<K_DMA - 1>();
+    __syncthreads();  // B0: tile `it` landed for all waves; phase B of it - 1 is done with kf / pt
+    const uint8_t* ks = kst + stage * KTILE;
     const int kbase = kv_lo + it * TK;
 
-    // ---- phase A: S^T = K Q^T for this wave's 16 rows, softmax, P^T -> LDS ----
-    float4_t s[4][1];
+    // ---- convert dims 0..511 of the raw tile to f16 (wave w: keys NW*i + w,
+    //      lane l: f16 chunk l = dims 8l .. 8l + 7) ----
+    {
+      int2_t raw[TK / NW];   // every read in flight before the first conversion
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) s[mt][0] = float4_t{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < TK / NW; ++i)
+        raw[i] = *(const int2_t*)(ks + cv_rd[i % CV_RP] + (i / CV_RP) * (CV_RP * NW * KROW));
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int sp = 0; sp < KPAIRS; ++sp) {
+      for (int i = 0; i < TK / NW; ++i)
+        *(half8_t*)(kf + cv_wr[i % CV_WP] + (i / CV_WP) * (CV_WP * NW * FROW)) =
+            bytes8_to_op<FP8>((uint32_t)raw[i][0], (uint32_t)raw[i][1]);
+    }
+    __syncthreads();  // B1: f16 tile complete
+
+    // ---- phase A: S^T = K Q^T for this wave's rows, softmax, P^T -> LDS ----
+    float4_t s[4][NTA];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTA; ++nt) s[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    // K operands of the next 64 dims are read while the MFMAs of the current
+    // ones run (a single wave per SIMD has nothing else to hide LDS latency).
+    {
+      constexpr int SPF = DV / 64;        // 8 steps from the f16 tile, then the rope step
+      half8_t ka[2][4][2];
+      uint4_t rope_raw[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) ka[0][mt][h] = *(const half8_t*)(kf + mt * 16 * FROW + qa_off[0][h]);
+#pragma unroll
+      for (int sp = 0; sp < SPF; ++sp) {
+        const int cur = sp & 1;
+        if (sp + 1 < SPF) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              ka[cur ^ 1][mt][h] =
+                  *(const half8_t*)(kf + mt * 16 * FROW + ((sp + 1) >> 1) * 256 + qa_off[(sp + 1) & 1][h]);
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            const int key = mt * 16 + l16;
+            rope_raw[mt] = *(const uint4_t*)(ks + key * KROW + swz<KROW>(4 * SPF + grp, key) * 16);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NTA; ++nt) {
+            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[cur][mt][0], q.hi[nt][2 * sp], s[mt][nt], 0, 0, 0);
+            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[cur][mt][1], q.hi[nt][2 * sp + 1], s[mt][nt], 0, 0, 0);
+            if constexpr (HILO) {
+              s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[cur][mt][0], q.lo[nt][2 * sp], s[mt][nt], 0, 0, 0);
+              s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[cur][mt][1], q.lo[nt][2 * sp + 1], s[mt][nt], 0, 0, 0);
+            }
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      constexpr int sp = SPF;   // rope dims 512..575, converted from the raw tile
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const int row = mt * 16 + l16;
-        const uint4_t raw = *(const uint4_t*)(ks + row * KROW + swz<KROW>(4 * sp + grp, row) * 16);
-        const half8_t a0 = bytes8_to_op<FP8>(raw[0], raw[1]);
-        const half8_t a1 = bytes8_to_op<FP8>(raw[2], raw[3]);
-        s[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, q.hi[0][2 * sp], s[mt][0], 0, 0, 0);
-        s[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.hi[0][2 * sp + 1], s[mt][0], 0, 0, 0);
-        if constexpr (HILO) {
-          s[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, q.lo[0][2 * sp], s[mt][0], 0, 0, 0);
-          s[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.lo[0][2 * sp + 1], s[mt][0], 0, 0, 0);
+        const half8_t a0 = bytes8_to_op<FP8>(rope_raw[mt][0], rope_raw[mt][1]);
+        const half8_t a1 = bytes8_to_op<FP8>(rope_raw[mt][2], rope_raw[mt][3]);
+#pragma unroll
+        for (int nt = 0; nt < NTA; ++nt) {
+          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, q.hi[nt][2 * sp], s[mt][nt], 0, 0, 0);
+          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.hi[nt][2 * sp + 1], s[mt][nt], 0, 0, 0);
+          if constexpr (HILO) {
+            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, q.lo[nt][2 * sp], s[mt][nt], 0, 0, 0);
+            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.lo[nt][2 * sp + 1], s[mt][nt], 0, 0, 0);
+          }
         }
       }
     }
-    half8_t pb[2][1];
     {
-      // softmax_tile rescales sa.o (one dummy tile); the real O lives in phase B,
-      // which applies the per-row factor published below.
-      const float m_before = sa.m[0];
-      softmax_tile<DQK, 1, 1, HILO>(p, u, kbase, grp, q, s, sa, pb);
-      const float m_use = sa.m[0] == -INFINITY ? 0.f : sa.m[0];
-      if (grp == 0) alpha_lds[wave * 16 + l16] = __builtin_amdgcn_exp2f(m_before - m_use);
+      half8_t pb[2][NTA];
+      float m_before[NTA];
+#pragma unroll
+      for (int nt = 0; nt < NTA; ++nt) m_before[nt] = sa.m[nt];
+      // O lives in phase B, which applies the per-row factor published here.
+      softmax_tile<DQK, NTA, 0, HILO>(p, u, kbase, grp, q, s, sa, pb);
+#pragma unroll
+      for (int nt = 0; nt < NTA; ++nt) {
+        const float m_use = sa.m[nt] == -INFINITY ? 0.f : sa.m[nt];
+        if (grp == 0) alpha_lds[(wave * NTA + nt) * 16 + l16] = __builtin_amdgcn_exp2f(m_before[nt] - m_use);
+        pt_lds[((wave * NTA + nt) * 2 + 0) * 64 + lane] = pb[0][nt];
+        pt_lds[((wave * NTA + nt) * 2 + 1) * 64 + lane] = pb[1][nt];
+      }
     }
-    pt_lds[(wave * 2 + 0) * 64 + lane] = pb[0][0];
-    pt_lds[(wave * 2 + 1) * 64 + lane] = pb[1][0];
-    __syncthreads();
+    __syncthreads();  // B2: P^T and factors ready; every wave is done with raw stage `stage`
+    if (it + 2 < n_tiles) issue_tile(it + 2, stage);
 
-    // ---- phase B: O^T[64 dims of this wave][all rows] += V^T P^T ----
+    // ---- phase B: O^T[128 dims of this wave][all rows] += V^T P^T ----
     {
       float al[NTB];
       bool grew = false;
@@ -1331,40 +1453,46 @@ __global__ __launch_bounds__(512, 1) void paged_mla_kernel(AttnParams p) {
           for (int nt = 0; nt < NTB; ++nt) o[md][nt] *= al[nt];
       }
     }
-    const int jr = l16 >> 1;
-    const int hlf = lane & 1;
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
-      const int vrow = 32 * ks2 + (jr < 4 ? 4 * grp + jr : 16 + 4 * grp + (jr - 4));
       half8_t va[MDW];
+      half8_t pbn[NTB];
 #pragma unroll
       for (int md = 0; md < MDW; ++md) {
-        const int chunk = wave * MDW + md;   // 16-byte chunk = 16 output dims
-        const uint8_t* addr = ks + vrow * KROW + swz<KROW>(chunk, vrow) * 16 + hlf * 8;
-        const int2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) int2_t*)(addr));
-        va[md] = bytes8_to_op<FP8>((uint32_t)raw[0], (uint32_t)raw[1]);
+        // lane: keys kappa(grp, j) for j = tr_j and tr_j + 4 (keys 32ks2 + 4grp + tr_j
+        // and 16 more), dims 4*tr_q .. 4*tr_q + 3 of this 16-dim tile; the
+        // transpose hands lane i dim i of keys j = 0..3
+        const uint8_t* va_base = kf + vb_off[md] + (32 * ks2) * FROW;
+        const short4_t ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(va_base));
+        const short4_t rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(va_base + 16 * FROW));
+        va[md] = __builtin_shufflevector(__builtin_bit_cast(half4_t, ra), __builtin_bit_cast(half4_t, rb),
+                                         0, 1, 2, 3, 4, 5, 6, 7);
       }
 #pragma unroll
-      for (int nt = 0; nt < NTB; ++nt) {
-        const half8_t pbn = pt_lds[(nt * 2 + ks2) * 64 + lane];
+      for (int nt = 0; nt < NTB; ++nt) pbn[nt] = pt_lds[(nt * 2 + ks2) * 64 + lane];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt)
 #pragma unroll
         for (int md = 0; md < MDW; ++md)
-          o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[md], pbn, o[md][nt], 0, 0, 0);
-      }
+          o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[md], pbn[nt], o[md][nt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
   // ---- epilogue: row sums and lse from the owner waves, outputs per dim slice ----
   const int H_q = p.num_q_heads;
-  {
-    const float lt = row_sum4(sa.l[0]);
-    const float lse_nat = lt > 0.f ? (sa.m[0] + __log2f(lt)) * LN2F : -INFINITY;
-    if (grp == 0) lrow_lds[wave * 16 + l16] = lt;
-    if (grp == 0 && q.ok[0]) {
-      const int tok = u.tok0 + q.tok[0];
-      if (u.split) p.part_lse[((int64_t)tok * p.max_chunks + c) * H_q + q.head[0]] = lse_nat;
-      else if (p.lse) p.lse[(int64_t)tok * H_q + q.head[0]] = lse_nat;
+#pragma unroll
+  for (int nt = 0; nt < NTA; ++nt) {
+    const float lt = row_sum4(sa.l[nt]);
+    const float lse_nat = lt > 0.f ? (sa.m[nt] + __log2f(lt)) * LN2F : -INFINITY;
+    if (grp == 0) lrow_lds[(wave * NTA + nt) * 16 + l16] = lt;
+    if (grp == 0 && q.ok[nt]) {
+      const int tok = u.tok0 + q.tok[nt];
+      if (u.split) p.part_lse[((int64_t)tok * p.max_chunks + c) * H_q + q.head[nt]] = lse_nat;
+      else if (p.lse) p.lse[(int64_t)tok * H_q + q.head[nt]] = lse_nat;
     }
   }
   __syncthreads();
@@ -1486,7 +1614,7 @@ hipError_t launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
 
 template <bool FP8, bool HILO>
 hipError_t launch_mla(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((paged_mla_kernel<FP8, HILO>), grid, dim3(512), 0, stream, p);
+  hipLaunchKernelGGL((paged_mla_kernel<FP8, HILO>), grid, dim3(MLA_WAVES * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1509,8 +1637,8 @@ struct Entry {
 // (for it, nw counts the waves that split one unit's key range)
 #define PA_DEC(D, FP8, NT, HL, KS) \
   Entry{AttnConfig{D, D, FP8, false, NT, KS, HL, 0}, &launch_decode<D, FP8, NT, HL, KS>}
-// the split-phase MLA kernel (128 rows, 8 waves) is marked nstage == 1
-#define PA_MLA(FP8, HL) Entry{AttnConfig{576, 512, FP8, true, 1, 8, HL, 1}, &launch_mla<FP8, HL>}
+// the MLA kernel (8 waves and 128 rows, or 4 and 64 with hi + lo query parts) is marked nstage == 1
+#define PA_MLA(FP8, HL) Entry{AttnConfig{576, 512, FP8, true, 1, MLA_WAVES, HL, 1}, &launch_mla<FP8, HL>}
 
 #define PA_SET(D, FP8, HL)                                                                       \
   PA_DEC(D, FP8, 1, HL, 1), PA_DEC(D, FP8, 1, HL, 2), PA_DEC(D, FP8, 1, HL, 4),                    \

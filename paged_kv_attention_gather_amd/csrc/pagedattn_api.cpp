@@ -179,8 +179,8 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   cfg.hilo = p->scale_mode == PA_SCALE_PER_CHANNEL || p->q_dtype == PA_DTYPE_F32;
   if (shared) {
     cfg.nt = 1;
-    cfg.nw = 8;
-    cfg.nstage = 1;  // split-phase MLA kernel
+    cfg.nw = 4;
+    cfg.nstage = 1;  // MLA kernel
   } else if (rows_max <= 64) {
     cfg.nt = (int)ceil_div(rows_max, 16);
     cfg.nw = 1;
