@@ -12,10 +12,13 @@ per-channel scales, chunk 512): the one the decode KV-bandwidth metric is
 quoted on.  --config 1..5 selects another workload.
 
 Prints ONE JSON line with the headline metric, the roofline of the attention
-kernel (its duration isolated with HIP events on the launch stream: the
-merge-only time, measured with the public split_kv_merge call on the same
-partials, is subtracted from the full call) and the oracle's throughput on a
-bounded sample of the same workload (cpu_baseline).
+kernel and the oracle's throughput on a bounded sample of the same workload
+(cpu_baseline).  The attention kernel is timed on its own: each step makes the
+ABI call with PA_FLAG_DEFER_MERGE and then runs split_kv_merge, with HIP
+events on the launch stream before, between and after, so a step is still the
+whole path.  The roofline's "traffic" (HBM bytes per launch of the attention
+kernel) comes from the FETCH_SIZE / WRITE_SIZE counter summary committed in
+profiles/, and is null when that summary was taken on other kernel sources.
 """
 import argparse
 import json
@@ -36,7 +39,7 @@ WORKLOAD_TEXT = {
     2: "decode_int8: B=64 q_len=1 H_q=32 H_kv=8 D=128 P=64 L~U[512,4096] int8 per-channel chunk=512",
     3: "append_prefill: B=8 n~U[256,1024] L~U[0,2048] H_q=32 H_kv=8 D=128 P=64 int8 per-head causal",
     4: "spec_decode: B=128 q_len=5 H_q=64 H_kv=8 D=128 P=64 L~lognormal(2048,1)[128,32768] int8 per-channel chunk=1024",
-    5: "mla_decode: B=32 q_len=1 H_q=128 H_kv=1 D_qk=576 D_v=512 P=64 L~U[4096,16384] fp8 per-tensor chunk=512",
+    5: "mla_decode: B=32 q_len=1 H_q=128 H_kv=1 D_qk=576 D_v=512 P=64 L~U[4096,16384] fp8 per-tensor chunk=2048",
 }
 
 
@@ -95,6 +98,38 @@ def cpu_baseline(idx, budget_s=15.0):
                       f"host cores visible: {len(os.sched_getaffinity(0))})"}
 
 
+def kernel_name(dp):
+    """Name of the attention kernel the library launches for this problem."""
+    w = dp.w
+    if w.shared_kv:
+        return "paged_mla_kernel"
+    rows = (int(w.decode_q_len) if dp.decode else int(w.q_lens.max())) * (w.num_q_heads // w.num_kv_heads)
+    return "paged_decode_kernel" if rows <= 32 else "paged_attn_kernel"
+
+
+def hbm_traffic(config, chunk):
+    """HBM bytes per launch of the attention kernel from the committed counter
+    summary, or (None, reason) when it does not cover these kernel sources."""
+    from paged_kv_attention_gather_amd import build
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    text = open(path).read()
+    start = text.find("```json")
+    if start < 0:
+        return None, "no counter table"
+    data = json.loads(text[start + 7:text.index("```", start + 7)])
+    digest = build.source_digest()
+    if data.get("source_digest") != digest:
+        return None, f"counters taken on sources {data.get('source_digest')}, kernel now {digest}"
+    row = data.get("configs", {}).get(str(config))
+    if not row or row.get("chunk_size") != chunk:
+        return None, "no counters for this workload"
+    fetch = row["fetch_kib_per_dispatch"] * 1024 * data["fetch_factor"]
+    write = row["write_kib_per_dispatch"] * 1024 * data["write_factor"]
+    return int(round(fetch + write)), "profiles/hbm_traffic_counters.md"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,7 +169,7 @@ def main():
 
     print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
     w = config_workload(args.config)
-    dp = DeviceProblem(w, chunk_size=args.chunk)
+    dp = DeviceProblem(w, chunk_size=args.chunk, defer_merge=True)
     chunk = dp.prob.chunk_size
     kv_bytes, alg_bytes, flops = work_figures(w)
     stream = torch.cuda.current_stream()
@@ -148,42 +183,26 @@ def main():
     for _ in range(args.warmup):
         do_flush()
         dp.run()
+        dp.merge()
     torch.cuda.synchronize()
 
-    # Full ABI call (attention + merge), per step, flushed caches.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # Timed steps: [flush] e0 attention e1 merge e2, all on the launch stream.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t_wall0 = time.perf_counter()
     for i in range(args.steps):
         do_flush()
         ev[i][0].record(stream)
         dp.run()
         ev[i][1].record(stream)
+        dp.merge()
+        ev[i][2].record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
-    step_ms = [a.elapsed_time(b) for a, b in ev]
+    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
+    attn_list = [e[0].elapsed_time(e[1]) for e in ev]
     ms = float(np.mean(step_ms))
-
-    # Merge-only time on the same partials (public split_kv_merge entry point),
-    # with the partials cache-resident as they are right after the attention kernel.
-    merge_ms = 0.0
-    if chunk > 0:
-        mc = -(-(int(w.seq_lens_kv.max()) + int(w.q_lens.max())) // chunk)
-        po_bytes = dp.total_q * mc * w.num_q_heads * w.head_dim_v * 4
-        lse_off = (po_bytes + 255) // 256 * 256
-        base = dp.workspace.data_ptr()
-        out2 = torch.empty_like(dp.out)
-        lse2 = torch.empty_like(dp.lse)
-        cu = None if dp.decode else dp.cu_seqlens_q
-        qlu = int(w.decode_q_len) if dp.decode else 0
-        mev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-        for i in range(args.steps):
-            mev[i][0].record(stream)
-            L.split_kv_merge(base, base + lse_off, cu, dp.seq_lens_kv, qlu, w.batch, dp.total_q,
-                             int(w.q_lens.max()), w.num_q_heads, w.head_dim_v, chunk, mc, out2, lse2)
-            mev[i][1].record(stream)
-        torch.cuda.synchronize()
-        merge_ms = float(np.mean([a.elapsed_time(b) for a, b in mev]))
-    attn_ms = max(ms - merge_ms, 1e-6)
+    attn_ms = float(np.mean(attn_list))
+    merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if chunk > 0 else 0.0
 
     if args.config in (1, 3):
         value, unit = flops / (ms * 1e-3) / 1e12, "TFLOP/s"
@@ -192,14 +211,22 @@ def main():
     if args.config in (3, 5):
         achieved = flops / (attn_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_F16_PEAK_TFS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFS, 4)}
     else:
         achieved = alg_bytes / (attn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
-    roof["kernel"] = "paged_attn_kernel"
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    traffic, note = hbm_traffic(args.config, chunk)
+    roof["traffic"] = traffic
+    if traffic is not None:
+        roof["traffic_over_alg_bytes"] = round(traffic / alg_bytes, 4)
+    roof["traffic_source"] = note
+    roof["kernel"] = kernel_name(dp)
     roof["kernel_ms"] = round(attn_ms, 5)
+    roof["kernel_min_ms"] = round(float(np.min(attn_list)), 5)
     roof["merge_ms"] = round(merge_ms, 5)
+    roof["alg_bytes_per_launch"] = alg_bytes
+    roof["flops_per_launch"] = flops
 
     line = {
         "metric": "decode: KV GB/s & %HBM peak; append: attention TFLOP/s & %MFMA peak",

@@ -91,7 +91,19 @@ typedef struct pa_problem {
   int32_t causal;             /* 1: bottom-right causal mask, 0: none */
   float sm_scale;             /* softmax scale on q . k (> 0) */
   int32_t chunk_size;         /* 0: no split-KV; else a multiple of 64 keys */
+  int32_t flags;              /* PA_FLAG_* bits, 0 for the default behaviour */
 } pa_problem;
+
+/* pa_problem.flags bits.
+ * PA_FLAG_DEFER_MERGE: with chunk_size > 0 the attention call writes the
+ *   per-chunk partials of multi-chunk requests to the workspace (and the
+ *   final rows of single-chunk requests to out / lse) but does not enqueue
+ *   split_kv_merge; the caller runs split_kv_merge on that workspace later,
+ *   for instance after adding partial states of its own.  Ignored when
+ *   chunk_size is 0. */
+enum {
+  PA_FLAG_DEFER_MERGE = 1
+};
 
 /*
  * paged_attn_workspace_size - bytes of workspace the attention calls need.
@@ -128,7 +140,8 @@ size_t paged_attn_workspace_size(const pa_problem* prob, int32_t total_q);
  *               paged_attn_workspace_size() is 0).
  * Requests with n_b = 0 write nothing.  With chunk_size > 0, requests that
  * span more than one chunk go through the workspace and split_kv_merge is
- * enqueued on the same stream; single-chunk requests are written directly.
+ * enqueued on the same stream (unless PA_FLAG_DEFER_MERGE); single-chunk
+ * requests are written directly.  Unknown flag bits are INVALID_ARG.
  */
 int32_t paged_attn_append(const pa_problem* prob, int32_t total_q, const void* q,
                           const void* k_cache, const void* v_cache, const float* k_scale,

@@ -29,6 +29,8 @@ SCALE_PER_TENSOR = 0
 SCALE_PER_HEAD = 1
 SCALE_PER_CHANNEL = 2
 
+FLAG_DEFER_MERGE = 1
+
 #: Every entry point include/pagedattn.h declares.
 EXPORTS = (
     "paged_attn_workspace_size",
@@ -67,6 +69,7 @@ class PaProblem(ctypes.Structure):
         ("causal", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
         ("chunk_size", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -146,7 +149,8 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_problem(**fields) -> PaProblem:
-    """Build a PaProblem from keyword fields (every field is required)."""
+    """Build a PaProblem from keyword fields (every field but ``flags`` is required)."""
+    fields.setdefault("flags", 0)
     names = [f for f, _ in PaProblem._fields_]
     missing = [n for n in names if n not in fields]
     extra = [k for k in fields if k not in names]

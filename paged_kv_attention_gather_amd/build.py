@@ -19,6 +19,20 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = ["pa_kernels.hip", "pagedattn_api.cpp"]
+
+
+def source_digest() -> str:
+    """First 16 hex digits of the SHA-256 of every kernel source and header
+    (in a fixed order): identifies the code that a set of counters measured."""
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(os.listdir(CSRC)) + ["../../include/pagedattn.h"]
+    for name in files:
+        path = os.path.normpath(os.path.join(CSRC, name))
+        if os.path.isfile(path):
+            h.update(name.encode())
+            h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 ARCH = "gfx950"
 
 

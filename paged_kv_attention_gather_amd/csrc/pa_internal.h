@@ -40,6 +40,7 @@ struct AttnParams {
   int32_t chunk_size;           // 0 = no split
   int32_t max_chunks;           // chunk slots in the grid / partial buffers
   int32_t row_tiles;
+  int32_t batch;
   int32_t q_is_f32;
   int32_t scale_mode;
   int32_t causal;

@@ -266,6 +266,25 @@ __device__ __forceinline__ bool unit_setup(const AttnParams& p, int b, int rt, i
   return true;
 }
 
+// Unit of a workgroup of the shared-tile kernels.  Workgroup L runs on XCD
+// L % 8 (round-robin dispatch).  A group is the row tiles of one (request, KV
+// head, chunk): they read the same KV tiles, so they are kept on one XCD (one
+// L2), in consecutive dispatch slots there; groups are dealt round-robin over
+// the XCDs in (request, head, chunk) order, which keeps the XCDs balanced when
+// requests differ in length.  Later (longer, causal) row tiles go first.
+// False for the padding past the last group.
+__device__ __forceinline__ bool shared_tile_unit(const AttnParams& p, int& b, int& g, int& c, int& rt) {
+  const int L = (int)blockIdx.x;
+  const int slot = L >> 3;
+  rt = p.row_tiles - 1 - slot % p.row_tiles;
+  int r = (slot / p.row_tiles) * 8 + (L & 7);   // group index
+  c = r % p.max_chunks;
+  r /= p.max_chunks;
+  g = r % p.num_kv_heads;
+  b = r / p.num_kv_heads;
+  return b < p.batch;
+}
+
 // Query rows of one wave as the B operand of S^T = K Q^T.
 // k-step 2s covers dims 64s + 16*grp + [0,8), k-step 2s+1 dims 64s + 16*grp + [8,16).
 // A row is multiplied by a power of two 2^k that puts its largest element in
@@ -745,10 +764,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void paged_attn_kernel(At
   const int grp = lane >> 4;
   // grid = (row tiles * chunks, H_kv, B): the row tiles of one request and head
   // are dispatched next to each other (they read the same KV), longest first
-  const int b = (int)blockIdx.z;
-  const int g = (int)blockIdx.y;
-  const int rt = p.row_tiles - 1 - (int)(blockIdx.x / p.max_chunks);
-  const int c = (int)(blockIdx.x % p.max_chunks);
+  int b, g, c, rt;
+  if (!shared_tile_unit(p, b, g, c, rt)) return;
 
   Unit u;
   if (!unit_setup<ROWS>(p, b, rt, c, u)) return;
@@ -1222,11 +1239,8 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int l16 = lane & 15;
   const int grp = lane >> 4;
-  const int b = (int)blockIdx.z;
-  const int g = (int)blockIdx.y;
-  // the row tiles of one chunk are adjacent, so they share its KV tiles in L2
-  const int rt = p.row_tiles - 1 - (int)(blockIdx.x % p.row_tiles);
-  const int c = (int)(blockIdx.x / p.row_tiles);
+  int b, g, c, rt;
+  if (!shared_tile_unit(p, b, g, c, rt)) return;   // a chunk's row tiles share an XCD
 
   Unit u;
   if (!unit_setup<ROWS>(p, b, rt, c, u)) return;

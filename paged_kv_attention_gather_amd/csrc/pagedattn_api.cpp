@@ -68,6 +68,7 @@ int32_t check_problem(const pa_problem* p) {
                 p->head_dim_qk, p->head_dim_v);
   if (log2_exact(p->page_size) < 0 || p->page_size < 16 || p->page_size > 1024)
     return fail(PA_ERR_UNSUPPORTED, "page_size %d must be a power of two in [16, 1024]", p->page_size);
+  if (p->flags & ~PA_FLAG_DEFER_MERGE) return fail(PA_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
   if (p->num_pages <= 0 || p->max_pages_per_seq <= 0)
     return fail(PA_ERR_INVALID_ARG, "num_pages and max_pages_per_seq must be positive");
   if (p->max_q_len < 0 || p->max_kv_len < 0)
@@ -197,7 +198,8 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   const int64_t rows_per_wg = 16LL * cfg.nt * (cfg.nstage == 0 ? 1 : cfg.nw);  // decode: nw splits keys
   const int64_t row_tiles = ceil_div(rows_max, rows_per_wg);
   const int64_t max_chunks = max_chunks_of(p);
-  if (row_tiles > 65535 || max_chunks > 65535 || row_tiles * max_chunks > 0x7fffffffLL)
+  if (row_tiles > 65535 || max_chunks > 65535 ||
+      (int64_t)p->batch * p->num_kv_heads * row_tiles * max_chunks > 0x7ffffff0LL)
     return fail(PA_ERR_UNSUPPORTED, "grid too large (%lld row tiles, %lld chunks, %lld request-heads)",
                 (long long)row_tiles, (long long)max_chunks,
                 (long long)p->batch * p->num_kv_heads);
@@ -249,12 +251,15 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   // requests dispatch last); the shared-tile kernel keeps one request-head's
   // row tiles adjacent.
   const bool decode_kernel = cfg.nstage == 0;
+  // shared-tile kernels: ceil(groups / 8) rounds of 8 groups x row_tiles workgroups
+  const int64_t groups = (int64_t)p->batch * p->num_kv_heads * max_chunks;
+  ap.batch = p->batch;
   dim3 grid = decode_kernel
                   ? dim3((unsigned)(p->batch * p->num_kv_heads), (unsigned)row_tiles, (unsigned)max_chunks)
-                  : dim3((unsigned)(row_tiles * max_chunks), (unsigned)p->num_kv_heads, (unsigned)p->batch);
+                  : dim3((unsigned)(ceil_div(groups, 8) * 8 * row_tiles), 1, 1);
   hipError_t e = pa::launch_attention(cfg, ap, grid, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
-  if (p->chunk_size > 0) {
+  if (p->chunk_size > 0 && !(p->flags & PA_FLAG_DEFER_MERGE)) {
     pa::MergeParams mp{};
     mp.part_o = ap.part_o;
     mp.part_lse = ap.part_lse;

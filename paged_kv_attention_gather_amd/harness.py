@@ -18,7 +18,7 @@ _KV_DTYPES = {"i8": L.DTYPE_I8, "fp8_e4m3": L.DTYPE_FP8_E4M3}
 _SCALE_MODES = {"tensor": L.SCALE_PER_TENSOR, "head": L.SCALE_PER_HEAD, "channel": L.SCALE_PER_CHANNEL}
 
 
-def problem_for(w, chunk_size=None, q_row_stride=None) -> L.PaProblem:
+def problem_for(w, chunk_size=None, q_row_stride=None, flags=0) -> L.PaProblem:
     """The pa_problem of a workload stored as contiguous
     [num_pages, H_kv, P, D] caches and [total_q, H_q, D_qk] queries."""
     H, P = w.num_kv_heads, w.page_size
@@ -34,13 +34,14 @@ def problem_for(w, chunk_size=None, q_row_stride=None) -> L.PaProblem:
         v_stride_page=H * P * vD, v_stride_head=P * vD, v_stride_token=vD,
         q_dtype=_Q_DTYPES[w.q_dtype], kv_dtype=_KV_DTYPES[w.kv_dtype],
         scale_mode=_SCALE_MODES[w.scale_mode], causal=int(bool(w.causal)),
-        sm_scale=float(w.sm_scale), chunk_size=int(w.chunk_size if chunk_size is None else chunk_size))
+        sm_scale=float(w.sm_scale), chunk_size=int(w.chunk_size if chunk_size is None else chunk_size),
+        flags=int(flags))
 
 
 class DeviceProblem:
     """Device tensors of a workload plus its outputs and workspace."""
 
-    def __init__(self, w, device="cuda", chunk_size=None, decode=None):
+    def __init__(self, w, device="cuda", chunk_size=None, decode=None, defer_merge=False):
         import torch
         self.torch = torch
         self.w = w
@@ -58,7 +59,7 @@ class DeviceProblem:
         self.q_lens = torch.from_numpy(np.ascontiguousarray(w.q_lens, dtype=np.int32)).to(dev)
         self.cu_seqlens_q = torch.from_numpy(np.ascontiguousarray(w.cu_seqlens_q, dtype=np.int32)).to(dev)
         self.block_table = torch.from_numpy(np.ascontiguousarray(w.block_table, dtype=np.int32)).to(dev)
-        self.prob = problem_for(w, chunk_size=chunk_size)
+        self.prob = problem_for(w, chunk_size=chunk_size, flags=L.FLAG_DEFER_MERGE if defer_merge else 0)
         self.total_q = int(w.total_q)
         self.out = torch.empty((self.total_q, w.num_q_heads, w.head_dim_v), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((self.total_q, w.num_q_heads), dtype=torch.float32, device=dev)
@@ -77,6 +78,22 @@ class DeviceProblem:
                                 self.k_scale, self.v_scale, self.cu_seqlens_q, self.seq_lens_kv,
                                 self.block_table, self.out, self.lse, self.workspace,
                                 self.workspace_bytes, stream)
+
+    def merge(self, stream=None) -> None:
+        """Enqueue split_kv_merge over this problem's workspace (the second half
+        of a call made with defer_merge=True; a no-op without split-KV)."""
+        C = int(self.prob.chunk_size)
+        if C <= 0:
+            return
+        w = self.w
+        mc = max(1, -(-(int(self.prob.max_kv_len) + int(self.prob.max_q_len)) // C))
+        po_bytes = self.total_q * mc * w.num_q_heads * w.head_dim_v * 4
+        base = self.workspace.data_ptr()
+        L.split_kv_merge(base, base + (po_bytes + 255) // 256 * 256,
+                         None if self.decode else self.cu_seqlens_q, self.seq_lens_kv,
+                         int(w.decode_q_len) if self.decode else 0, w.batch, self.total_q,
+                         int(self.prob.max_q_len), w.num_q_heads, w.head_dim_v, C, mc, self.out, self.lse,
+                         stream)
 
     def outputs(self):
         """(out as float64 NumPy, lse as float64 NumPy) after synchronizing."""

@@ -58,6 +58,14 @@ def base_problem(**over):
     return P.make_problem(**f)
 
 
+def test_problem_struct_matches_header():
+    """The binding's PaProblem mirrors the header field for field (same order)."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct pa_problem \{(.*?)\} pa_problem;", text, flags=re.S).group(1)
+    names = re.findall(r"([a-z_0-9]+)\s*[,;]", body)
+    assert names == [f for f, _ in L.PaProblem._fields_]
+
+
 def test_workspace_size_formula(lib):
     prob = base_problem()
     total_q = 8
@@ -100,6 +108,7 @@ def _append(prob, total_q=8, workspace=None, ws_bytes=0, **ptrs):
     (dict(k_stride_token=120), L.PA_ERR_INVALID_ARG),             # not 16-byte multiple
     (dict(batch=-1), L.PA_ERR_INVALID_ARG),
     (dict(batch=70000), L.PA_ERR_UNSUPPORTED),
+    (dict(flags=2), L.PA_ERR_INVALID_ARG),                        # unknown flag bit
 ])
 def test_invalid_problems_are_rejected(lib, over, status):
     assert _decode(base_problem(**over)) == status

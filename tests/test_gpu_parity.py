@@ -184,6 +184,25 @@ def test_decode_split_waves_parity(case, waves, monkeypatch):
 
 # ------------------------------------------------------------------ merge --
 
+@pytest.mark.parametrize("case", ["decode_q8_g8", "append_chunked", "mla_int8_g16_q2"])
+def test_deferred_merge_matches_single_call(case):
+    """PA_FLAG_DEFER_MERGE + an explicit split_kv_merge gives the bits of the
+    single call (same kernels, same order of operations)."""
+    need_gpu()
+    from paged_kv_attention_gather_amd.harness import DeviceProblem
+    w = _edge(case, **EDGE_CASES[case])
+    announce(f"deferred merge {case}")
+    a = DeviceProblem(w)
+    a.run()
+    ref = a.outputs()
+    d = DeviceProblem(w, defer_merge=True)
+    d.out.zero_()
+    d.run()
+    d.merge()
+    got = d.outputs()
+    n = int(w.q_lens.sum())
+    assert np.array_equal(ref[0][:n], got[0][:n]) and np.array_equal(ref[1][:n], got[1][:n])
+
 def test_split_kv_merge_against_oracle_partials():
     torch = need_gpu()
     import paged_kv_attention_gather_amd as P
