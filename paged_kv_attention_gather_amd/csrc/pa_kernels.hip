@@ -979,17 +979,15 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
   const int32_t* table_row = p.block_table + (int64_t)b * p.max_pages_per_seq;
   const int page_shift = p.page_shift;
 
-  // Page-id window: lane l holds the physical page of page index pw_base + l.
-  // The first window is read before the request length is known, in parallel
-  // with it (entries past the request's last page are read, from within its
-  // block-table row, but never used as addresses).
-  int pw_base = (p.chunk_size > 0 ? c * p.chunk_size : 0) >> page_shift;
-  int pw_val = table_row[min(pw_base + lane, p.max_pages_per_seq - 1)];
-
   Unit u;
   if (!unit_setup<16 * NT>(p, b, rt, c, u)) return;
   const int key_end = u.key_end, kv_lo = u.kv_lo, n_tiles = u.n_tiles;
-  const int last_page = n_tiles > 0 ? (key_end - 1) >> page_shift : 0;  // never used past it
+  const int last_page = n_tiles > 0 ? (key_end - 1) >> page_shift : 0;  // never read past it
+
+  // Page-id window: lane l holds the physical page of page index pw_base + l
+  // (clamped to the unit's last page, so no entry past the request is read).
+  int pw_base = kv_lo >> page_shift;
+  int pw_val = table_row[min(pw_base + lane, last_page)];
   const bool one_page = page_shift >= 6;
   const int ld_row = lane / CPR, ld_chunk = lane % CPR;
   const int64_t k_lane = (int64_t)ld_row * p.k_stride_token + 16 * ld_chunk;
