@@ -732,7 +732,7 @@ __device__ __forceinline__ void load_v_scales(const AttnParams& p, int g, int la
 // rare refill of the page-id window, which waits for itself.
 
 template <int DQK, int DV, bool FP8, int NT, int NW, bool SHARED, bool HILO, int NSTAGE>
-__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void paged_attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void paged_attn_kernel(AttnParams p) {
   constexpr int ROWS_W = 16 * NT;
   constexpr int ROWS = ROWS_W * NW;
   constexpr int KROW = DQK;                       // bytes per K row in LDS
@@ -1655,8 +1655,8 @@ struct Entry {
 #define PA_SET(D, FP8, HL)                                                                       \
   PA_DEC(D, FP8, 1, HL, 1), PA_DEC(D, FP8, 1, HL, 2), PA_DEC(D, FP8, 1, HL, 4),                    \
       PA_DEC(D, FP8, 2, HL, 1), PA_DEC(D, FP8, 2, HL, 2), PA_DEC(D, FP8, 2, HL, 4),                 \
-      PA_ENTRY(D, D, FP8, 3, 1, false, HL, 2),                                                      \
-      PA_ENTRY(D, D, FP8, 4, 1, false, HL, 2), PA_ENTRY(D, D, FP8, 2, 4, false, HL, 2)
+      PA_ENTRY(D, D, FP8, 1, 3, false, HL, 2), PA_ENTRY(D, D, FP8, 1, 4, false, HL, 2),             \
+      PA_ENTRY(D, D, FP8, 2, 4, false, HL, 2)
 
 const Entry kTable[] = {
     PA_SET(64, false, false),   PA_SET(64, false, true),

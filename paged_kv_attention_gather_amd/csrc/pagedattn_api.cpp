@@ -182,12 +182,16 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
     cfg.nt = 1;
     cfg.nw = 4;
     cfg.nstage = 1;  // MLA kernel
-  } else if (rows_max <= 64) {
+  } else if (rows_max <= 32) {
+    // register-staged decode kernel
     cfg.nt = (int)ceil_div(rows_max, 16);
-    cfg.nw = 1;
-    // up to 32 rows: register-staged decode kernel; more rows: LDS-staged
-    cfg.nstage = cfg.nt <= 2 ? 0 : 2;
-    if (cfg.nstage == 0) cfg.nw = decode_split_waves(p, cfg.nt);
+    cfg.nw = decode_split_waves(p, cfg.nt);
+    cfg.nstage = 0;
+  } else if (rows_max <= 64) {
+    // shared-tile kernel, 16 rows per wave, 3 or 4 waves sharing LDS-DMA tiles
+    cfg.nt = 1;
+    cfg.nw = (int)ceil_div(rows_max, 16);
+    cfg.nstage = 2;
   } else {
     cfg.nt = 2;
     cfg.nw = 4;
