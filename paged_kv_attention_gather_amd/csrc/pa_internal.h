@@ -83,6 +83,7 @@ struct AttnConfig {
   int nw;           // waves per workgroup (they split the rows, share KV tiles)
   bool hilo;        // Q carries per-channel scales or is fp32: f16 hi + lo parts
   int nstage;       // KV tiles staged in LDS (0: register-staged decode kernel, 1: MLA kernel)
+  bool f16_tiles;   // shared-tile kernel converts each tile to f16 in LDS once
 };
 
 // Returns hipSuccess, hipErrorInvalidValue when no specialization matches.

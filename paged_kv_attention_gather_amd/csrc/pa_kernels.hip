@@ -136,6 +136,15 @@ __device__ __forceinline__ int swz(int chunk, int row) {
   }
 }
 
+// XOR swizzle of the 16-byte chunks of an f16 key row of 256 or 1024 bytes
+// (a whole number of 64-bank rows): the 16 keys of an MFMA operand read land
+// on 16 distinct bank groups, and the 8 keys that a 16-bit transposed read
+// pairs up land on 8 distinct 32-byte groups.  Only the low four chunk bits
+// change.
+__device__ __forceinline__ int kf_swz(int chunk, int key) {
+  return chunk ^ (((key & 7) << 1) | ((key >> 3) & 1));
+}
+
 // Page-table address function shared by the attention loads and the debug
 // gather: key -> (physical page, slot) -> row address (FlashInfer
 // persistent.cuh prefetch_offest; XQA KVTilePartLoader::loadPages).
@@ -202,16 +211,38 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-__device__ __forceinline__ float row_max4(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// Max / sum over the four 16-lane groups (lanes l, l^16, l^32, l^48) with the
+// gfx950 lane-swap VALU ops instead of LDS permutes.  With both operands equal,
+// v_permlane16_swap returns, in every lane l, the pair {v[l], v[l ^ 16]} (one
+// in each result), and v_permlane32_swap the pair {v[l], v[l ^ 32]}; max and
+// + are symmetric, so no lane select is needed and every lane of a row gets
+// the same bits.
+__device__ __forceinline__ float xor16_max(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
 }
-__device__ __forceinline__ float row_sum4(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+__device__ __forceinline__ float xor32_max(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
 }
+__device__ __forceinline__ float xor16_sum(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float row_max4(float v) { return xor32_max(xor16_max(v)); }
+__device__ __forceinline__ float row_sum4(float v) { return xor32_sum(xor16_sum(v)); }
 
 }  // namespace
 
@@ -731,7 +762,10 @@ __device__ __forceinline__ void load_v_scales(const AttnParams& p, int g, int la
 // No other vector-memory instruction is issued inside the main loop except the
 // rare refill of the page-id window, which waits for itself.
 
-template <int DQK, int DV, bool FP8, int NT, int NW, bool SHARED, bool HILO, int NSTAGE>
+// CONV: the workgroup converts each raw K/V tile to f16 tiles in LDS once
+// (each wave a quarter) and the waves read MFMA operands from those, instead of
+// every wave converting the whole raw tile for its own rows (D = 128 only).
+template <int DQK, int DV, bool FP8, int NT, int NW, bool SHARED, bool HILO, int NSTAGE, bool CONV>
 __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void paged_attn_kernel(AttnParams p) {
   constexpr int ROWS_W = 16 * NT;
   constexpr int ROWS = ROWS_W * NW;
@@ -753,10 +787,15 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
   constexpr float KV_OFF = FP8 ? 0.f : 1152.f;
   static_assert(DQK % 64 == 0 && DV % 16 == 0, "head dims");
   static_assert(KCH % 64 == 0 && VCH % 64 == 0, "tile chunks");
-  static_assert(NSTAGE == 2 || NW == 1, "deep pipelines are single-wave (per-wave DMA counts)");
+  static_assert(NSTAGE == 2 || NW == 1 || (KCH % (64 * NW) == 0 && VCH % (64 * NW) == 0),
+                "deep multi-wave pipelines need equal per-wave DMA counts");
   static_assert(DMA_PER_TILE * (NSTAGE - 2) <= 63, "vmcnt range");
+  static_assert(!CONV || (DQK == 128 && DV == 128 && !SHARED && (TK * 16) % (64 * NW) == 0),
+                "f16 tiles: 256-byte rows, separate K and V");
+  constexpr int FROW = 2 * DQK;                   // f16 row bytes (CONV)
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t f16t[CONV ? 2 * TK * FROW : 16];   // K then V
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -894,6 +933,86 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
     const uint8_t* ks = smem + stage * STAGE;
     const uint8_t* vs = SHARED ? ks : ks + KTILE;
     const int kbase = kv_lo + it * TK;
+
+    if constexpr (CONV) {
+      // raw K and V rows -> f16 rows; thread item: key i*(256/16)... (16 half-chunks
+      // of 8 bytes per 128-byte row; lanes of a wave cover 4 consecutive keys)
+      constexpr int ITEMS = TK * 16 / (64 * NW);   // per thread, for K and again for V
+      int2_t raw[2][ITEMS];
+#pragma unroll
+      for (int i = 0; i < ITEMS; ++i) {
+        const int item = (i * NW + wave) * 64 + lane;
+        const int key = item >> 4, hc = item & 15;
+        const int src = key * KROW + swz<KROW>(hc >> 1, key) * 16 + (hc & 1) * 8;
+        raw[0][i] = *(const int2_t*)(ks + src);
+        raw[1][i] = *(const int2_t*)(vs + src);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < ITEMS; ++i) {
+        const int item = (i * NW + wave) * 64 + lane;
+        const int key = item >> 4, hc = item & 15;
+        const int dst = key * FROW + kf_swz(hc, key) * 16;
+        *(half8_t*)(f16t + dst) = bytes8_to_op<FP8>((uint32_t)raw[0][i][0], (uint32_t)raw[0][i][1]);
+        *(half8_t*)(f16t + TK * FROW + dst) = bytes8_to_op<FP8>((uint32_t)raw[1][i][0], (uint32_t)raw[1][i][1]);
+      }
+      __syncthreads();   // f16 tiles complete (the next B0 orders their reuse)
+
+      float4_t s[4][NT];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) s[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+      half8_t ka[KPAIRS][4][2];
+#pragma unroll
+      for (int sp = 0; sp < KPAIRS; ++sp)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int key = mt * 16 + l16;
+            ka[sp][mt][h] = *(const half8_t*)(f16t + key * FROW + kf_swz(8 * sp + 2 * grp + h, key) * 16);
+          }
+#pragma unroll
+      for (int sp = 0; sp < KPAIRS; ++sp)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[sp][mt][h], q.hi[nt][2 * sp + h], s[mt][nt], 0, 0, 0);
+              if constexpr (HILO)
+                s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[sp][mt][h], q.lo[nt][2 * sp + h], s[mt][nt], 0, 0, 0);
+            }
+      half8_t pb[2][NT];
+      softmax_tile<DQK, NT, MD, HILO>(p, u, kbase, grp, q, s, st, pb);
+      // O^T += V^T P^T, V^T by the 16-bit transposed read of the f16 V tile
+      const int tr_j = l16 >> 2, tr_q = l16 & 3;
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        half8_t va[MD];
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+          const int kA = 32 * ks2 + 4 * grp + tr_j;
+          const int kB = kA + 16;
+          const int fch = 2 * md + (tr_q >> 1);
+          const uint8_t* vt = f16t + TK * FROW;
+          const short4_t ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4_t*)(vt + kA * FROW + kf_swz(fch, kA) * 16 + (tr_q & 1) * 8));
+          const short4_t rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4_t*)(vt + kB * FROW + kf_swz(fch, kB) * 16 + (tr_q & 1) * 8));
+          va[md] = __builtin_shufflevector(__builtin_bit_cast(half4_t, ra), __builtin_bit_cast(half4_t, rb),
+                                           0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            st.o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[md], pb[ks2][nt], st.o[md][nt], 0, 0, 0);
+      }
+      continue;
+    }
 
     // ---- S^T = K Q^T: 4 x NT independent accumulator chains ----
     float4_t s[4][NT];
@@ -1200,13 +1319,6 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
 //   phase B  wave w accumulates O^T for output dims (512 / NW) * w onwards of
 //            all rows: V^T comes from the f16 tile by the 16-bit LDS transpose
 //            read, P^T and the per-row rescale factors from phase A.
-
-// XOR swizzle of the 16-byte chunks of a 1024-byte f16 key row: the 16 keys of
-// an MFMA operand read land on 16 distinct bank groups, and the 8 keys that a
-// transposed read pairs up land on 8 distinct 32-byte groups.
-__device__ __forceinline__ int kf_swz(int chunk, int key) {
-  return chunk ^ (((key & 7) << 1) | ((key >> 3) & 1));
-}
 
 constexpr int MLA_WAVES = 4;  // waves (= 16-row tiles) per MLA workgroup
 
@@ -1617,9 +1729,9 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherParams p) {
 // ------------------------------------------------------------------ launch --
 
 namespace {
-template <int DQK, int DV, bool FP8, int NT, int NW, bool SHARED, bool HILO, int NSTAGE>
+template <int DQK, int DV, bool FP8, int NT, int NW, bool SHARED, bool HILO, int NSTAGE, bool CONV>
 hipError_t launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((paged_attn_kernel<DQK, DV, FP8, NT, NW, SHARED, HILO, NSTAGE>), grid,
+  hipLaunchKernelGGL((paged_attn_kernel<DQK, DV, FP8, NT, NW, SHARED, HILO, NSTAGE, CONV>), grid,
                      dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
 }
@@ -1645,12 +1757,14 @@ struct Entry {
 
 // nstage == 0 marks the register-staged single-wave decode kernel.
 #define PA_ENTRY(DQK, DV, FP8, NT, NW, SH, HL, NS) \
-  Entry{AttnConfig{DQK, DV, FP8, SH, NT, NW, HL, NS}, &launch_one<DQK, DV, FP8, NT, NW, SH, HL, NS>}
+  Entry{AttnConfig{DQK, DV, FP8, SH, NT, NW, HL, NS, false}, &launch_one<DQK, DV, FP8, NT, NW, SH, HL, NS, false>}
+#define PA_CONV(D, FP8, HL) \
+  Entry{AttnConfig{D, D, FP8, false, 2, 4, HL, 3, true}, &launch_one<D, D, FP8, 2, 4, false, HL, 3, true>}
 // (for it, nw counts the waves that split one unit's key range)
 #define PA_DEC(D, FP8, NT, HL, KS) \
-  Entry{AttnConfig{D, D, FP8, false, NT, KS, HL, 0}, &launch_decode<D, FP8, NT, HL, KS>}
+  Entry{AttnConfig{D, D, FP8, false, NT, KS, HL, 0, false}, &launch_decode<D, FP8, NT, HL, KS>}
 // the MLA kernel (8 waves and 128 rows, or 4 and 64 with hi + lo query parts) is marked nstage == 1
-#define PA_MLA(FP8, HL) Entry{AttnConfig{576, 512, FP8, true, 1, MLA_WAVES, HL, 1}, &launch_mla<FP8, HL>}
+#define PA_MLA(FP8, HL) Entry{AttnConfig{576, 512, FP8, true, 1, MLA_WAVES, HL, 1, false}, &launch_mla<FP8, HL>}
 
 #define PA_SET(D, FP8, HL)                                                                       \
   PA_DEC(D, FP8, 1, HL, 1), PA_DEC(D, FP8, 1, HL, 2), PA_DEC(D, FP8, 1, HL, 4),                    \
@@ -1664,13 +1778,14 @@ const Entry kTable[] = {
     PA_SET(128, false, false), PA_SET(128, false, true),
     PA_SET(128, true, false),  PA_SET(128, true, true),
     PA_MLA(true, false), PA_MLA(true, true), PA_MLA(false, false), PA_MLA(false, true),
+    PA_CONV(128, false, false), PA_CONV(128, false, true), PA_CONV(128, true, false), PA_CONV(128, true, true),
 };
 
 const Entry* find_entry(const AttnConfig& c) {
   for (const Entry& e : kTable)
     if (e.cfg.dqk == c.dqk && e.cfg.dv == c.dv && e.cfg.fp8 == c.fp8 &&
         e.cfg.shared_kv == c.shared_kv && e.cfg.nt == c.nt && e.cfg.nw == c.nw &&
-        e.cfg.hilo == c.hilo && e.cfg.nstage == c.nstage)
+        e.cfg.hilo == c.hilo && e.cfg.nstage == c.nstage && e.cfg.f16_tiles == c.f16_tiles)
       return &e;
   return nullptr;
 }

@@ -195,7 +195,8 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   } else {
     cfg.nt = 2;
     cfg.nw = 4;
-    cfg.nstage = 2;
+    cfg.f16_tiles = cfg.dqk == 128;
+    cfg.nstage = cfg.f16_tiles ? 3 : 2;
   }
   if (!pa::attention_supported(cfg))
     return fail(PA_ERR_UNSUPPORTED, "no compiled kernel for this configuration");
