@@ -38,6 +38,7 @@ typedef int int2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef int int4_t __attribute__((ext_vector_type(4)));
 
 constexpr int TK = 64;  // keys per KV tile
 constexpr float LAZY_LOG2 = 8.f;  // softmax reference-max slack (log2 units)
@@ -573,6 +574,113 @@ __device__ __forceinline__ void query_finish(const AttnParams& p, const Unit& u,
   }
 }
 
+// Query rows for S^T = K Q^T on the int8 MFMA (v_mfma_i32_16x16x64_i8), used
+// with int8 caches: K bytes go to the MFMA as they are, and each query row,
+// scaled by 32639 / max|row| and rounded to an integer q (|q| <= 32639), is
+// split into balanced base-256 digits q = 256 qh + ql, qh and ql in
+// [-128, 127].  Then S = 256 (K . qh) + K . ql with both products exact in
+// int32; the rounding of q is the only error (2^-15 of the row maximum per
+// element).  Lane l holds, per 64-dim step s, the digits of dims
+// 64s + 16*grp + [0, 16) of row l16, the same dims its K operand holds.
+template <int DQK, int NT>
+struct QRowsI8 {
+  static constexpr int KSTEPS = DQK / 64;
+  int4_t qh[KSTEPS][NT], ql[KSTEPS][NT];   // step-major: one step's operands for all row tiles
+  float row_mult[NT];
+  float kbias[NT];   // 0: no operand offset on K
+  int tok[NT], head[NT];
+  bool ok[NT];
+};
+
+// Digits of one row from its 16 * KSTEPS lane values (already scaled by the
+// per-channel K scales and sm_scale * log2(e) when those are folded).
+template <int DQK, int NT>
+__device__ __forceinline__ void query_digits(float (&xq)[DQK / 64][16], int nt, float mult_rest,
+                                             QRowsI8<DQK, NT>& q) {
+  constexpr int KSTEPS = DQK / 64;
+  float amax = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < KSTEPS; ++sp)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(xq[sp][e]));
+  amax = row_max4(amax);
+  const bool nz = amax > 1e-30f;
+  const float up = nz ? 32639.f / amax : 0.f;
+  q.row_mult[nt] = nz ? (amax / 32639.f) * mult_rest : 0.f;
+  q.kbias[nt] = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < KSTEPS; ++sp) {
+    uint32_t h[4] = {0u, 0u, 0u, 0u}, l[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int v = min(max((int)rintf(xq[sp][e] * up), -32639), 32639);
+      const int dh = (v + 128) >> 8;
+      const int dl = v - dh * 256;
+      h[e / 4] |= ((uint32_t)dh & 0xffu) << (8 * (e % 4));
+      l[e / 4] |= ((uint32_t)dl & 0xffu) << (8 * (e % 4));
+    }
+    q.qh[sp][nt] = int4_t{(int)h[0], (int)h[1], (int)h[2], (int)h[3]};
+    q.ql[sp][nt] = int4_t{(int)l[0], (int)l[1], (int)l[2], (int)l[3]};
+  }
+}
+
+// query_finish for the int8 MFMA (see QRowsI8).
+template <int DQK, int NT>
+__device__ __forceinline__ void query_finish_i8(const AttnParams& p, const Unit& u, int g, int row_base,
+                                                int lane, const QRaw<DQK, NT>& raw, QRowsI8<DQK, NT>& q) {
+  constexpr int KPAIRS = DQK / 64;
+  const int l16 = lane & 15;
+  const int mode = p.scale_mode;
+  const bool fold_channel = mode == PA_SCALE_PER_CHANNEL;
+  const float k_uniform = fold_channel ? 1.f : raw.k_uniform;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = row_base + nt * 16 + l16;
+    q.ok[nt] = r < u.rows_total;
+    q.tok[nt] = q.ok[nt] ? r / u.G : 0;
+    q.head[nt] = g * u.G + (q.ok[nt] ? r % u.G : 0);
+    float xq[KPAIRS][16];
+#pragma unroll
+    for (int sp = 0; sp < KPAIRS; ++sp)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float x;
+        if (p.q_is_f32) {
+          const uint32_t bits = raw.x[nt][sp][e / 4][e % 4];
+          x = __builtin_bit_cast(float, bits);
+        } else {
+          const uint32_t w = raw.x[nt][sp][e / 8][(e % 8) / 2];
+          x = bf16_to_f32((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
+        }
+        if (fold_channel) x *= p.qk_mult * raw.ksc[sp][e / 4][e % 4];
+        xq[sp][e] = q.ok[nt] ? x : 0.f;
+      }
+    query_digits<DQK, NT>(xq, nt, fold_channel ? 1.f : p.qk_mult * k_uniform, q);
+  }
+}
+
+// S^T += K Q^T over one 64-dim step on the int8 MFMA: `a` holds the lane's 16
+// K bytes; the two digit products accumulate apart (combined by s_from_i8).
+template <int NT>
+__device__ __forceinline__ void qk_i8_step(const int4_t& a, const int4_t (&qh)[NT], const int4_t (&ql)[NT],
+                                           int4_t (&acc_h)[NT], int4_t (&acc_l)[NT]) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    acc_h[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qh[nt], acc_h[nt], 0, 0, 0);
+    acc_l[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, ql[nt], acc_l[nt], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ float4_t s_from_i8(const int4_t& h, const int4_t& l) {
+  float4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hi = h[i], lo = l[i];
+    r[i] = 256.f * (float)hi + (float)lo;
+  }
+  return r;
+}
+
 // Online-softmax state of one wave: O^T accumulators (lane holds dims
 // 16*md + 4*grp + i of row l16), running max (log2 units) and denominator.
 template <int NT, int MD>
@@ -595,9 +703,9 @@ __device__ __forceinline__ void softmax_init(SoftmaxState<NT, MD>& st) {
 // Masks one 64-key tile of S^T, updates the running max/denominator, rescales
 // O when a row maximum grows, and returns P^T (f16) in the B-operand layout of
 // the PV MFMA: pb[ks][nt] holds keys {32ks + 4grp + i, 32ks + 16 + 4grp + i}.
-template <int DQK, int NT, int MD, bool HILO>
+template <int NT, int MD, typename QT>
 __device__ __forceinline__ void softmax_tile(const AttnParams& p, const Unit& u, int kbase, int grp,
-                                             const QRows<DQK, NT, HILO>& q, float4_t (&s)[4][NT],
+                                             const QT& q, float4_t (&s)[4][NT],
                                              SoftmaxState<NT, MD>& st, half8_t (&pb)[2][NT]) {
   const bool need_mask = kbase + TK > u.mask_from;
   const half2_t ones2 = {(_Float16)1.0f, (_Float16)1.0f};
@@ -690,9 +798,9 @@ __device__ __forceinline__ void pv_tile(const uint8_t* vs, int lane, const half8
 
 // Normalize, remove the int8 operand offset, apply V scales and write the final
 // bf16 row + natural lse, or the chunk's fp32 partial + lse.
-template <int DQK, int DV, int NT, bool HILO>
+template <int DV, int NT, typename QT>
 __device__ __forceinline__ void write_rows(const AttnParams& p, const Unit& u, int g, int c, int lane,
-                                           float kv_off, const QRows<DQK, NT, HILO>& q,
+                                           float kv_off, const QT& q,
                                            const SoftmaxState<NT, DV / 16>& st,
                                            const float4_t (&vsc)[DV / 16]) {
   constexpr int MD = DV / 16;
@@ -986,7 +1094,7 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
                 s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[sp][mt][h], q.lo[nt][2 * sp + h], s[mt][nt], 0, 0, 0);
             }
       half8_t pb[2][NT];
-      softmax_tile<DQK, NT, MD, HILO>(p, u, kbase, grp, q, s, st, pb);
+      softmax_tile<NT, MD>(p, u, kbase, grp, q, s, st, pb);
       // O^T += V^T P^T, V^T by the 16-bit transposed read of the f16 V tile
       const int tr_j = l16 >> 2, tr_q = l16 & 3;
 #pragma unroll
@@ -1049,13 +1157,13 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
     }
 
     half8_t pb[2][NT];
-    softmax_tile<DQK, NT, MD, HILO>(p, u, kbase, grp, q, s, st, pb);
+    softmax_tile<NT, MD>(p, u, kbase, grp, q, s, st, pb);
     pv_tile<FP8, NT, MD, VROW>(vs, lane, pb, st);
   }
 
   float4_t vsc[MD];
   load_v_scales<DV>(p, g, lane, vsc);
-  write_rows<DQK, DV, NT, HILO>(p, u, g, c, lane, KV_OFF, q, st, vsc);
+  write_rows<DV, NT>(p, u, g, c, lane, KV_OFF, q, st, vsc);
 }
 
 // -------------------------------------------------------- decode attention --
@@ -1156,10 +1264,12 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
 
   SoftmaxState<NT, MD> st;
   softmax_init(st);
+  // int8 caches use the int8 MFMA for S^T (QRowsI8); fp8 caches the f16 one
+  using QT = typename std::conditional<FP8, QRows<D, NT, HILO>, QRowsI8<D, NT>>::type;
   if (n_tiles == 0) {
     // No visible key in this unit: (0, -inf) rows, written by wave 0.
     if (wv > 0) return;
-    QRows<D, NT, HILO> q;
+    QT q;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int r = u.row0 + nt * 16 + l16;
@@ -1170,7 +1280,7 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
     float4_t vsc[MD];
 #pragma unroll
     for (int md = 0; md < MD; ++md) vsc[md] = float4_t{0.f, 0.f, 0.f, 0.f};
-    write_rows<D, D, NT, HILO>(p, u, g, c, lane, KV_OFF, q, st, vsc);
+    write_rows<D, NT>(p, u, g, c, lane, KV_OFF, q, st, vsc);
     return;
   }
 
@@ -1185,8 +1295,9 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) vs_lane[i] = p.v_scale[fold_channel ? (int64_t)g * D + lane + 64 * i : 0];
   load_tile(min(wv, n_tiles - 1));
-  QRows<D, NT, HILO> q;
-  query_finish<D, NT, HILO>(p, u, g, u.row0, lane, KV_OFF, qraw, q);
+  QT q;
+  if constexpr (FP8) query_finish<D, NT, HILO>(p, u, g, u.row0, lane, KV_OFF, qraw, q);
+  else query_finish_i8<D, NT>(p, u, g, u.row0, lane, qraw, q);
 
   for (int it = wv; it < n_tiles; it += KS) {
     const int kbase = kv_lo + it * TK;
@@ -1201,6 +1312,28 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
 
     // ---- S^T = K Q^T: 4 x NT independent accumulator chains ----
     float4_t s[4][NT];
+    if constexpr (!FP8) {
+      int4_t acc_h[4][NT], acc_l[4][NT];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] = acc_l[mt][nt] = int4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int sp = 0; sp < KPAIRS; ++sp) {
+        int4_t raw[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int row = mt * 16 + l16;
+          raw[mt] = *(const int4_t*)(ktile + row * D + swz<D>(4 * sp + grp, row) * 16);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) qk_i8_step<NT>(raw[mt], q.qh[sp], q.ql[sp], acc_h[mt], acc_l[mt]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) s[mt][nt] = s_from_i8(acc_h[mt][nt], acc_l[mt][nt]);
+    } else {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -1233,8 +1366,10 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
       }
     }
 
+    }
+
     half8_t pb[2][NT];
-    softmax_tile<D, NT, MD, HILO>(p, u, kbase, grp, q, s, st, pb);
+    softmax_tile<NT, MD>(p, u, kbase, grp, q, s, st, pb);
     pv_tile<FP8, NT, MD, D>(vtile, lane, pb, st);
   }
 
@@ -1300,7 +1435,7 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
   } else {
     load_v_scales<D>(p, g, lane, vsc);
   }
-  write_rows<D, D, NT, HILO>(p, u, g, c, lane, KV_OFF, q, st, vsc);
+  write_rows<D, NT>(p, u, g, c, lane, KV_OFF, q, st, vsc);
 }
 
 // ------------------------------------------------------- MLA latent decode --
@@ -1549,7 +1684,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
 #pragma unroll
       for (int nt = 0; nt < NTA; ++nt) m_before[nt] = sa.m[nt];
       // O lives in phase B, which applies the per-row factor published here.
-      softmax_tile<DQK, NTA, 0, HILO>(p, u, kbase, grp, q, s, sa, pb);
+      softmax_tile<NTA, 0>(p, u, kbase, grp, q, s, sa, pb);
 #pragma unroll
       for (int nt = 0; nt < NTA; ++nt) {
         const float m_use = sa.m[nt] == -INFINITY ? 0.f : sa.m[nt];
