@@ -671,12 +671,14 @@ __device__ __forceinline__ void qk_i8_step(const int4_t& a, const int4_t (&qh)[N
   }
 }
 
+// 256 * (K . qh) + K . ql, combined in int32 (|K . qh| < 2^21, so no
+// overflow) and converted once.
 __device__ __forceinline__ float4_t s_from_i8(const int4_t& h, const int4_t& l) {
   float4_t r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int hi = h[i], lo = l[i];
-    r[i] = 256.f * (float)hi + (float)lo;
+    r[i] = (float)(int)(((uint32_t)hi << 8) + (uint32_t)lo);
   }
   return r;
 }
@@ -901,9 +903,14 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
   static_assert(!CONV || (DQK == 128 && DV == 128 && !SHARED && (TK * 16) % (64 * NW) == 0),
                 "f16 tiles: 256-byte rows, separate K and V");
   constexpr int FROW = 2 * DQK;                   // f16 row bytes (CONV)
+  // int8 caches: S^T on the int8 MFMA (QRowsI8), except with f16 tiles, where
+  // converting K once per workgroup costs less than turning int32 S into fp32
+  // in every wave
+  constexpr bool I8QK = !FP8 && DQK <= 128 && !CONV;
+  constexpr int VF16 = I8QK ? 0 : TK * FROW;      // offset of the f16 V tile (after f16 K)
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t f16t[CONV ? 2 * TK * FROW : 16];   // K then V
+  __shared__ __attribute__((aligned(1024))) uint8_t f16t[CONV ? VF16 + TK * FROW : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1019,8 +1026,15 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
   for (int st = 0; st < NSTAGE - 1; ++st)
     if (st < n_tiles) issue_tile(st, st);
 
-  QRows<DQK, NT, HILO> q;
-  load_query<DQK, NT, HILO>(p, u, g, u.row0 + wave * ROWS_W, lane, KV_OFF, q);
+  using QT = typename std::conditional<I8QK, QRowsI8<DQK, NT>, QRows<DQK, NT, HILO>>::type;
+  QT q;
+  if constexpr (I8QK) {
+    QRaw<DQK, NT> qraw;
+    query_fetch<DQK, NT>(p, u, g, u.row0 + wave * ROWS_W, lane, qraw);
+    query_finish_i8<DQK, NT>(p, u, g, u.row0 + wave * ROWS_W, lane, qraw, q);
+  } else {
+    load_query<DQK, NT, HILO>(p, u, g, u.row0 + wave * ROWS_W, lane, KV_OFF, q);
+  }
   SoftmaxState<NT, MD> st;
   softmax_init(st);
 
@@ -1043,17 +1057,19 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
     const int kbase = kv_lo + it * TK;
 
     if constexpr (CONV) {
-      // raw K and V rows -> f16 rows; thread item: key i*(256/16)... (16 half-chunks
-      // of 8 bytes per 128-byte row; lanes of a wave cover 4 consecutive keys)
-      constexpr int ITEMS = TK * 16 / (64 * NW);   // per thread, for K and again for V
-      int2_t raw[2][ITEMS];
+      // raw rows -> f16 rows (V always; K only when S^T is not on the int8 MFMA);
+      // thread item: one 8-byte half-chunk of a 128-byte row, a wave's lanes
+      // covering 4 consecutive keys
+      constexpr int ITEMS = TK * 16 / (64 * NW);   // per thread and matrix
+      constexpr int NM = I8QK ? 1 : 2;              // matrices converted: V (and K)
+      int2_t raw[NM][ITEMS];
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
         const int item = (i * NW + wave) * 64 + lane;
         const int key = item >> 4, hc = item & 15;
         const int src = key * KROW + swz<KROW>(hc >> 1, key) * 16 + (hc & 1) * 8;
-        raw[0][i] = *(const int2_t*)(ks + src);
-        raw[1][i] = *(const int2_t*)(vs + src);
+        raw[0][i] = *(const int2_t*)(vs + src);
+        if constexpr (NM == 2) raw[1][i] = *(const int2_t*)(ks + src);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1061,12 +1077,37 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
         const int item = (i * NW + wave) * 64 + lane;
         const int key = item >> 4, hc = item & 15;
         const int dst = key * FROW + kf_swz(hc, key) * 16;
-        *(half8_t*)(f16t + dst) = bytes8_to_op<FP8>((uint32_t)raw[0][i][0], (uint32_t)raw[0][i][1]);
-        *(half8_t*)(f16t + TK * FROW + dst) = bytes8_to_op<FP8>((uint32_t)raw[1][i][0], (uint32_t)raw[1][i][1]);
+        *(half8_t*)(f16t + VF16 + dst) = bytes8_to_op<FP8>((uint32_t)raw[0][i][0], (uint32_t)raw[0][i][1]);
+        if constexpr (NM == 2)
+          *(half8_t*)(f16t + dst) = bytes8_to_op<FP8>((uint32_t)raw[1][i][0], (uint32_t)raw[1][i][1]);
       }
       __syncthreads();   // f16 tiles complete (the next B0 orders their reuse)
 
       float4_t s[4][NT];
+      if constexpr (I8QK) {
+        // K bytes straight from the raw tile into the int8 MFMA
+        int4_t acc_h[4][NT], acc_l[4][NT];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] = acc_l[mt][nt] = int4_t{0, 0, 0, 0};
+        int4_t kraw[KPAIRS][4];
+#pragma unroll
+        for (int sp = 0; sp < KPAIRS; ++sp)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            const int row = mt * 16 + l16;
+            kraw[sp][mt] = *(const int4_t*)(ks + row * KROW + swz<KROW>(4 * sp + grp, row) * 16);
+          }
+#pragma unroll
+        for (int sp = 0; sp < KPAIRS; ++sp)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) qk_i8_step<NT>(kraw[sp][mt], q.qh[sp], q.ql[sp], acc_h[mt], acc_l[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) s[mt][nt] = s_from_i8(acc_h[mt][nt], acc_l[mt][nt]);
+      } else {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -1093,6 +1134,7 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
               if constexpr (HILO)
                 s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[sp][mt][h], q.lo[nt][2 * sp + h], s[mt][nt], 0, 0, 0);
             }
+      }
       half8_t pb[2][NT];
       softmax_tile<NT, MD>(p, u, kbase, grp, q, s, st, pb);
       // O^T += V^T P^T, V^T by the 16-bit transposed read of the f16 V tile
@@ -1105,7 +1147,7 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
           const int kA = 32 * ks2 + 4 * grp + tr_j;
           const int kB = kA + 16;
           const int fch = 2 * md + (tr_q >> 1);
-          const uint8_t* vt = f16t + TK * FROW;
+          const uint8_t* vt = f16t + VF16;
           const short4_t ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) short4_t*)(vt + kA * FROW + kf_swz(fch, kA) * 16 + (tr_q & 1) * 8));
           const short4_t rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -1124,6 +1166,28 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
 
     // ---- S^T = K Q^T: 4 x NT independent accumulator chains ----
     float4_t s[4][NT];
+    if constexpr (I8QK) {
+      int4_t acc_h[4][NT], acc_l[4][NT];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] = acc_l[mt][nt] = int4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int sp = 0; sp < KPAIRS; ++sp) {
+        int4_t raw[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int row = mt * 16 + l16;
+          raw[mt] = *(const int4_t*)(ks + row * KROW + swz<KROW>(4 * sp + grp, row) * 16);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) qk_i8_step<NT>(raw[mt], q.qh[sp], q.ql[sp], acc_h[mt], acc_l[mt]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) s[mt][nt] = s_from_i8(acc_h[mt][nt], acc_l[mt][nt]);
+    } else {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -1154,6 +1218,8 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
               s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt], q.lo[nt][2 * sp + hk], s[mt][nt], 0, 0, 0);
         }
       }
+    }
+
     }
 
     half8_t pb[2][NT];
