@@ -107,6 +107,17 @@ def kernel_name(dp):
     return "paged_decode_kernel" if rows <= 32 else "paged_attn_kernel"
 
 
+def compute_dtype(dp):
+    """MFMA operand types: int8 caches through the decode kernel or the 16-row
+    shared-tile variants take S = K Q^T on the int8 MFMA (f16 for PV); every
+    other path multiplies f16 (cache values converted exactly)."""
+    w = dp.w
+    rows = (int(w.decode_q_len) if dp.decode else int(w.q_lens.max())) * (w.num_q_heads // w.num_kv_heads)
+    if w.kv_dtype == "i8" and not w.shared_kv and rows <= 64:
+        return "i8/f16"
+    return "f16"
+
+
 def hbm_traffic(config, chunk):
     """HBM bytes per launch of the attention kernel from the committed counter
     summary, or (None, reason) when it does not cover these kernel sources."""
@@ -232,7 +243,7 @@ def main():
         "metric": "decode: KV GB/s & %HBM peak; append: attention TFLOP/s & %MFMA peak",
         "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "scaling": "weak", "vs_baseline": None, "dtype": compute_dtype(dp),
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config], "global_batch": int(w.batch),
                    "kv_dtype": w.kv_dtype, "chunk_size": int(chunk), "cache_flush": not args.no_flush,
