@@ -576,16 +576,20 @@ __device__ __forceinline__ void query_finish(const AttnParams& p, const Unit& u,
 
 // Query rows for S^T = K Q^T on the int8 MFMA (v_mfma_i32_16x16x64_i8), used
 // with int8 caches: K bytes go to the MFMA as they are, and each query row,
-// scaled by 32639 / max|row| and rounded to an integer q (|q| <= 32639), is
-// split into balanced base-256 digits q = 256 qh + ql, qh and ql in
-// [-128, 127].  Then S = 256 (K . qh) + K . ql with both products exact in
-// int32; the rounding of q is the only error (2^-15 of the row maximum per
-// element).  Lane l holds, per 64-dim step s, the digits of dims
-// 64s + 16*grp + [0, 16) of row l16, the same dims its K operand holds.
+// scaled by QI8_MAX / max|row| and rounded to an integer q, is split into three
+// balanced base-256 digits q = 65536 qh + 256 qm + ql, each in [-128, 127].
+// S = 65536 (K . qh) + 256 (K . qm) + K . ql with every product exact in int32;
+// the rounding of q, 2^-23 of the row maximum per element, is the only error,
+// so rows with outlier channels keep their small elements (two digits, 2^-15,
+// were not enough for rows whose maximum is 16x their typical element).  Lane
+// l holds, per 64-dim step s, the digits of dims 64s + 16*grp + [0, 16) of row
+// l16, the same dims its K operand holds.
+constexpr float QI8_MAX = 8355000.f;   // |q| <= 127 * 65536 + 32767: top digit stays in int8
+
 template <int DQK, int NT>
 struct QRowsI8 {
   static constexpr int KSTEPS = DQK / 64;
-  int4_t qh[KSTEPS][NT], ql[KSTEPS][NT];   // step-major: one step's operands for all row tiles
+  int4_t qd[KSTEPS][3][NT];   // step, digit (high, middle, low), row tile
   float row_mult[NT];
   float kbias[NT];   // 0: no operand offset on K
   int tok[NT], head[NT];
@@ -605,22 +609,25 @@ __device__ __forceinline__ void query_digits(float (&xq)[DQK / 64][16], int nt, 
     for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(xq[sp][e]));
   amax = row_max4(amax);
   const bool nz = amax > 1e-30f;
-  const float up = nz ? 32639.f / amax : 0.f;
-  q.row_mult[nt] = nz ? (amax / 32639.f) * mult_rest : 0.f;
+  const float up = nz ? QI8_MAX / amax : 0.f;
+  q.row_mult[nt] = nz ? (amax / QI8_MAX) * mult_rest : 0.f;
   q.kbias[nt] = 0.f;
 #pragma unroll
   for (int sp = 0; sp < KSTEPS; ++sp) {
-    uint32_t h[4] = {0u, 0u, 0u, 0u}, l[4] = {0u, 0u, 0u, 0u};
+    uint32_t w[3][4] = {};
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int v = min(max((int)rintf(xq[sp][e] * up), -32639), 32639);
-      const int dh = (v + 128) >> 8;
-      const int dl = v - dh * 256;
-      h[e / 4] |= ((uint32_t)dh & 0xffu) << (8 * (e % 4));
-      l[e / 4] |= ((uint32_t)dl & 0xffu) << (8 * (e % 4));
+      const int v = min(max((int)rintf(xq[sp][e] * up), -8355000), 8355000);
+      const int d0 = ((v + 128) & 255) - 128;        // low digit
+      const int v1 = (v - d0) >> 8;
+      const int d1 = ((v1 + 128) & 255) - 128;       // middle digit
+      const int d2 = (v1 - d1) >> 8;                 // high digit, |d2| <= 128 * (8355000 / 2^23)
+      w[0][e / 4] |= ((uint32_t)d2 & 0xffu) << (8 * (e % 4));
+      w[1][e / 4] |= ((uint32_t)d1 & 0xffu) << (8 * (e % 4));
+      w[2][e / 4] |= ((uint32_t)d0 & 0xffu) << (8 * (e % 4));
     }
-    q.qh[sp][nt] = int4_t{(int)h[0], (int)h[1], (int)h[2], (int)h[3]};
-    q.ql[sp][nt] = int4_t{(int)l[0], (int)l[1], (int)l[2], (int)l[3]};
+#pragma unroll
+    for (int k = 0; k < 3; ++k) q.qd[sp][k][nt] = int4_t{(int)w[k][0], (int)w[k][1], (int)w[k][2], (int)w[k][3]};
   }
 }
 
@@ -660,25 +667,24 @@ __device__ __forceinline__ void query_finish_i8(const AttnParams& p, const Unit&
 }
 
 // S^T += K Q^T over one 64-dim step on the int8 MFMA: `a` holds the lane's 16
-// K bytes; the two digit products accumulate apart (combined by s_from_i8).
+// K bytes; the three digit products accumulate apart (combined by s_from_i8).
 template <int NT>
-__device__ __forceinline__ void qk_i8_step(const int4_t& a, const int4_t (&qh)[NT], const int4_t (&ql)[NT],
-                                           int4_t (&acc_h)[NT], int4_t (&acc_l)[NT]) {
+__device__ __forceinline__ void qk_i8_step(const int4_t& a, const int4_t (&qd)[3][NT], int4_t (&acc)[3][NT]) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    acc_h[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qh[nt], acc_h[nt], 0, 0, 0);
-    acc_l[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, ql[nt], acc_l[nt], 0, 0, 0);
-  }
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[k][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qd[k][nt], acc[k][nt], 0, 0, 0);
 }
 
-// 256 * (K . qh) + K . ql, combined in int32 (|K . qh| < 2^21, so no
-// overflow) and converted once.
-__device__ __forceinline__ float4_t s_from_i8(const int4_t& h, const int4_t& l) {
+// 65536 h + 256 m + l: (h << 8) + m is exact in int32 (|K . qh| < 2^21), the
+// last step runs in fp32 (relative rounding 2^-24).
+__device__ __forceinline__ float4_t s_from_i8(const int4_t& h, const int4_t& m, const int4_t& l) {
   float4_t r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int hi = h[i], lo = l[i];
-    r[i] = (float)(int)(((uint32_t)hi << 8) + (uint32_t)lo);
+    const int hi = h[i], mi = m[i], lo = l[i];
+    const int t = (int)(((uint32_t)hi << 8) + (uint32_t)mi);
+    r[i] = fmaf((float)t, 256.f, (float)lo);
   }
   return r;
 }
@@ -1084,30 +1090,7 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
       __syncthreads();   // f16 tiles complete (the next B0 orders their reuse)
 
       float4_t s[4][NT];
-      if constexpr (I8QK) {
-        // K bytes straight from the raw tile into the int8 MFMA
-        int4_t acc_h[4][NT], acc_l[4][NT];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] = acc_l[mt][nt] = int4_t{0, 0, 0, 0};
-        int4_t kraw[KPAIRS][4];
-#pragma unroll
-        for (int sp = 0; sp < KPAIRS; ++sp)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            const int row = mt * 16 + l16;
-            kraw[sp][mt] = *(const int4_t*)(ks + row * KROW + swz<KROW>(4 * sp + grp, row) * 16);
-          }
-#pragma unroll
-        for (int sp = 0; sp < KPAIRS; ++sp)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) qk_i8_step<NT>(kraw[sp][mt], q.qh[sp], q.ql[sp], acc_h[mt], acc_l[mt]);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) s[mt][nt] = s_from_i8(acc_h[mt][nt], acc_l[mt][nt]);
-      } else {
+      {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -1167,11 +1150,13 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
     // ---- S^T = K Q^T: 4 x NT independent accumulator chains ----
     float4_t s[4][NT];
     if constexpr (I8QK) {
-      int4_t acc_h[4][NT], acc_l[4][NT];
+      int4_t acc[4][3][NT];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] = acc_l[mt][nt] = int4_t{0, 0, 0, 0};
+        for (int k = 0; k < 3; ++k)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[mt][k][nt] = int4_t{0, 0, 0, 0};
 #pragma unroll
       for (int sp = 0; sp < KPAIRS; ++sp) {
         int4_t raw[4];
@@ -1181,12 +1166,12 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
           raw[mt] = *(const int4_t*)(ks + row * KROW + swz<KROW>(4 * sp + grp, row) * 16);
         }
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) qk_i8_step<NT>(raw[mt], q.qh[sp], q.ql[sp], acc_h[mt], acc_l[mt]);
+        for (int mt = 0; mt < 4; ++mt) qk_i8_step<NT>(raw[mt], q.qd[sp], acc[mt]);
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) s[mt][nt] = s_from_i8(acc_h[mt][nt], acc_l[mt][nt]);
+        for (int nt = 0; nt < NT; ++nt) s[mt][nt] = s_from_i8(acc[mt][0][nt], acc[mt][1][nt], acc[mt][2][nt]);
     } else {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -1379,11 +1364,13 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
     // ---- S^T = K Q^T: 4 x NT independent accumulator chains ----
     float4_t s[4][NT];
     if constexpr (!FP8) {
-      int4_t acc_h[4][NT], acc_l[4][NT];
+      int4_t acc[4][3][NT];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc_h[mt][nt] = acc_l[mt][nt] = int4_t{0, 0, 0, 0};
+        for (int k = 0; k < 3; ++k)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[mt][k][nt] = int4_t{0, 0, 0, 0};
 #pragma unroll
       for (int sp = 0; sp < KPAIRS; ++sp) {
         int4_t raw[4];
@@ -1393,12 +1380,12 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
           raw[mt] = *(const int4_t*)(ktile + row * D + swz<D>(4 * sp + grp, row) * 16);
         }
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) qk_i8_step<NT>(raw[mt], q.qh[sp], q.ql[sp], acc_h[mt], acc_l[mt]);
+        for (int mt = 0; mt < 4; ++mt) qk_i8_step<NT>(raw[mt], q.qd[sp], acc[mt]);
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) s[mt][nt] = s_from_i8(acc_h[mt][nt], acc_l[mt][nt]);
+        for (int nt = 0; nt < NT; ++nt) s[mt][nt] = s_from_i8(acc[mt][0][nt], acc[mt][1][nt], acc[mt][2][nt]);
     } else {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)

@@ -139,6 +139,15 @@ EDGE_CASES = {
                                   q_lens=[2, 2, 2], seq_lens_kv=[5, 140, 700], decode=True, chunk_size=256),
     "decode_noncausal_drafts": dict(q_lens=[4, 4], seq_lens_kv=[60, 300], decode=True, causal=False,
                                     chunk_size=128),
+    # query rows whose channels 3 and 77 are 256x the rest: the int8 paths
+    # quantise each query row relative to its maximum, so small channels must
+    # survive next to a large one (one row per decode unit, 40 packed rows,
+    # and the append kernel)
+    "decode_query_outliers_head": dict(scale_mode="head", q_lens=[1, 1, 1], seq_lens_kv=[5, 300, 1200],
+                                       decode=True, chunk_size=256, q_outliers=((3, 77), 256.0)),
+    "spec40_query_outliers_channel": dict(num_q_heads=16, q_lens=[5, 5], seq_lens_kv=[40, 700], decode=True,
+                                          chunk_size=256, q_outliers=((3, 77), 256.0)),
+    "append_query_outliers_channel": dict(q_lens=[40, 7], seq_lens_kv=[100, 5], q_outliers=((3, 77), 256.0)),
     "mla_int8_g16_q2": dict(num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
                             shared_kv=True, scale_mode="tensor", q_lens=[2, 2], seq_lens_kv=[63, 900],
                             decode=True, chunk_size=256),

@@ -125,6 +125,7 @@ def make_workload(
     scale_range=(0.002, 0.03),
     extra_table_cols: int = 0,
     poison_tail: bool = False,
+    q_outliers: Optional[tuple] = None,
     rng: Optional[np.random.Generator] = None,
 ) -> Workload:
     """Draw one workload.  ``q_lens``/``seq_lens_kv`` are given explicitly; the
@@ -133,6 +134,10 @@ def make_workload(
     ``poison_tail`` fills the unused slots of each request's last page with
     0x7F bytes (NaN in e4m3fn, 127 in int8) so a kernel that lets keys beyond
     the sequence leak into the result is caught.
+
+    ``q_outliers = (channels, factor)`` multiplies those query channels by
+    ``factor`` before rounding (outlier channels, as language-model queries
+    have), so each query row spans a wide dynamic range.
     """
     rng = rng if rng is not None else _rng(seed)
     q_lens = np.asarray(q_lens, dtype=np.int32)
@@ -164,6 +169,9 @@ def make_workload(
     total_q = int(cu[-1])
 
     qf = rng.standard_normal((total_q, num_q_heads, head_dim_qk), dtype=np.float32)
+    if q_outliers is not None:
+        chans, factor = q_outliers
+        qf[:, :, list(chans)] *= np.float32(factor)
     q = _to_bf16_bits(qf) if q_dtype == "bf16" else qf
 
     H = num_kv_heads
