@@ -39,7 +39,7 @@ WORKLOAD_TEXT = {
     2: "decode_int8: B=64 q_len=1 H_q=32 H_kv=8 D=128 P=64 L~U[512,4096] int8 per-channel chunk=512",
     3: "append_prefill: B=8 n~U[256,1024] L~U[0,2048] H_q=32 H_kv=8 D=128 P=64 int8 per-head causal",
     4: "spec_decode: B=128 q_len=5 H_q=64 H_kv=8 D=128 P=64 L~lognormal(2048,1)[128,32768] int8 per-channel chunk=1024",
-    5: "mla_decode: B=32 q_len=1 H_q=128 H_kv=1 D_qk=576 D_v=512 P=64 L~U[4096,16384] fp8 per-tensor chunk=2048",
+    5: "mla_decode: B=32 q_len=1 H_q=128 H_kv=1 D_qk=576 D_v=512 P=64 L~U[4096,16384] fp8 per-tensor chunk=3072",
 }
 
 

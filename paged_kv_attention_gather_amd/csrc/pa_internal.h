@@ -41,6 +41,7 @@ struct AttnParams {
   int32_t max_chunks;           // chunk slots in the grid / partial buffers
   int32_t row_tiles;
   int32_t batch;
+  int32_t compact_groups;       // shared-tile kernels: number only the groups that hold work
   int32_t q_is_f32;
   int32_t scale_mode;
   int32_t causal;
@@ -87,6 +88,8 @@ struct AttnConfig {
 };
 
 // Returns hipSuccess, hipErrorInvalidValue when no specialization matches.
+// Workgroups of the kernel `cfg` selects that fit on one CU at once (0: unknown).
+int resident_per_cu(const AttnConfig& cfg);
 hipError_t launch_attention(const AttnConfig& cfg, const AttnParams& p, dim3 grid,
                             hipStream_t stream);
 hipError_t launch_merge(int dv, const MergeParams& p, int batch, int max_q_len,

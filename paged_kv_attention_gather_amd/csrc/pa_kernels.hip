@@ -257,26 +257,24 @@ __device__ __forceinline__ float row_sum4(float v) { return xor32_sum(xor16_sum(
 
 struct Unit {
   int n, tok0, G, rows_total, row0, L, T;
-  int kv_lo, kv_hi, n_chunks, key_end, mask_from, n_tiles;
+  int c, kv_lo, kv_hi, n_chunks, key_end, mask_from, n_tiles;
   bool split;
 };
 
 // Fills `u` for row tile rt and chunk c of request b; false when the unit is empty.
+// tok0, n: the request's first query token and query length; L: its cached keys.
 template <int ROWS>
-__device__ __forceinline__ bool unit_setup(const AttnParams& p, int b, int rt, int c, Unit& u) {
-  if (p.cu_seqlens_q) {
-    u.tok0 = p.cu_seqlens_q[b];
-    u.n = p.cu_seqlens_q[b + 1] - u.tok0;
-  } else {
-    u.n = p.q_len_uniform;
-    u.tok0 = b * u.n;
-  }
+__device__ __forceinline__ bool unit_setup_from(const AttnParams& p, int rt, int c, int tok0, int n, int L,
+                                                Unit& u) {
+  u.tok0 = tok0;
+  u.n = n;
   u.G = p.group;
   u.rows_total = u.n * u.G;
   u.row0 = rt * ROWS;
   if (u.row0 >= u.rows_total) return false;
-  u.L = p.seq_lens_kv[b];
+  u.L = L;
   u.T = u.L + u.n;
+  u.c = c;
   u.kv_lo = 0;
   u.kv_hi = u.T;
   u.n_chunks = 1;
@@ -298,23 +296,84 @@ __device__ __forceinline__ bool unit_setup(const AttnParams& p, int b, int rt, i
   return true;
 }
 
+template <int ROWS>
+__device__ __forceinline__ bool unit_setup(const AttnParams& p, int b, int rt, int c, Unit& u) {
+  const int tok0 = p.cu_seqlens_q ? p.cu_seqlens_q[b] : b * p.q_len_uniform;
+  const int n = p.cu_seqlens_q ? p.cu_seqlens_q[b + 1] - tok0 : p.q_len_uniform;
+  return unit_setup_from<ROWS>(p, rt, c, tok0, n, p.seq_lens_kv[b], u);
+}
+
 // Unit of a workgroup of the shared-tile kernels.  Workgroup L runs on XCD
 // L % 8 (round-robin dispatch).  A group is the row tiles of one (request, KV
 // head, chunk): they read the same KV tiles, so they are kept on one XCD (one
-// L2), in consecutive dispatch slots there; groups are dealt round-robin over
-// the XCDs in (request, head, chunk) order, which keeps the XCDs balanced when
-// requests differ in length.  Later (longer, causal) row tiles go first.
-// False for the padding past the last group.
-__device__ __forceinline__ bool shared_tile_unit(const AttnParams& p, int& b, int& g, int& c, int& rt) {
+// L2), in consecutive dispatch slots there, and groups are dealt round-robin
+// over the XCDs in (request, head, chunk) order.  Later (longer, causal) row
+// tiles go first.
+//
+// Group numbering: when the grid is many rounds of resident workgroups deep,
+// group r is slot r of the (request, head, chunk) grid, empty or not (empty
+// ones exit at once and the dispatcher balances the rest).  When the grid is
+// about one round deep (compact_groups), only the groups that hold work are
+// numbered, so every XCD gets the same number of them (+-1) however the
+// request lengths are spread, and no XCD is left with more workgroups than
+// CUs.  False for the padding past the last group and for empty row tiles;
+// otherwise `u` is set.
+template <int ROWS>
+__device__ __forceinline__ bool shared_tile_unit(const AttnParams& p, int& b, int& g, Unit& u) {
   const int L = (int)blockIdx.x;
+  const int lane = (int)threadIdx.x & 63;
   const int slot = L >> 3;
-  rt = p.row_tiles - 1 - slot % p.row_tiles;
+  const int rt = p.row_tiles - 1 - slot % p.row_tiles;
   int r = (slot / p.row_tiles) * 8 + (L & 7);   // group index
-  c = r % p.max_chunks;
-  r /= p.max_chunks;
-  g = r % p.num_kv_heads;
-  b = r / p.num_kv_heads;
-  return b < p.batch;
+  if (!p.compact_groups) {
+    const int c = r % p.max_chunks;
+    r /= p.max_chunks;
+    g = r % p.num_kv_heads;
+    b = r / p.num_kv_heads;
+    return b < p.batch && unit_setup<ROWS>(p, b, rt, c, u);
+  }
+  // lane l looks at request b0 + l: first token, query length, cached keys
+  auto fetch = [&](int b0, int& tok0, int& n, int& kl) {
+    const int bb = min(b0 + lane, p.batch - 1);
+    tok0 = p.cu_seqlens_q ? p.cu_seqlens_q[bb] : bb * p.q_len_uniform;
+    n = p.cu_seqlens_q ? p.cu_seqlens_q[bb + 1] : tok0 + p.q_len_uniform;
+    kl = p.seq_lens_kv[bb];
+  };
+  int tok0, n, kl;
+  fetch(0, tok0, n, kl);
+  int base = 0;
+  for (int b0 = 0; b0 < p.batch; b0 += 64) {
+    int tok0_nx = 0, n_nx = 0, kl_nx = 0;
+    if (b0 + 64 < p.batch) fetch(b0 + 64, tok0_nx, n_nx, kl_nx);   // next batch in flight
+    n -= tok0;
+    int cnt = 0;   // groups of request b0 + lane: KV heads x chunks with work
+    if (b0 + lane < p.batch && n > 0)
+      cnt = p.num_kv_heads * (p.chunk_size > 0 ? min((kl + n + p.chunk_size - 1) / p.chunk_size, p.max_chunks) : 1);
+    int incl = cnt;   // inclusive prefix sum over the 64 lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += t;
+    }
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    if (r < base + total) {
+      const uint64_t hit = __ballot(base + incl > r);
+      const int lb = (int)__builtin_ctzll(hit);
+      const int start = base + __builtin_amdgcn_readlane(incl - cnt, lb);
+      const int nch = __builtin_amdgcn_readlane(cnt, lb) / p.num_kv_heads;
+      b = b0 + lb;
+      r -= start;
+      g = r / nch;
+      const int c = r - g * nch;
+      return unit_setup_from<ROWS>(p, rt, c, __builtin_amdgcn_readlane(tok0, lb), __builtin_amdgcn_readlane(n, lb),
+                                   __builtin_amdgcn_readlane(kl, lb), u);
+    }
+    base += total;
+    tok0 = tok0_nx;
+    n = n_nx;
+    kl = kl_nx;
+  }
+  return false;
 }
 
 // Query rows of one wave as the B operand of S^T = K Q^T.
@@ -924,11 +983,9 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
   const int grp = lane >> 4;
   // grid = (row tiles * chunks, H_kv, B): the row tiles of one request and head
   // are dispatched next to each other (they read the same KV), longest first
-  int b, g, c, rt;
-  if (!shared_tile_unit(p, b, g, c, rt)) return;
-
+  int b, g;
   Unit u;
-  if (!unit_setup<ROWS>(p, b, rt, c, u)) return;
+  if (!shared_tile_unit<ROWS>(p, b, g, u)) return;
   const int32_t* table_row = p.block_table + (int64_t)b * p.max_pages_per_seq;
   const int key_end = u.key_end, kv_lo = u.kv_lo, n_tiles = u.n_tiles;
 
@@ -1214,7 +1271,7 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
 
   float4_t vsc[MD];
   load_v_scales<DV>(p, g, lane, vsc);
-  write_rows<DV, NT>(p, u, g, c, lane, KV_OFF, q, st, vsc);
+  write_rows<DV, NT>(p, u, g, u.c, lane, KV_OFF, q, st, vsc);
 }
 
 // -------------------------------------------------------- decode attention --
@@ -1537,11 +1594,9 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int l16 = lane & 15;
   const int grp = lane >> 4;
-  int b, g, c, rt;
-  if (!shared_tile_unit(p, b, g, c, rt)) return;   // a chunk's row tiles share an XCD
-
+  int b, g;
   Unit u;
-  if (!unit_setup<ROWS>(p, b, rt, c, u)) return;
+  if (!shared_tile_unit<ROWS>(p, b, g, u)) return;   // a chunk's row tiles share an XCD
   const int32_t* table_row = p.block_table + (int64_t)b * p.max_pages_per_seq;
   const int key_end = u.key_end, kv_lo = u.kv_lo, n_tiles = u.n_tiles;
   const int page_shift = p.page_shift;
@@ -1803,7 +1858,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
     if (grp == 0) lrow_lds[(wave * NTA + nt) * 16 + l16] = lt;
     if (grp == 0 && q.ok[nt]) {
       const int tok = u.tok0 + q.tok[nt];
-      if (u.split) p.part_lse[((int64_t)tok * p.max_chunks + c) * H_q + q.head[nt]] = lse_nat;
+      if (u.split) p.part_lse[((int64_t)tok * p.max_chunks + u.c) * H_q + q.head[nt]] = lse_nat;
       else if (p.lse) p.lse[(int64_t)tok * H_q + q.head[nt]] = lse_nat;
     }
   }
@@ -1828,7 +1883,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
     const float off = lt > 0.f ? KV_OFF : 0.f;
     const int tok = u.tok0 + r / u.G;
     const int h = g * u.G + r % u.G;
-    float* prow = u.split ? p.part_o + (((int64_t)tok * p.max_chunks + c) * H_q + h) * DV : nullptr;
+    float* prow = u.split ? p.part_o + (((int64_t)tok * p.max_chunks + u.c) * H_q + h) * DV : nullptr;
     uint16_t* orow = p.out + ((int64_t)tok * H_q + h) * DV;
 #pragma unroll
     for (int md = 0; md < MDW; ++md) {
@@ -1937,22 +1992,48 @@ hipError_t launch_decode(const AttnParams& p, dim3 grid, hipStream_t stream) {
 }
 
 using LaunchFn = hipError_t (*)(const AttnParams&, dim3, hipStream_t);
+using OccFn = int (*)();
+
+// Workgroups of one kernel that fit on a CU at once (0 if the query fails).
+template <typename K>
+int occupancy_of(K kernel, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess) return 0;
+  return n;
+}
+template <int DQK, int DV, bool FP8, int NT, int NW, bool SHARED, bool HILO, int NSTAGE, bool CONV>
+int occ_one() {
+  return occupancy_of(paged_attn_kernel<DQK, DV, FP8, NT, NW, SHARED, HILO, NSTAGE, CONV>, 64 * NW);
+}
+template <bool FP8, bool HILO>
+int occ_mla() {
+  return occupancy_of(paged_mla_kernel<FP8, HILO>, MLA_WAVES * 64);
+}
+template <int D, bool FP8, int NT, bool HILO, int KS>
+int occ_decode() {
+  return occupancy_of(paged_decode_kernel<D, FP8, NT, HILO, KS>, 64 * KS);
+}
 
 struct Entry {
   AttnConfig cfg;
   LaunchFn fn;
+  OccFn occ;
 };
 
 // nstage == 0 marks the register-staged single-wave decode kernel.
-#define PA_ENTRY(DQK, DV, FP8, NT, NW, SH, HL, NS) \
-  Entry{AttnConfig{DQK, DV, FP8, SH, NT, NW, HL, NS, false}, &launch_one<DQK, DV, FP8, NT, NW, SH, HL, NS, false>}
-#define PA_CONV(D, FP8, HL) \
-  Entry{AttnConfig{D, D, FP8, false, 2, 4, HL, 3, true}, &launch_one<D, D, FP8, 2, 4, false, HL, 3, true>}
+#define PA_ENTRY(DQK, DV, FP8, NT, NW, SH, HL, NS)                                   \
+  Entry{AttnConfig{DQK, DV, FP8, SH, NT, NW, HL, NS, false},                          \
+        &launch_one<DQK, DV, FP8, NT, NW, SH, HL, NS, false>, &occ_one<DQK, DV, FP8, NT, NW, SH, HL, NS, false>}
+#define PA_CONV(D, FP8, HL)                                                           \
+  Entry{AttnConfig{D, D, FP8, false, 2, 4, HL, 3, true}, &launch_one<D, D, FP8, 2, 4, false, HL, 3, true>, \
+        &occ_one<D, D, FP8, 2, 4, false, HL, 3, true>}
 // (for it, nw counts the waves that split one unit's key range)
-#define PA_DEC(D, FP8, NT, HL, KS) \
-  Entry{AttnConfig{D, D, FP8, false, NT, KS, HL, 0, false}, &launch_decode<D, FP8, NT, HL, KS>}
-// the MLA kernel (8 waves and 128 rows, or 4 and 64 with hi + lo query parts) is marked nstage == 1
-#define PA_MLA(FP8, HL) Entry{AttnConfig{576, 512, FP8, true, 1, MLA_WAVES, HL, 1, false}, &launch_mla<FP8, HL>}
+#define PA_DEC(D, FP8, NT, HL, KS)                                                                       \
+  Entry{AttnConfig{D, D, FP8, false, NT, KS, HL, 0, false}, &launch_decode<D, FP8, NT, HL, KS>, \
+        &occ_decode<D, FP8, NT, HL, KS>}
+// the MLA kernel (4 waves and 64 rows) is marked nstage == 1
+#define PA_MLA(FP8, HL) \
+  Entry{AttnConfig{576, 512, FP8, true, 1, MLA_WAVES, HL, 1, false}, &launch_mla<FP8, HL>, &occ_mla<FP8, HL>}
 
 #define PA_SET(D, FP8, HL)                                                                       \
   PA_DEC(D, FP8, 1, HL, 1), PA_DEC(D, FP8, 1, HL, 2), PA_DEC(D, FP8, 1, HL, 4),                    \
@@ -1986,6 +2067,11 @@ hipError_t launch_attention(const AttnConfig& cfg, const AttnParams& p, dim3 gri
   const Entry* e = find_entry(cfg);
   if (!e) return hipErrorInvalidValue;
   return e->fn(p, grid, stream);
+}
+
+int resident_per_cu(const AttnConfig& cfg) {
+  const Entry* e = find_entry(cfg);
+  return e ? e->occ() : 0;
 }
 
 hipError_t launch_merge(int dv, const MergeParams& p, int batch, int max_q_len,

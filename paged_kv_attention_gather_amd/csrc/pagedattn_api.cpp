@@ -262,6 +262,21 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   dim3 grid = decode_kernel
                   ? dim3((unsigned)(p->batch * p->num_kv_heads), (unsigned)row_tiles, (unsigned)max_chunks)
                   : dim3((unsigned)(ceil_div(groups, 8) * 8 * row_tiles), 1, 1);
+  // Number only the groups with work when the whole grid is at most two rounds
+  // of resident workgroups (then an XCD that drew more workgroups than it has
+  // CUs would run a second, mostly idle round); deeper grids balance by dispatch.
+  // PAGEDATTN_COMPACT_GROUPS (0 or 1) overrides the choice, for tuning and tests.
+  ap.compact_groups = 0;
+  const char* cg_env = std::getenv("PAGEDATTN_COMPACT_GROUPS");
+  if (cg_env && (cg_env[0] == '0' || cg_env[0] == '1') && cg_env[1] == 0) {
+    ap.compact_groups = cg_env[0] == '1';
+  } else if (!decode_kernel) {
+    int dev = 0, cus = 0;
+    const int per_cu = pa::resident_per_cu(cfg);
+    if (per_cu > 0 && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      ap.compact_groups = (int64_t)grid.x <= 2LL * per_cu * cus;
+  }
   hipError_t e = pa::launch_attention(cfg, ap, grid, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (p->chunk_size > 0 && !(p->flags & PA_FLAG_DEFER_MERGE)) {

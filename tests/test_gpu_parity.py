@@ -165,6 +165,27 @@ def test_edge_case_parity(case):
     compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what=case)
 
 
+# Shared-tile and MLA workgroups find their (request, head, chunk) either from
+# the grid slot directly or, for grids about one round deep, by numbering only
+# the groups that hold work; both numberings are forced here on cases with
+# empty requests, chunked keys and several row tiles.
+GROUP_NUMBERING_CASES = ["append_zero_len_request", "append_chunked", "spec40_query_outliers_channel",
+                         "mla_int8_g16_q2"]
+
+
+@pytest.mark.parametrize("compact", ["0", "1"])
+@pytest.mark.parametrize("case", GROUP_NUMBERING_CASES)
+def test_group_numbering_parity(case, compact, monkeypatch):
+    need_gpu()
+    monkeypatch.setenv("PAGEDATTN_COMPACT_GROUPS", compact)
+    w = _edge(case, **EDGE_CASES[case])
+    announce(f"edge case {case} compact_groups={compact}")
+    _, (out, lse) = _run(w)
+    O_ref, lse_ref = oracle.attention(w)
+    n = int(w.q_lens.sum())
+    compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what=f"{case} compact={compact}")
+
+
 # Decode units whose key range is split across 2 or 4 waves of a workgroup
 # (states merged in LDS), forced through the tuning override; a request with
 # fewer tiles than waves leaves some waves empty.

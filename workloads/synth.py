@@ -293,7 +293,7 @@ def _cfg4(seed=104, batch=128):
         num_pages=max(16384, 2 * pages), rng=rng)
 
 
-def _cfg5(seed=105, batch=32, chunk_size=2048):
+def _cfg5(seed=105, batch=32, chunk_size=3072):
     rng = _rng(seed)
     L = rng.integers(4096, 16384 + 1, size=batch).astype(np.int32)
     return make_workload(
