@@ -26,6 +26,7 @@ from .reference import (  # noqa: F401
     dequant_rows,
     gather_rows,
     visible_keys,
+    visible_set,
     request_attention,
     attention,
     chunk_partials,

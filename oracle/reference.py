@@ -128,6 +128,25 @@ def visible_keys(L: int, n: int, t: int, causal: bool) -> int:
     return (L + t + 1) if causal else (L + n)
 
 
+def visible_set(L: int, n: int, t: int, causal: bool, tree_row: Optional[np.ndarray] = None) -> np.ndarray:
+    """Boolean visibility of the T = L + n keys for appended token t.
+
+    Without a tree mask this is the prefix of ``visible_keys``.  With one (the
+    c8 decode kernel's optional ``attn_mask``, a ``[bsz, max_q, max_q]`` bool
+    tensor for tree-structured speculative drafts, passed to its mask step
+    with the request's ``batch_id * attn_mask_len * attn_mask_len`` offset),
+    the L cached keys stay visible and appended key L + s is visible to token
+    t exactly when ``tree_row[s]`` (the mask's row t) is nonzero; the mask
+    takes the place of the causal rule inside the appended block."""
+    vis = np.zeros(L + n, dtype=bool)
+    if tree_row is None:
+        vis[:visible_keys(L, n, t, causal)] = True
+    else:
+        vis[:L] = True
+        vis[L:] = np.asarray(tree_row[:n]) != 0
+    return vis
+
+
 # --------------------------------------------------------------- attention ---
 
 def query_heads_of(g: int, G: int):
@@ -173,6 +192,8 @@ def request_attention(w, b: int, key_lo: int = 0, key_hi: Optional[int] = None):
     q0 = int(w.cu_seqlens_q[b])
     q = _q_values(w, np.arange(q0, q0 + n))                        # [n, H_q, D_qk]
     vcache = w.k_cache if w.shared_kv else w.v_cache
+    tree = getattr(w, "tree_mask", None)
+    vis = [visible_set(L, n, t, w.causal, None if tree is None else tree[b, t]) for t in range(n)]
     for g in range(w.num_kv_heads):
         k_raw = gather_rows(w.k_cache, w.block_table[b], g, T, w.page_size, w.head_dim_qk)
         v_raw = gather_rows(vcache, w.block_table[b], g, T, w.page_size, w.head_dim_v)
@@ -181,11 +202,11 @@ def request_attention(w, b: int, key_lo: int = 0, key_hi: Optional[int] = None):
         for h in query_heads_of(g, G):
             z_all = w.sm_scale * (q[:, h, :] @ K.T)                       # [n, T]
             for t in range(n):
-                hi = min(visible_keys(L, n, t, w.causal), key_hi)
-                if hi <= key_lo:
+                sel = np.nonzero(vis[t][key_lo:key_hi])[0] + key_lo
+                if sel.size == 0:
                     continue
-                p, l = _softmax_lse(z_all[t, key_lo:hi])
-                O[t, h] = p @ V[key_lo:hi]
+                p, l = _softmax_lse(z_all[t, sel])
+                O[t, h] = p @ V[sel]
                 lse[t, h] = l
     return O, lse
 

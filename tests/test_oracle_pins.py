@@ -364,6 +364,92 @@ def test_small_variants_are_finite():
         assert np.isfinite(O).all() and np.isfinite(lse).all()
 
 
+# ------------------------------------------------------ draft-tree mask ---
+# The c8 decode kernel's optional attn_mask [bsz, max_q, max_q]: cached keys
+# stay visible, appended key L + s is visible to token t iff mask[b, t, s].
+
+def _with_tree(w, rows_of_b, mask_len=None):
+    ml = mask_len or max(len(r) for r in rows_of_b)
+    tm = np.full((w.batch, ml, ml), 0xAA, np.uint8)
+    for b, rows in enumerate(rows_of_b):
+        n = len(rows)
+        tm[b, :n, :n] = np.asarray(rows, np.uint8)
+    return dataclasses.replace(w, tree_mask=tm)
+
+
+def test_tree_causal_triangle_equals_causal():
+    w = tiny(seed=41, q_lens=(4, 3), seq_lens_kv=(6, 11))
+    tri = [np.tril(np.ones((n, n), np.uint8)) for n in (4, 3)]
+    wt = _with_tree(w, tri, mask_len=6)
+    O, lse = oracle.attention(w)
+    Ot, lset = oracle.attention(wt)
+    assert np.array_equal(O, Ot) and np.array_equal(lse, lset)
+
+
+# Drafts 0..4 with parents 1 -> 0, 2 -> 0, 3 -> 1, 4 -> 2; each token sees its
+# ancestors and itself (written out by hand, not derived from the parents).
+HAND_TREE = [[1, 0, 0, 0, 0],
+             [1, 1, 0, 0, 0],
+             [1, 0, 1, 0, 0],
+             [1, 1, 0, 1, 0],
+             [1, 0, 1, 0, 1]]
+HAND_VISIBLE_DRAFTS = [{0}, {0, 1}, {0, 2}, {0, 1, 3}, {0, 2, 4}]
+
+
+def test_tree_zero_query_closed_form():
+    """Zero queries give uniform weights, and V row j = 100 * e_j (through the
+    page table) makes O[t] the indicator of the visible keys / their count."""
+    L, n = 2, 5
+    w = tiny(seed=43, q_lens=(n,), seq_lens_kv=(L,), H_q=2, H_kv=1, D=8, Dv=8, scale_mode="head",
+             q_dtype="f32")
+    v = np.zeros_like(w.v_cache)
+    for j in range(L + n):
+        v[int(w.block_table[0, j // w.page_size]), 0, j % w.page_size, j] = 100
+    w = dataclasses.replace(w, q=np.zeros_like(w.q), v_cache=v,
+                            v_scale=np.ones_like(w.v_scale))
+    w = _with_tree(w, [HAND_TREE], mask_len=7)
+    O, lse = oracle.attention(w)
+    for t in range(n):
+        keys = set(range(L)) | {L + s for s in HAND_VISIBLE_DRAFTS[t]}
+        want = np.array([100.0 / len(keys) if j in keys else 0.0 for j in range(8)])
+        for h in range(2):
+            np.testing.assert_allclose(O[t, h], want, rtol=0, atol=1e-13)
+            assert abs(lse[t, h] - math.log(len(keys))) <= 1e-14
+
+
+def test_tree_against_torch_sdpa():
+    w = _dense_kv_identity_layout(tiny(seed=45, q_lens=(5, 4), seq_lens_kv=(7, 0), tree=True, tree_mask_len=6))
+    O, lse = oracle.attention(w)
+    npp, P, G = w.block_table.shape[1], w.page_size, w.group
+    Q = _q_f64(w)
+    for b in range(w.batch):
+        n, L = int(w.q_lens[b]), int(w.seq_lens_kv[b])
+        q0 = int(w.cu_seqlens_q[b])
+        mask = torch.ones(n, L + n, dtype=torch.bool)
+        mask[:, L:] = torch.from_numpy(w.tree_mask[b, :n, :n] != 0)
+        for g in range(w.num_kv_heads):
+            kraw = w.k_cache[b * npp:(b + 1) * npp, g].reshape(npp * P, -1)[:L + n]
+            vraw = w.v_cache[b * npp:(b + 1) * npp, g].reshape(npp * P, -1)[:L + n]
+            K = _torch_dequant(kraw, w.kv_dtype, w.k_scale, w.scale_mode, g)
+            V = _torch_dequant(vraw, w.kv_dtype, w.v_scale, w.scale_mode, g)
+            for h in range(g * G, (g + 1) * G):
+                q = Q[q0:q0 + n, h]
+                o = torch.nn.functional.scaled_dot_product_attention(
+                    q[None, None], K[None, None], V[None, None], attn_mask=mask[None, None], scale=w.sm_scale)[0, 0]
+                z = torch.where(mask, (q @ K.T) * w.sm_scale, torch.tensor(-math.inf, dtype=torch.float64))
+                np.testing.assert_allclose(O[q0:q0 + n, h], o.numpy(), rtol=0, atol=1e-12)
+                np.testing.assert_allclose(lse[q0:q0 + n, h], torch.logsumexp(z, 1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_tree_split_merge_equals_unsplit():
+    w = tiny(seed=47, q_lens=(6, 3), seq_lens_kv=(13, 2), tree=True, tree_mask_len=8)
+    O, lse = oracle.attention(w)
+    for C in (4, 8):
+        Os, lses = oracle.attention_split(w, C)
+        np.testing.assert_allclose(Os, O, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lses, lse, rtol=0, atol=1e-12)
+
+
 # --------------------------------------------------------- planted bugs ---
 # Each planted mistake in the oracle must make at least one pin fail.
 
@@ -429,3 +515,19 @@ def test_planted_unweighted_merge_is_caught(monkeypatch):
         return O, np.max(lc, axis=1)
     monkeypatch.setattr(oa, "merge_partials", bad_merge)
     assert _fails(lambda: test_p6_split_merge_equals_unsplit(4))
+
+
+def test_planted_transposed_tree_mask_is_caught(monkeypatch):
+    # reads column t of the hand tree where row t belongs
+    real = oa.visible_set
+    full = np.asarray(HAND_TREE, np.uint8)
+    monkeypatch.setattr(oa, "visible_set", lambda L, n, t, causal, tree_row=None:
+                        real(L, n, t, causal, None if tree_row is None else full[:, t]))
+    assert _fails(test_tree_zero_query_closed_form)
+
+
+def test_planted_tree_mask_ignored_is_caught(monkeypatch):
+    real = oa.visible_set
+    monkeypatch.setattr(oa, "visible_set", lambda L, n, t, causal, tree_row=None: real(L, n, t, causal, None))
+    assert _fails(test_tree_zero_query_closed_form)
+    assert _fails(test_tree_against_torch_sdpa)

@@ -58,6 +58,8 @@ class Workload:
     v_cache: Optional[np.ndarray]
     k_scale: np.ndarray
     v_scale: np.ndarray
+    # [B, mask_len, mask_len] uint8 draft-tree visibility (row t, column s), or None
+    tree_mask: Optional[np.ndarray] = None
 
     @property
     def group(self) -> int:
@@ -126,6 +128,8 @@ def make_workload(
     extra_table_cols: int = 0,
     poison_tail: bool = False,
     q_outliers: Optional[tuple] = None,
+    tree: bool = False,
+    tree_mask_len: Optional[int] = None,
     rng: Optional[np.random.Generator] = None,
 ) -> Workload:
     """Draw one workload.  ``q_lens``/``seq_lens_kv`` are given explicitly; the
@@ -134,6 +138,12 @@ def make_workload(
     ``poison_tail`` fills the unused slots of each request's last page with
     0x7F bytes (NaN in e4m3fn, 127 in int8) so a kernel that lets keys beyond
     the sequence leak into the result is caught.
+
+    ``tree`` draws a random draft tree per request (draft 0 is the root, the
+    parent of draft s >= 1 is uniform over drafts 0..s-1) and stores its
+    ancestor-or-self matrix as ``tree_mask`` [B, mask_len, mask_len] uint8
+    (mask_len = ``tree_mask_len`` or the largest q_len; unused entries 0xAA),
+    drawn after every other array so the rest of the workload is unchanged.
 
     ``q_outliers = (channels, factor)`` multiplies those query channels by
     ``factor`` before rounding (outlier channels, as language-model queries
@@ -229,6 +239,20 @@ def make_workload(
                 if not shared_kv:
                     v_cache[last, :, first_unused:, :] = 0x7F
 
+    tree_mask = None
+    if tree:
+        ml = int(tree_mask_len) if tree_mask_len is not None else int(q_lens.max()) if B else 1
+        tree_mask = np.full((B, ml, ml), 0xAA, dtype=np.uint8)
+        for b in range(B):
+            n = int(q_lens[b])
+            anc = np.zeros((n, n), dtype=np.uint8)
+            for t in range(n):
+                anc[t, t] = 1
+                if t > 0:
+                    parent = int(rng.integers(0, t))
+                    anc[t, :t] = anc[parent, :t]
+            tree_mask[b, :n, :n] = anc
+
     return Workload(
         name=name, seed=seed, batch=B, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
         head_dim_qk=head_dim_qk, head_dim_v=head_dim_v, page_size=P, num_pages=num_pages,
@@ -237,7 +261,7 @@ def make_workload(
         decode_q_len=int(q_lens[0]) if (decode and B) else (1 if decode else None),
         shared_kv=shared_kv, q_lens=q_lens, seq_lens_kv=seq_lens_kv, cu_seqlens_q=cu,
         block_table=block_table, q=q, k_cache=k_cache, v_cache=v_cache,
-        k_scale=k_scale, v_scale=v_scale,
+        k_scale=k_scale, v_scale=v_scale, tree_mask=tree_mask,
     )
 
 
