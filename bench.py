@@ -54,6 +54,8 @@ def work_figures(w):
     table = int(((T + w.page_size - 1) // w.page_size).sum()) * 4
     scales = w.k_scale.nbytes + w.v_scale.nbytes
     total = kv + q_bytes + out_bytes + table + scales
+    if getattr(w, "tree_mask", None) is not None:
+        total += int((w.q_lens.astype(np.int64) ** 2).sum())   # the mask entries that are read
     vis = 0
     for b in range(w.batch):
         n, L = int(w.q_lens[b]), int(w.seq_lens_kv[b])
@@ -151,6 +153,9 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="skip the per-step cache flush")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--tree", action="store_true",
+                    help="spec-decode workload (config 4) with a random draft tree per request, "
+                         "through paged_attn_decode_tree")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -178,8 +183,11 @@ def main():
     from paged_kv_attention_gather_amd.harness import DeviceProblem
     from workloads import config_workload
 
+    if args.tree and args.config != 4:
+        print("--tree applies to the spec-decode workload (--config 4)", file=sys.stderr)
+        sys.exit(2)
     print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
-    w = config_workload(args.config)
+    w = config_workload(args.config, tree=True) if args.tree else config_workload(args.config)
     dp = DeviceProblem(w, chunk_size=args.chunk, defer_merge=True)
     chunk = dp.prob.chunk_size
     kv_bytes, alg_bytes, flops = work_figures(w)
@@ -227,7 +235,7 @@ def main():
         achieved = alg_bytes / (attn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    traffic, note = hbm_traffic(args.config, chunk)
+    traffic, note = (None, "no counters for the draft-tree kernels") if args.tree else hbm_traffic(args.config, chunk)
     roof["traffic"] = traffic
     if traffic is not None:
         roof["traffic_over_alg_bytes"] = round(traffic / alg_bytes, 4)
@@ -245,7 +253,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": compute_dtype(dp),
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.config], "global_batch": int(w.batch),
+        "config": {"workload": WORKLOAD_TEXT[args.config] + (" + random draft tree" if args.tree else ""),
+                   "global_batch": int(w.batch),
                    "kv_dtype": w.kv_dtype, "chunk_size": int(chunk), "cache_flush": not args.no_flush,
                    "kv_bytes": kv_bytes, "alg_bytes": alg_bytes, "flops": flops,
                    "min_ms": round(float(np.min(step_ms)), 5),

@@ -166,6 +166,33 @@ int32_t paged_attn_decode(const pa_problem* prob, int32_t q_len, const void* q,
                           size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attn_decode_tree - speculative decode with a draft tree.
+ *
+ * The decode path of FastDeploy append_attention_c8_impl.cuh takes an
+ * optional attn_mask of shape [bsz, max_q, max_q] for tree-structured drafts
+ * (multi_query_append_attention_c8_warp1_4_kernel hands its mask step the
+ * request's slice at offset batch_id * attn_mask_len * attn_mask_len, and the
+ * host reads attn_mask_len from the mask's second dimension).  Here:
+ *   tree_mask      device, uint8 [B, tree_mask_len, tree_mask_len], row-major,
+ *                  caller-owned, read only.  Entry [b][t][s] != 0 makes
+ *                  appended key L_b + s visible to token t of request b; 0
+ *                  hides it.  Only entries with t, s < q_len are read.
+ *   tree_mask_len  q_len <= tree_mask_len <= 64.
+ * Cached keys (j < L_b) stay visible to every token; the mask takes the place
+ * of the causal rule inside the appended block, whatever prob->causal says.
+ * Everything else is as for paged_attn_decode.  Supported for the int8/fp8
+ * layouts with D_qk 64 or 128 and at most 64 packed rows (q_len * H_q / H_kv);
+ * MLA (576/512) and wider row counts are UNSUPPORTED, a null mask or a length
+ * outside [q_len, 64] is INVALID_ARG.
+ */
+int32_t paged_attn_decode_tree(const pa_problem* prob, int32_t q_len, const void* q,
+                               const void* k_cache, const void* v_cache, const float* k_scale,
+                               const float* v_scale, const int32_t* seq_lens_kv,
+                               const int32_t* block_table, const uint8_t* tree_mask,
+                               int32_t tree_mask_len, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
  * split_kv_merge - log-sum-exp merge of split-KV partials.
  *
  * For every query token t of request b and head h, with C_b = ceil((L_b + n_b)

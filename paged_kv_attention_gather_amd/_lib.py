@@ -36,6 +36,7 @@ EXPORTS = (
     "paged_attn_workspace_size",
     "paged_attn_append",
     "paged_attn_decode",
+    "paged_attn_decode_tree",
     "split_kv_merge",
     "pa_gather_debug",
     "pa_status_string",
@@ -104,6 +105,9 @@ def lib() -> ctypes.CDLL:
     L.paged_attn_decode.argtypes = [ctypes.POINTER(PaProblem), _I32, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _P, _P, ctypes.c_size_t, _P]
     L.paged_attn_decode.restype = _I32
+    L.paged_attn_decode_tree.argtypes = [ctypes.POINTER(PaProblem), _I32, _P, _P, _P, _P, _P, _P, _P,
+                                         _P, _I32, _P, _P, _P, ctypes.c_size_t, _P]
+    L.paged_attn_decode_tree.restype = _I32
     L.split_kv_merge.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                  _P, _P, _P]
     L.split_kv_merge.restype = _I32
@@ -184,6 +188,16 @@ def paged_attn_decode(prob, q_len, q, k_cache, v_cache, k_scale, v_scale, seq_le
         ctypes.byref(prob), int(q_len), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
         _ptr(v_scale), _ptr(seq_lens_kv), _ptr(block_table), _ptr(out), _ptr(lse),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def paged_attn_decode_tree(prob, q_len, q, k_cache, v_cache, k_scale, v_scale, seq_lens_kv,
+                           block_table, tree_mask, tree_mask_len, out, lse=None, workspace=None,
+                           workspace_bytes=None, stream=None) -> None:
+    ws_bytes = _nbytes(workspace) if workspace_bytes is None else int(workspace_bytes)
+    _check(lib().paged_attn_decode_tree(
+        ctypes.byref(prob), int(q_len), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+        _ptr(v_scale), _ptr(seq_lens_kv), _ptr(block_table), _ptr(tree_mask), int(tree_mask_len),
+        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def split_kv_merge(partial_o, partial_lse, cu_seqlens_q, seq_lens_kv, q_len_uniform, batch,

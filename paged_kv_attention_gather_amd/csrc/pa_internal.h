@@ -24,6 +24,7 @@ struct AttnParams {
   const int32_t* cu_seqlens_q;  // null: uniform q_len_uniform tokens per request
   const int32_t* seq_lens_kv;
   const int32_t* block_table;
+  const uint8_t* tree_mask;     // [B, tree_mask_len, tree_mask_len] draft visibility, or null
   uint16_t* out;                // bf16 [total_q, H_q, D_v]
   float* lse;                   // [total_q, H_q] or null
   float* part_o;                // [total_q, max_chunks, H_q, D_v] (split only)
@@ -45,6 +46,7 @@ struct AttnParams {
   int32_t q_is_f32;
   int32_t scale_mode;
   int32_t causal;
+  int32_t tree_mask_len;
   float qk_mult;                // sm_scale * log2(e)
 };
 
@@ -85,6 +87,7 @@ struct AttnConfig {
   bool hilo;        // Q carries per-channel scales or is fp32: f16 hi + lo parts
   int nstage;       // KV tiles staged in LDS (0: register-staged decode kernel, 1: MLA kernel)
   bool f16_tiles;   // shared-tile kernel converts each tile to f16 in LDS once
+  bool tree;        // draft-tree mask over the appended keys (decode-path kernels)
 };
 
 // Returns hipSuccess, hipErrorInvalidValue when no specialization matches.

@@ -289,9 +289,12 @@ __device__ __forceinline__ bool unit_setup_from(const AttnParams& p, int rt, int
   u.split = u.n_chunks > 1;
   const int last_tok = (min(u.rows_total, u.row0 + ROWS) - 1) / u.G;
   const int first_tok = u.row0 / u.G;
-  // Bottom-right causal: token t sees keys j <= L + t.
-  u.key_end = p.causal ? min(u.kv_hi, u.L + last_tok + 1) : u.kv_hi;
-  u.mask_from = p.causal ? min(u.kv_hi, u.L + first_tok + 1) : u.kv_hi;  // keys >= this need masks
+  // Bottom-right causal: token t sees keys j <= L + t.  A draft-tree mask
+  // decides every appended key instead (cached keys stay visible).
+  const bool causal_rule = p.causal && !p.tree_mask;
+  u.key_end = causal_rule ? min(u.kv_hi, u.L + last_tok + 1) : u.kv_hi;
+  u.mask_from = p.tree_mask ? min(u.kv_hi, u.L)
+                            : (p.causal ? min(u.kv_hi, u.L + first_tok + 1) : u.kv_hi);  // keys >= this need masks
   u.n_tiles = u.key_end > u.kv_lo ? (u.key_end - u.kv_lo + TK - 1) / TK : 0;
   return true;
 }
@@ -767,27 +770,84 @@ __device__ __forceinline__ void softmax_init(SoftmaxState<NT, MD>& st) {
   }
 }
 
+// Draft-tree visibility of the rows of one wave (row_base + 16 nt + lane % 16),
+// written to `rows_lds` (two words per row: bits 0..31 and 32..63): bit s is
+// set when appended key L + s is visible to the row's token, i.e.
+// tree_mask[b][t][s] != 0 with s < n.  The four lanes of a row read 16
+// entries each and combine them with two xor shuffles; lane group 0 stores.
+// Rows past the last token read token n - 1 (their results are never
+// written).  The words live in LDS, not registers, because only the tiles
+// that reach the appended keys read them.  The same wave reads them back, so
+// LDS ordering within the wave is all the synchronisation needed.
+template <int NT>
+__device__ __forceinline__ void load_tree_bits(const AttnParams& p, int b, const Unit& u, int row_base, int lane,
+                                               uint32_t* rows_lds) {
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int ml = p.tree_mask_len;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = row_base + nt * 16 + l16;
+    const int t = min(r / u.G, u.n - 1);
+    const uint8_t* row = p.tree_mask + ((int64_t)b * ml + t) * ml;
+    uint32_t bits = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int sidx = 16 * grp + e;
+      const uint8_t v = row[min(sidx, u.n - 1)];
+      bits |= (uint32_t)(sidx < u.n && v != 0) << e;
+    }
+    uint32_t w = bits << (16 * (grp & 1));
+    w |= (uint32_t)__shfl_xor((int)w, 16, 64);
+    const uint32_t other = (uint32_t)__shfl_xor((int)w, 32, 64);
+    if (grp == 0) {
+      rows_lds[2 * (nt * 16 + l16)] = w;
+      rows_lds[2 * (nt * 16 + l16) + 1] = other;
+    }
+  }
+}
+
 // Masks one 64-key tile of S^T, updates the running max/denominator, rescales
 // O when a row maximum grows, and returns P^T (f16) in the B-operand layout of
 // the PV MFMA: pb[ks][nt] holds keys {32ks + 4grp + i, 32ks + 16 + 4grp + i}.
-template <int NT, int MD, typename QT>
+template <int NT, int MD, typename QT, bool TREE = false>
 __device__ __forceinline__ void softmax_tile(const AttnParams& p, const Unit& u, int kbase, int grp,
                                              const QT& q, float4_t (&s)[4][NT],
-                                             SoftmaxState<NT, MD>& st, half8_t (&pb)[2][NT]) {
+                                             SoftmaxState<NT, MD>& st, half8_t (&pb)[2][NT],
+                                             const uint32_t* tree_rows = nullptr) {
   const bool need_mask = kbase + TK > u.mask_from;
   const half2_t ones2 = {(_Float16)1.0f, (_Float16)1.0f};
   float alpha[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     if (need_mask) {
-      const int lim = p.causal ? min(u.kv_hi, u.L + q.tok[nt] + 1) : u.kv_hi;
+      if constexpr (TREE) {
+        // Visibility of keys kbase + j, j < 64, as one 64-bit word: the cached
+        // keys below min(kv_hi, L), the appended keys whose draft bit is set,
+        // nothing at or past kv_hi.  Lane group grp tests bits 16 mt + 4 grp + i.
+        const int r16 = (int)threadIdx.x & 15;
+        const uint64_t drafts = ((uint64_t)tree_rows[2 * (nt * 16 + r16) + 1] << 32) | tree_rows[2 * (nt * 16 + r16)];
+        const int dl = u.L - kbase;   // key kbase + j is draft j - dl
+        const uint64_t vis_d = dl >= 0 ? (dl < 64 ? drafts << dl : 0ull) : (-dl < 64 ? drafts >> (-dl) : 0ull);
+        const int nc = min(max(min(u.kv_hi, u.L) - kbase, 0), 64);
+        const int ne = min(max(u.kv_hi - kbase, 0), 64);
+        const uint64_t below_c = nc >= 64 ? ~0ull : ((1ull << nc) - 1);
+        const uint64_t below_e = ne >= 64 ? ~0ull : ((1ull << ne) - 1);
+        const uint64_t vis = ((below_c | vis_d) & below_e) >> (4 * grp);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kbase + mt * 16 + grp * 4 + i;
-          if (key >= lim) s[mt][nt][i] = -INFINITY;
-        }
+          for (int i = 0; i < 4; ++i)
+            if (!((vis >> (mt * 16 + i)) & 1ull)) s[mt][nt][i] = -INFINITY;
+      } else {
+        const int lim = p.causal ? min(u.kv_hi, u.L + q.tok[nt] + 1) : u.kv_hi;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kbase + mt * 16 + grp * 4 + i;
+            if (key >= lim) s[mt][nt][i] = -INFINITY;
+          }
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -940,7 +1000,7 @@ __device__ __forceinline__ void load_v_scales(const AttnParams& p, int g, int la
 // CONV: the workgroup converts each raw K/V tile to f16 tiles in LDS once
 // (each wave a quarter) and the waves read MFMA operands from those, instead of
 // every wave converting the whole raw tile for its own rows (D = 128 only).
-template <int DQK, int DV, bool FP8, int NT, int NW, bool SHARED, bool HILO, int NSTAGE, bool CONV>
+template <int DQK, int DV, bool FP8, int NT, int NW, bool SHARED, bool HILO, int NSTAGE, bool CONV, bool TREE>
 __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void paged_attn_kernel(AttnParams p) {
   constexpr int ROWS_W = 16 * NT;
   constexpr int ROWS = ROWS_W * NW;
@@ -1098,6 +1158,9 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
   } else {
     load_query<DQK, NT, HILO>(p, u, g, u.row0 + wave * ROWS_W, lane, KV_OFF, q);
   }
+  __shared__ uint32_t tree_lds[TREE ? NW * NT * 32 : 1];
+  uint32_t* const tb = tree_lds + (TREE ? wave * NT * 32 : 0);
+  if constexpr (TREE) load_tree_bits<NT>(p, b, u, u.row0 + wave * ROWS_W, lane, tb);
   SoftmaxState<NT, MD> st;
   softmax_init(st);
 
@@ -1176,7 +1239,7 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
             }
       }
       half8_t pb[2][NT];
-      softmax_tile<NT, MD>(p, u, kbase, grp, q, s, st, pb);
+      softmax_tile<NT, MD, QT, TREE>(p, u, kbase, grp, q, s, st, pb, tb);
       // O^T += V^T P^T, V^T by the 16-bit transposed read of the f16 V tile
       const int tr_j = l16 >> 2, tr_q = l16 & 3;
 #pragma unroll
@@ -1265,7 +1328,7 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
     }
 
     half8_t pb[2][NT];
-    softmax_tile<NT, MD>(p, u, kbase, grp, q, s, st, pb);
+    softmax_tile<NT, MD, QT, TREE>(p, u, kbase, grp, q, s, st, pb, tb);
     pv_tile<FP8, NT, MD, VROW>(vs, lane, pb, st);
   }
 
@@ -1286,7 +1349,7 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
 // iteration to arrive while the register file, not LDS, holds the bytes in
 // flight.  K is then read back in the MFMA A-operand layout, V transposed.
 
-template <int D, bool FP8, int NT, bool HILO, int KS>
+template <int D, bool FP8, int NT, bool HILO, int KS, bool TREE>
 __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnParams p) {
   constexpr int KPAIRS = D / 64;
   constexpr int MD = D / 16;
@@ -1402,6 +1465,9 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
   float vs_lane[D / 64];   // per-channel V scales (other modes re-read the first one)
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) vs_lane[i] = p.v_scale[fold_channel ? (int64_t)g * D + lane + 64 * i : 0];
+  __shared__ uint32_t tree_lds[TREE ? NT * 32 : 1];   // tree kernels run one wave per unit
+  uint32_t* const tb = tree_lds;
+  if constexpr (TREE) load_tree_bits<NT>(p, b, u, u.row0, lane, tb);
   load_tile(min(wv, n_tiles - 1));
   QT q;
   if constexpr (FP8) query_finish<D, NT, HILO>(p, u, g, u.row0, lane, KV_OFF, qraw, q);
@@ -1479,7 +1545,7 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
     }
 
     half8_t pb[2][NT];
-    softmax_tile<NT, MD>(p, u, kbase, grp, q, s, st, pb);
+    softmax_tile<NT, MD, QT, TREE>(p, u, kbase, grp, q, s, st, pb, tb);
     pv_tile<FP8, NT, MD, D>(vtile, lane, pb, st);
   }
 
@@ -1972,9 +2038,9 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherParams p) {
 // ------------------------------------------------------------------ launch --
 
 namespace {
-template <int DQK, int DV, bool FP8, int NT, int NW, bool SHARED, bool HILO, int NSTAGE, bool CONV>
+template <int DQK, int DV, bool FP8, int NT, int NW, bool SHARED, bool HILO, int NSTAGE, bool CONV, bool TREE>
 hipError_t launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((paged_attn_kernel<DQK, DV, FP8, NT, NW, SHARED, HILO, NSTAGE, CONV>), grid,
+  hipLaunchKernelGGL((paged_attn_kernel<DQK, DV, FP8, NT, NW, SHARED, HILO, NSTAGE, CONV, TREE>), grid,
                      dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
 }
@@ -1985,9 +2051,9 @@ hipError_t launch_mla(const AttnParams& p, dim3 grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool FP8, int NT, bool HILO, int KS>
+template <int D, bool FP8, int NT, bool HILO, int KS, bool TREE>
 hipError_t launch_decode(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((paged_decode_kernel<D, FP8, NT, HILO, KS>), grid, dim3(64 * KS), 0, stream, p);
+  hipLaunchKernelGGL((paged_decode_kernel<D, FP8, NT, HILO, KS, TREE>), grid, dim3(64 * KS), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -2001,17 +2067,17 @@ int occupancy_of(K kernel, int threads) {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess) return 0;
   return n;
 }
-template <int DQK, int DV, bool FP8, int NT, int NW, bool SHARED, bool HILO, int NSTAGE, bool CONV>
+template <int DQK, int DV, bool FP8, int NT, int NW, bool SHARED, bool HILO, int NSTAGE, bool CONV, bool TREE>
 int occ_one() {
-  return occupancy_of(paged_attn_kernel<DQK, DV, FP8, NT, NW, SHARED, HILO, NSTAGE, CONV>, 64 * NW);
+  return occupancy_of(paged_attn_kernel<DQK, DV, FP8, NT, NW, SHARED, HILO, NSTAGE, CONV, TREE>, 64 * NW);
 }
 template <bool FP8, bool HILO>
 int occ_mla() {
   return occupancy_of(paged_mla_kernel<FP8, HILO>, MLA_WAVES * 64);
 }
-template <int D, bool FP8, int NT, bool HILO, int KS>
+template <int D, bool FP8, int NT, bool HILO, int KS, bool TREE>
 int occ_decode() {
-  return occupancy_of(paged_decode_kernel<D, FP8, NT, HILO, KS>, 64 * KS);
+  return occupancy_of(paged_decode_kernel<D, FP8, NT, HILO, KS, TREE>, 64 * KS);
 }
 
 struct Entry {
@@ -2021,25 +2087,32 @@ struct Entry {
 };
 
 // nstage == 0 marks the register-staged single-wave decode kernel.
-#define PA_ENTRY(DQK, DV, FP8, NT, NW, SH, HL, NS)                                   \
-  Entry{AttnConfig{DQK, DV, FP8, SH, NT, NW, HL, NS, false},                          \
-        &launch_one<DQK, DV, FP8, NT, NW, SH, HL, NS, false>, &occ_one<DQK, DV, FP8, NT, NW, SH, HL, NS, false>}
-#define PA_CONV(D, FP8, HL)                                                           \
-  Entry{AttnConfig{D, D, FP8, false, 2, 4, HL, 3, true}, &launch_one<D, D, FP8, 2, 4, false, HL, 3, true>, \
-        &occ_one<D, D, FP8, 2, 4, false, HL, 3, true>}
+#define PA_ENTRY_T(DQK, DV, FP8, NT, NW, SH, HL, NS, TR)                                      \
+  Entry{AttnConfig{DQK, DV, FP8, SH, NT, NW, HL, NS, false, TR},                                \
+        &launch_one<DQK, DV, FP8, NT, NW, SH, HL, NS, false, TR>,                               \
+        &occ_one<DQK, DV, FP8, NT, NW, SH, HL, NS, false, TR>}
+#define PA_ENTRY(DQK, DV, FP8, NT, NW, SH, HL, NS) PA_ENTRY_T(DQK, DV, FP8, NT, NW, SH, HL, NS, false)
+#define PA_CONV(D, FP8, HL)                                                                     \
+  Entry{AttnConfig{D, D, FP8, false, 2, 4, HL, 3, true, false},                                 \
+        &launch_one<D, D, FP8, 2, 4, false, HL, 3, true, false>, &occ_one<D, D, FP8, 2, 4, false, HL, 3, true, false>}
 // (for it, nw counts the waves that split one unit's key range)
-#define PA_DEC(D, FP8, NT, HL, KS)                                                                       \
-  Entry{AttnConfig{D, D, FP8, false, NT, KS, HL, 0, false}, &launch_decode<D, FP8, NT, HL, KS>, \
-        &occ_decode<D, FP8, NT, HL, KS>}
+#define PA_DEC_T(D, FP8, NT, HL, KS, TR)                                                        \
+  Entry{AttnConfig{D, D, FP8, false, NT, KS, HL, 0, false, TR}, &launch_decode<D, FP8, NT, HL, KS, TR>, \
+        &occ_decode<D, FP8, NT, HL, KS, TR>}
+#define PA_DEC(D, FP8, NT, HL, KS) PA_DEC_T(D, FP8, NT, HL, KS, false)
 // the MLA kernel (4 waves and 64 rows) is marked nstage == 1
 #define PA_MLA(FP8, HL) \
-  Entry{AttnConfig{576, 512, FP8, true, 1, MLA_WAVES, HL, 1, false}, &launch_mla<FP8, HL>, &occ_mla<FP8, HL>}
+  Entry{AttnConfig{576, 512, FP8, true, 1, MLA_WAVES, HL, 1, false, false}, &launch_mla<FP8, HL>, &occ_mla<FP8, HL>}
 
 #define PA_SET(D, FP8, HL)                                                                       \
   PA_DEC(D, FP8, 1, HL, 1), PA_DEC(D, FP8, 1, HL, 2), PA_DEC(D, FP8, 1, HL, 4),                    \
       PA_DEC(D, FP8, 2, HL, 1), PA_DEC(D, FP8, 2, HL, 2), PA_DEC(D, FP8, 2, HL, 4),                 \
       PA_ENTRY(D, D, FP8, 1, 3, false, HL, 2), PA_ENTRY(D, D, FP8, 1, 4, false, HL, 2),             \
       PA_ENTRY(D, D, FP8, 2, 4, false, HL, 2)
+// draft-tree variants: up to 64 packed rows, one wave per decode unit
+#define PA_TREE_SET(D, FP8, HL)                                                                  \
+  PA_DEC_T(D, FP8, 1, HL, 1, true), PA_DEC_T(D, FP8, 2, HL, 1, true),                              \
+      PA_ENTRY_T(D, D, FP8, 1, 3, false, HL, 2, true), PA_ENTRY_T(D, D, FP8, 1, 4, false, HL, 2, true)
 
 const Entry kTable[] = {
     PA_SET(64, false, false),   PA_SET(64, false, true),
@@ -2048,13 +2121,18 @@ const Entry kTable[] = {
     PA_SET(128, true, false),  PA_SET(128, true, true),
     PA_MLA(true, false), PA_MLA(true, true), PA_MLA(false, false), PA_MLA(false, true),
     PA_CONV(128, false, false), PA_CONV(128, false, true), PA_CONV(128, true, false), PA_CONV(128, true, true),
+    PA_TREE_SET(64, false, false),  PA_TREE_SET(64, false, true),
+    PA_TREE_SET(64, true, false),   PA_TREE_SET(64, true, true),
+    PA_TREE_SET(128, false, false), PA_TREE_SET(128, false, true),
+    PA_TREE_SET(128, true, false),  PA_TREE_SET(128, true, true),
 };
 
 const Entry* find_entry(const AttnConfig& c) {
   for (const Entry& e : kTable)
     if (e.cfg.dqk == c.dqk && e.cfg.dv == c.dv && e.cfg.fp8 == c.fp8 &&
         e.cfg.shared_kv == c.shared_kv && e.cfg.nt == c.nt && e.cfg.nw == c.nw &&
-        e.cfg.hilo == c.hilo && e.cfg.nstage == c.nstage && e.cfg.f16_tiles == c.f16_tiles)
+        e.cfg.hilo == c.hilo && e.cfg.nstage == c.nstage && e.cfg.f16_tiles == c.f16_tiles &&
+        e.cfg.tree == c.tree)
       return &e;
   return nullptr;
 }

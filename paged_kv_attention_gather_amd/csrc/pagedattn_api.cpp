@@ -119,11 +119,13 @@ WorkspaceLayout workspace_layout(const pa_problem* p, int64_t total_q) {
   return w;
 }
 
+// Draft trees (tree_mask != null, decode only) are checked by the caller.
 int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_t total_q,
                          const void* q, const void* k_cache, const void* v_cache,
                          const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
                          const int32_t* seq_lens_kv, const int32_t* block_table, void* out,
-                         float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                         float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                         const uint8_t* tree_mask = nullptr, int32_t tree_mask_len = 0) {
   int32_t st = check_problem(p);
   if (st != PA_OK) return st;
   if (decode) {
@@ -171,8 +173,15 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   }
   const int64_t G = p->num_q_heads / p->num_kv_heads;
   const int64_t rows_max = (int64_t)(decode ? q_len : p->max_q_len) * G;
+  if (tree_mask) {
+    if (shared) return fail(PA_ERR_UNSUPPORTED, "draft-tree masks are not supported with the MLA layout");
+    if (rows_max > 64)
+      return fail(PA_ERR_UNSUPPORTED, "draft-tree masks need q_len * G <= 64 packed rows (got %lld)",
+                  (long long)rows_max);
+  }
 
   pa::AttnConfig cfg{};
+  cfg.tree = tree_mask != nullptr;
   cfg.dqk = p->head_dim_qk;
   cfg.dv = p->head_dim_v;
   cfg.fp8 = p->kv_dtype == PA_DTYPE_FP8_E4M3;
@@ -185,7 +194,7 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   } else if (rows_max <= 32) {
     // register-staged decode kernel
     cfg.nt = (int)ceil_div(rows_max, 16);
-    cfg.nw = decode_split_waves(p, cfg.nt);
+    cfg.nw = cfg.tree ? 1 : decode_split_waves(p, cfg.nt);
     cfg.nstage = 0;
   } else if (rows_max <= 64) {
     // shared-tile kernel, 16 rows per wave, 3 or 4 waves sharing LDS-DMA tiles
@@ -226,6 +235,8 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   ap.cu_seqlens_q = decode ? nullptr : cu_seqlens_q;
   ap.seq_lens_kv = seq_lens_kv;
   ap.block_table = block_table;
+  ap.tree_mask = tree_mask;
+  ap.tree_mask_len = tree_mask_len;
   ap.out = static_cast<uint16_t*>(out);
   ap.lse = lse;
   ap.part_o = wl.total ? static_cast<float*>(workspace) : nullptr;
@@ -326,6 +337,22 @@ int32_t paged_attn_decode(const pa_problem* prob, int32_t q_len, const void* q,
   return attention_common(prob, true, q_len, total_q, q, k_cache, v_cache, k_scale, v_scale,
                           nullptr, seq_lens_kv, block_table, out, lse, workspace, workspace_bytes,
                           stream);
+}
+
+int32_t paged_attn_decode_tree(const pa_problem* prob, int32_t q_len, const void* q,
+                               const void* k_cache, const void* v_cache, const float* k_scale,
+                               const float* v_scale, const int32_t* seq_lens_kv,
+                               const int32_t* block_table, const uint8_t* tree_mask,
+                               int32_t tree_mask_len, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!prob) return fail(PA_ERR_INVALID_ARG, "problem is NULL");
+  if (!tree_mask) return fail(PA_ERR_INVALID_ARG, "tree_mask is NULL");
+  if (tree_mask_len < q_len || tree_mask_len > 64)
+    return fail(PA_ERR_INVALID_ARG, "tree_mask_len %d must lie in [q_len = %d, 64]", tree_mask_len, q_len);
+  const int64_t total_q = (int64_t)prob->batch * q_len;
+  return attention_common(prob, true, q_len, total_q, q, k_cache, v_cache, k_scale, v_scale,
+                          nullptr, seq_lens_kv, block_table, out, lse, workspace, workspace_bytes,
+                          stream, tree_mask, tree_mask_len);
 }
 
 int32_t split_kv_merge(const float* partial_o, const float* partial_lse,

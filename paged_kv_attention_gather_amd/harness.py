@@ -59,6 +59,8 @@ class DeviceProblem:
         self.q_lens = torch.from_numpy(np.ascontiguousarray(w.q_lens, dtype=np.int32)).to(dev)
         self.cu_seqlens_q = torch.from_numpy(np.ascontiguousarray(w.cu_seqlens_q, dtype=np.int32)).to(dev)
         self.block_table = torch.from_numpy(np.ascontiguousarray(w.block_table, dtype=np.int32)).to(dev)
+        tm = getattr(w, "tree_mask", None)
+        self.tree_mask = None if tm is None else torch.from_numpy(np.ascontiguousarray(tm, dtype=np.uint8)).to(dev)
         self.prob = problem_for(w, chunk_size=chunk_size, flags=L.FLAG_DEFER_MERGE if defer_merge else 0)
         self.total_q = int(w.total_q)
         self.out = torch.empty((self.total_q, w.num_q_heads, w.head_dim_v), dtype=torch.bfloat16, device=dev)
@@ -69,7 +71,12 @@ class DeviceProblem:
 
     def run(self, stream=None) -> None:
         """Enqueue one attention call (plus the split-KV merge when chunked)."""
-        if self.decode:
+        if self.tree_mask is not None:
+            L.paged_attn_decode_tree(self.prob, int(self.w.decode_q_len), self.q, self.k_cache, self.v_cache,
+                                     self.k_scale, self.v_scale, self.seq_lens_kv, self.block_table,
+                                     self.tree_mask, int(self.tree_mask.shape[1]), self.out, self.lse,
+                                     self.workspace, self.workspace_bytes, stream)
+        elif self.decode:
             L.paged_attn_decode(self.prob, int(self.w.decode_q_len), self.q, self.k_cache, self.v_cache,
                                 self.k_scale, self.v_scale, self.seq_lens_kv, self.block_table, self.out,
                                 self.lse, self.workspace, self.workspace_bytes, stream)

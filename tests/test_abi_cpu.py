@@ -145,6 +145,35 @@ def test_mla_layout_requires_shared_rows(lib):
     assert _decode(prob, v=FAKE + 4096) == L.PA_ERR_UNSUPPORTED
 
 
+def _tree(prob, q_len=1, mask=FAKE, mask_len=4, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, lens=FAKE, table=FAKE, out=FAKE, lse=None)
+    p.update(ptrs)
+    return L.lib().paged_attn_decode_tree(ctypes.byref(prob) if prob is not None else None, q_len, p["q"],
+                                          p["k"], p["v"], p["ks"], p["vs"], p["lens"], p["table"], mask,
+                                          mask_len, p["out"], p["lse"], None, 0, None)
+
+
+def test_tree_decode_validation(lib):
+    prob = base_problem(chunk_size=0, max_q_len=16)
+    assert _tree(None) == L.PA_ERR_INVALID_ARG
+    assert _tree(prob, q_len=4, mask=None) == L.PA_ERR_INVALID_ARG
+    assert _tree(prob, q_len=4, mask_len=3) == L.PA_ERR_INVALID_ARG        # shorter than q_len
+    assert _tree(prob, q_len=4, mask_len=65) == L.PA_ERR_INVALID_ARG       # beyond the 64-draft bitmask
+    assert _tree(prob, q_len=17, mask_len=17) == L.PA_ERR_INVALID_ARG      # q_len > max_q_len
+
+
+def test_tree_decode_row_limit_and_mla(lib):
+    # G = 8: 9 drafts are 72 packed rows, more than the tree kernels hold
+    prob = base_problem(num_q_heads=16, num_kv_heads=2, q_row_stride=16 * 128, chunk_size=0, max_q_len=16)
+    assert _tree(prob, q_len=9, mask_len=9) == L.PA_ERR_UNSUPPORTED
+    assert "64" in lib.pa_last_error().decode()
+    mla = base_problem(head_dim_qk=576, head_dim_v=512, num_q_heads=16, num_kv_heads=1,
+                       q_row_stride=16 * 576, k_stride_page=64 * 576, k_stride_head=64 * 576,
+                       k_stride_token=576, v_stride_page=64 * 576, v_stride_head=64 * 576,
+                       v_stride_token=576, chunk_size=0)
+    assert _tree(mla, q_len=2, mask_len=2) == L.PA_ERR_UNSUPPORTED
+
+
 def test_empty_batch_is_a_no_op(lib):
     assert _decode(base_problem(batch=0)) == L.PA_OK
     assert _append(base_problem(batch=0), total_q=0) == L.PA_OK

@@ -186,6 +186,62 @@ def test_group_numbering_parity(case, compact, monkeypatch):
     compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what=f"{case} compact={compact}")
 
 
+# Draft trees (paged_attn_decode_tree): every tree kernel (decode kernel with
+# 1 or 2 row tiles, shared-tile kernel with 3 or 4 waves), drafts that straddle
+# chunk and page boundaries, fp8 and fp32 queries, a mask wider than q_len
+# whose unused entries are nonzero, and a poisoned page tail.
+TREE_CASES = {
+    "tree_q4_g4_nt1": dict(q_lens=[4, 4, 4], seq_lens_kv=[0, 70, 600], decode=True, chunk_size=256,
+                           tree=True, tree_mask_len=6),
+    "tree_q4_g8_nt2_chunk64": dict(num_q_heads=16, q_lens=[4, 4], seq_lens_kv=[62, 300], decode=True,
+                                   chunk_size=64, tree=True),
+    "tree_q5_g8_nw3": dict(num_q_heads=16, q_lens=[5, 5], seq_lens_kv=[40, 700], decode=True, chunk_size=256,
+                           tree=True, tree_mask_len=8),
+    "tree_q8_g8_nw4_nochunk": dict(num_q_heads=16, q_lens=[8, 8], seq_lens_kv=[1, 190], decode=True,
+                                   chunk_size=0, tree=True),
+    "tree_d64_fp8_tensor": dict(head_dim_qk=64, head_dim_v=64, kv_dtype="fp8_e4m3", scale_mode="tensor",
+                                q_lens=[3, 3, 3], seq_lens_kv=[5, 140, 700], decode=True, chunk_size=256,
+                                tree=True),
+    "tree_f32_query_page16": dict(q_dtype="f32", page_size=16, q_lens=[6, 6], seq_lens_kv=[13, 77],
+                                  decode=True, chunk_size=64, tree=True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(TREE_CASES))
+def test_tree_decode_parity(case):
+    need_gpu()
+    w = _edge(case, **TREE_CASES[case])
+    announce(f"tree decode {case}")
+    _, (out, lse) = _run(w)
+    O_ref, lse_ref = oracle.attention(w)
+    n = int(w.q_lens.sum())
+    compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what=case)
+
+
+def test_tree_decode_poisoned_tail():
+    need_gpu()
+    w = _edge("tree_poison", num_q_heads=16, q_lens=[5, 5], seq_lens_kv=[59, 123], decode=True,
+              chunk_size=128, tree=True, poison_tail=True)
+    announce("tree decode poisoned tail")
+    _, (out, lse) = _run(w)
+    O_ref, lse_ref = oracle.attention(w)
+    compare(out, lse, O_ref, lse_ref, what="tree+poison")
+
+
+def test_tree_decode_full_spec_workload_sampled():
+    need_gpu()
+    w = config_workload(4, tree=True)
+    announce("tree decode on the full spec-decode workload (sampled requests)")
+    _, (out, lse) = _run(w)
+    rng = np.random.default_rng(1404)
+    T = w.kv_tokens()
+    pick = {int(np.argmax(T)), int(np.argmin(T))}
+    pick.update(rng.choice(w.batch, size=4, replace=False).tolist())
+    reqs = sorted(pick)
+    O_ref, lse_ref = oracle.attention(w, requests=reqs)
+    compare(out, lse, O_ref, lse_ref, rows=token_rows(w, reqs), what=f"spec_decode+tree requests {reqs}")
+
+
 # Decode units whose key range is split across 2 or 4 waves of a workgroup
 # (states merged in LDS), forced through the tuning override; a request with
 # fewer tiles than waves leaves some waves empty.

@@ -304,7 +304,7 @@ def _cfg3(seed=103, batch=8):
         rng=rng)
 
 
-def _cfg4(seed=104, batch=128):
+def _cfg4(seed=104, batch=128, tree=False):
     rng = _rng(seed)
     L = np.exp(rng.normal(math.log(2048.0), 1.0, size=batch))
     L = np.clip(np.rint(L), 128, 32768).astype(np.int32)
@@ -314,7 +314,7 @@ def _cfg4(seed=104, batch=128):
         num_q_heads=64, num_kv_heads=8, head_dim_qk=128, head_dim_v=128, page_size=64,
         q_dtype="bf16", kv_dtype="i8", scale_mode="channel", causal=True,
         sm_scale=1.0 / math.sqrt(128), chunk_size=1024, decode=True,
-        num_pages=max(16384, 2 * pages), rng=rng)
+        num_pages=max(16384, 2 * pages), tree=tree, rng=rng)
 
 
 def _cfg5(seed=105, batch=32, chunk_size=3072):
