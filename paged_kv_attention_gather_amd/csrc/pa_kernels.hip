@@ -1225,6 +1225,11 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
             const int key = mt * 16 + l16;
             ka[sp][mt][h] = *(const half8_t*)(f16t + key * FROW + kf_swz(8 * sp + 2 * grp + h, key) * 16);
           }
+      // QK, softmax and PV at raised wave priority: the other workgroup on the
+      // CU, if it is converting its tile or waiting at a barrier, yields the
+      // issue slots (measured 174 -> 163 us on the append workload; priority
+      // around the MFMA loops alone gave nothing)
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int sp = 0; sp < KPAIRS; ++sp)
 #pragma unroll
@@ -1264,6 +1269,7 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
           for (int nt = 0; nt < NT; ++nt)
             st.o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[md], pb[ks2][nt], st.o[md][nt], 0, 0, 0);
       }
+      __builtin_amdgcn_s_setprio(0);
       continue;
     }
 
