@@ -198,8 +198,10 @@ int32_t paged_attn_decode_tree(const pa_problem* prob, int32_t q_len, const void
  * For every query token t of request b and head h, with C_b = ceil((L_b + n_b)
  * / chunk_size) > 1: M = max_c lse_c, w_c = exp(lse_c - M), out = sum_c w_c O_c
  * / sum_c w_c (bf16), lse = M + ln sum_c w_c.  Chunks with lse_c = -inf carry
- * weight 0.  Rows with C_b <= 1 are left untouched (they were written
- * directly).  Follows FlashInfer persistent.cuh (BlockBatchReductionPersistent,
+ * weight 0; a row whose chunks are all -inf gets out = 0, lse = -inf.  Rows
+ * with C_b <= 1 are left untouched (they were written directly).  Slots c
+ * with C_b <= c < max_chunks may be read (they stay inside the buffers above)
+ * and their contents are ignored, whatever they hold.  Follows FlashInfer persistent.cuh (BlockBatchReductionPersistent,
  * which skips rows with 0 or 1 partials) and XQA mla_sm120.cu
  * (mergePartialOutputs); C_b is derived from the lengths as in FastDeploy's
  * merge launches.

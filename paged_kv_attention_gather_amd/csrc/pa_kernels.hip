@@ -1980,6 +1980,7 @@ template <int DV>
 __global__ __launch_bounds__(256) void split_merge_kernel(MergeParams p) {
   constexpr int LPR = DV / 4;
   constexpr int RPB = 256 / LPR;
+  constexpr int MB = 8;   // chunk slots loaded per round trip
   const int b = blockIdx.y;
   int n, tok0;
   if (p.cu_seqlens_q) {
@@ -1989,9 +1990,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MergeParams p) {
     n = p.q_len_uniform;
     tok0 = b * n;
   }
-  const int T = p.seq_lens_kv[b] + n;
-  const int nc = min((T + p.chunk_size - 1) / p.chunk_size, p.max_chunks);
-  if (nc <= 1) return;
+  const int kv_cached = p.seq_lens_kv[b];
   const int pair = blockIdx.x * RPB + (int)threadIdx.x / LPR;
   if (pair >= n * p.num_q_heads) return;
   const int t = pair / p.num_q_heads;
@@ -2001,28 +2000,54 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MergeParams p) {
   const int64_t H = p.num_q_heads;
   const float* lrow = p.part_lse + tok * p.max_chunks * H + h;
   const float* orow = p.part_o + (tok * p.max_chunks * H + h) * DV + lane * 4;
-  // Every lane of the row reads the (few, cached) lse values itself: no
-  // cross-lane step, and the loads of both passes are independent of each
-  // other so they are issued back to back.
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int cc = 0; cc < nc; ++cc) M = fmaxf(M, lrow[(int64_t)cc * H]);
+  // One pass with a running maximum.  Slots 0 and 1, which every merged row
+  // has, are loaded before the chunk count is known (with the length's load);
+  // later slots go out MB at a time, only those below the count.  So a row
+  // with 2 chunks costs one memory round trip and one with up to 2 + MB two,
+  // and single-chunk rows (written by the attention kernel, left alone here)
+  // read only two slots.  Loaded slots past the count are dropped by selects.
+  float M = -INFINITY, den = 0.f;
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-#pragma unroll 4
-  for (int cc = 0; cc < nc; ++cc) {
-    const float lc = lrow[(int64_t)cc * H];
-    const float4_t v = *(const float4_t*)(orow + (int64_t)cc * H * DV);
-    const float w = lc == -INFINITY ? 0.f : __expf(lc - M);
-    den += w;
-    acc += w * v;
+  auto merge_slot = [&](bool use, float l, const float4_t& o) {
+    use = use && l != -INFINITY;
+    const float m_new = use ? fmaxf(M, l) : M;
+    const float sc = m_new == M ? 1.f : __expf(M - m_new);   // M = -inf gives 0
+    const float w = use ? __expf(l - m_new) : 0.f;
+    den = den * sc + w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = acc[e] * sc + (use ? w * o[e] : 0.f);
+    M = m_new;
+  };
+  const int64_t c1 = min(1, p.max_chunks - 1);
+  const float l0 = lrow[0], l1 = lrow[c1 * H];
+  const float4_t o0 = *(const float4_t*)orow;
+  const float4_t o1 = *(const float4_t*)(orow + c1 * H * DV);
+  const int T = kv_cached + n;
+  const int nc = min((T + p.chunk_size - 1) / p.chunk_size, p.max_chunks);
+  merge_slot(nc > 0, l0, o0);
+  merge_slot(nc > 1, l1, o1);
+  for (int c0 = 2; c0 < nc; c0 += MB) {
+    float lc[MB];
+    float4_t v[MB];
+#pragma unroll
+    for (int k = 0; k < MB; ++k) {
+      lc[k] = -INFINITY;
+      v[k] = float4_t{0.f, 0.f, 0.f, 0.f};
+      if (c0 + k < nc) {
+        lc[k] = lrow[(int64_t)(c0 + k) * H];
+        v[k] = *(const float4_t*)(orow + (int64_t)(c0 + k) * H * DV);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < MB; ++k) merge_slot(c0 + k < nc, lc[k], v[k]);
   }
-  const float inv = 1.f / den;
+  if (nc <= 1) return;
+  const float inv = den > 0.f ? 1.f / den : 0.f;   // no visible key in any chunk: O = 0, lse = -inf
   uint16_t* dst = p.out + (tok * H + h) * DV + lane * 4;
   const uint32_t w0 = (uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16);
   const uint32_t w1 = (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16);
   *(int2_t*)dst = int2_t{(int)w0, (int)w1};
-  if (p.lse && lane == 0) p.lse[tok * H + h] = M + __logf(den);
+  if (p.lse && lane == 0) p.lse[tok * H + h] = den > 0.f ? M + __logf(den) : -INFINITY;
 }
 
 // ------------------------------------------------------------ debug gather --
