@@ -148,6 +148,13 @@ EDGE_CASES = {
     "spec40_query_outliers_channel": dict(num_q_heads=16, q_lens=[5, 5], seq_lens_kv=[40, 700], decode=True,
                                           chunk_size=256, q_outliers=((3, 77), 256.0)),
     "append_query_outliers_channel": dict(q_lens=[40, 7], seq_lens_kv=[100, 5], q_outliers=((3, 77), 256.0)),
+    # the limits of the ABI: decode q_len 64 (256 packed rows, the append-shaped
+    # kernel through the decode entry), page size 1024 (a 64-key tile inside
+    # one page, 16 tiles per page), and the tree's 64-draft bitmask
+    "decode_q64_g4_max_rows": dict(q_lens=[64, 64], seq_lens_kv=[3, 400], decode=True, chunk_size=256),
+    "append_page1024": dict(page_size=1024, q_lens=[70, 5], seq_lens_kv=[1500, 1019]),
+    "decode_page1024_chunked": dict(page_size=1024, q_lens=[2, 2, 2], seq_lens_kv=[2047, 1, 1100],
+                                    decode=True, chunk_size=512),
     "mla_int8_g16_q2": dict(num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
                             shared_kv=True, scale_mode="tensor", q_lens=[2, 2], seq_lens_kv=[63, 900],
                             decode=True, chunk_size=256),
@@ -202,6 +209,8 @@ TREE_CASES = {
     "tree_d64_fp8_tensor": dict(head_dim_qk=64, head_dim_v=64, kv_dtype="fp8_e4m3", scale_mode="tensor",
                                 q_lens=[3, 3, 3], seq_lens_kv=[5, 140, 700], decode=True, chunk_size=256,
                                 tree=True),
+    "tree_q64_g1_full_mask": dict(num_q_heads=2, num_kv_heads=2, q_lens=[64, 64], seq_lens_kv=[0, 333],
+                                  decode=True, chunk_size=128, tree=True),
     "tree_f32_query_page16": dict(q_dtype="f32", page_size=16, q_lens=[6, 6], seq_lens_kv=[13, 77],
                                   decode=True, chunk_size=64, tree=True),
 }
