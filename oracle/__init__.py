@@ -15,6 +15,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import it.  The product library never calls into it, and it
 shares no code, tables or helpers with the HIP kernels.
 
+``oracle.kv_write`` holds the cache append write (quantize the new tokens and
+scatter them into their pages).
+
 Every function is pinned by tests under ``tests/test_oracle_*.py`` against
 closed forms, invariants, brute force and independent library routines; no
 function here is "parity unpinned".
@@ -34,3 +37,4 @@ from .reference import (  # noqa: F401
     attention_split,
     gather_bytes,
 )
+from . import kv_write  # noqa: F401,E402

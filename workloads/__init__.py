@@ -11,4 +11,5 @@ from .synth import (  # noqa: F401
     make_workload,
     config_workload,
     small_variant,
+    kv_write_inputs,
 )

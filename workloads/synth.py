@@ -384,3 +384,31 @@ def small_variant(idx: int, seed: Optional[int] = None, poison_tail: bool = Fals
             sm_scale=1.0 / math.sqrt(576), chunk_size=512, decode=True, shared_kv=True,
             num_pages=64, poison_tail=poison_tail)
     raise ValueError(idx)
+
+
+def kv_write_inputs(w: Workload, seed: Optional[int] = None, spread: float = 1.3, in_dtype: str = "bf16"):
+    """New K/V rows for the cache append write of workload ``w``: one row per
+    appended token (``w.q_lens`` per request, ``[total_q, H_kv, D]``), values
+    N(0, 1) scaled so that value / scale spans about +-(spread x the code
+    range) (127 for int8, 448 for e4m3fn), so that some codes saturate.
+    Returns ``(k_vals, v_vals, k_in, v_in)``: binary32 values and the stored
+    input arrays (bf16 bit patterns as uint16, or float32); ``v_*`` are None
+    for the shared MLA layout."""
+    rng = _rng(w.seed + 7919 if seed is None else seed)
+    top = 127.0 if w.kv_dtype == "i8" else 448.0
+    H = w.num_kv_heads
+
+    def draw(D, scale):
+        s = np.asarray(scale, dtype=np.float32)
+        mag = float(np.median(s)) * top * spread / 3.0
+        x = (rng.standard_normal((w.total_q, H, D), dtype=np.float32) * np.float32(mag)).astype(np.float32)
+        if in_dtype == "bf16":
+            bits = _to_bf16_bits(x)
+            return (bits.astype(np.uint32) << 16).view(np.float32), bits
+        return x, x
+
+    k_vals, k_in = draw(w.head_dim_qk, w.k_scale)
+    if w.shared_kv:
+        return k_vals, None, k_in, None
+    v_vals, v_in = draw(w.head_dim_v, w.v_scale)
+    return k_vals, v_vals, k_in, v_in
