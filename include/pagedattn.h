@@ -193,6 +193,42 @@ int32_t paged_attn_decode_tree(const pa_problem* prob, int32_t q_len, const void
                                size_t workspace_bytes, void* stream);
 
 /*
+ * paged_kv_write - the cache append write: quantize the new tokens' K/V rows
+ * and scatter them into their pages.
+ *
+ * FastDeploy append_attention_c8_impl.cuh attends over kv_len = seq_lens_kv +
+ * q_len keys and reads the appended tokens' K/V from the cache; this call puts
+ * them there.  Token t (0 <= t < n_b) of request b goes to position L_b + t:
+ * page block_table[b][(L_b + t) / P], slot (L_b + t) % P, bytes 0..D-1 of the
+ * row.  With s the scale of its (head, channel) as for dequantization (per
+ * tensor, per KV head or per channel, prob->scale_mode) and r = x / s one
+ * correctly rounded binary32 division:
+ *   int8     code = clamp(round_half_even(r), -127, 127)
+ *   e4m3fn   code = nearest e4m3fn value (ties to an even mantissa), finite
+ *            values beyond 448 saturate to +-448, NaN gives 0x7F
+ * (the pages fix only the read side, value = code * s; this is its inverse).
+ *   prob            as for attention; q_dtype is the dtype of k_new / v_new
+ *                   (BF16 or F32), max_q_len bounds every n_b (grid size).
+ *   total_new       rows of k_new / v_new (= cu_seqlens_new[B]).
+ *   k_new, v_new    device [total_new, H_kv, D_qk] and [total_new, H_kv, D_v],
+ *                   dense, 16-byte aligned, read only.  For the shared latent
+ *                   layout (D_qk 576) v_new must be NULL: the 576-byte K row
+ *                   holds V in its first 512 bytes.
+ *   cu_seqlens_new  device int32 [B+1] prefix sums of n_b.
+ *   seq_lens_kv     device int32 [B] cached tokens L_b before this append.
+ *   block_table     device int32 [B, max_pages_per_seq]; entries up to page
+ *                   (L_b + n_b - 1) / P must name pages of the pool.
+ *   k_scale/v_scale device fp32 scales (layout of prob->scale_mode).
+ *   k_cache/v_cache device caches, written in place; nothing else changes.
+ * Rows of different requests must not map to the same slot (their order is
+ * unspecified).  Enqueued on `stream`; validation errors enqueue nothing.
+ */
+int32_t paged_kv_write(const pa_problem* prob, int32_t total_new, const void* k_new, const void* v_new,
+                       const int32_t* cu_seqlens_new, const int32_t* seq_lens_kv,
+                       const int32_t* block_table, const float* k_scale, const float* v_scale,
+                       void* k_cache, void* v_cache, void* stream);
+
+/*
  * split_kv_merge - log-sum-exp merge of split-KV partials.
  *
  * For every query token t of request b and head h, with C_b = ceil((L_b + n_b)

@@ -111,9 +111,10 @@ def kv_write(cache: np.ndarray, new_rows: np.ndarray, scale: np.ndarray, mode: s
     div = scale_table(scale, mode, H, D)
     for b in range(len(seq_lens_kv)):
         L = int(seq_lens_kv[b])
-        for r in range(int(cu_seqlens_new[b]), int(cu_seqlens_new[b + 1])):
-            pos = L + r - int(cu_seqlens_new[b])
+        r0, r1 = int(cu_seqlens_new[b]), int(cu_seqlens_new[b + 1])
+        codes = quantize(new_rows[r0:r1], np.broadcast_to(div, (r1 - r0, H, D)), kv_dtype)
+        for t in range(r1 - r0):
+            pos = L + t
             page = int(block_table[b][pos // page_size])
-            for h in range(H):
-                out[page, h, pos % page_size, :D] = quantize(new_rows[r, h], div[h], kv_dtype)
+            out[page, :, pos % page_size, :D] = codes[t]
     return out

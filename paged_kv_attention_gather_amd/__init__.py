@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     paged_attn_append,
     paged_attn_decode,
     paged_attn_decode_tree,
+    paged_kv_write,
     pa_gather_debug,
     split_kv_merge,
     workspace_size,

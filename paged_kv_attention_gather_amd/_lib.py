@@ -37,6 +37,7 @@ EXPORTS = (
     "paged_attn_append",
     "paged_attn_decode",
     "paged_attn_decode_tree",
+    "paged_kv_write",
     "split_kv_merge",
     "pa_gather_debug",
     "pa_status_string",
@@ -108,6 +109,8 @@ def lib() -> ctypes.CDLL:
     L.paged_attn_decode_tree.argtypes = [ctypes.POINTER(PaProblem), _I32, _P, _P, _P, _P, _P, _P, _P,
                                          _P, _I32, _P, _P, _P, ctypes.c_size_t, _P]
     L.paged_attn_decode_tree.restype = _I32
+    L.paged_kv_write.argtypes = [ctypes.POINTER(PaProblem), _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    L.paged_kv_write.restype = _I32
     L.split_kv_merge.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                  _P, _P, _P]
     L.split_kv_merge.restype = _I32
@@ -198,6 +201,13 @@ def paged_attn_decode_tree(prob, q_len, q, k_cache, v_cache, k_scale, v_scale, s
         ctypes.byref(prob), int(q_len), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
         _ptr(v_scale), _ptr(seq_lens_kv), _ptr(block_table), _ptr(tree_mask), int(tree_mask_len),
         _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def paged_kv_write(prob, total_new, k_new, v_new, cu_seqlens_new, seq_lens_kv, block_table, k_scale,
+                   v_scale, k_cache, v_cache, stream=None) -> None:
+    _check(lib().paged_kv_write(
+        ctypes.byref(prob), int(total_new), _ptr(k_new), _ptr(v_new), _ptr(cu_seqlens_new), _ptr(seq_lens_kv),
+        _ptr(block_table), _ptr(k_scale), _ptr(v_scale), _ptr(k_cache), _ptr(v_cache), _stream(stream)))
 
 
 def split_kv_merge(partial_o, partial_lse, cu_seqlens_q, seq_lens_kv, q_len_uniform, batch,

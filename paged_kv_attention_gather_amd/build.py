@@ -2,8 +2,9 @@
 
     python -m paged_kv_attention_gather_amd.build
 
-compiles csrc/pa_kernels.hip (the kernels) and csrc/pagedattn_api.cpp (the C
-ABI) into one shared library next to this file.  Every HIP source is compiled
+compiles csrc/pa_kernels.hip (the attention kernels), csrc/kv_write.hip (the
+cache append write) and csrc/pagedattn_api.cpp (the C ABI) into one shared
+library next to this file.  Every HIP source is compiled
 with packed fp32 VALU ops disabled.
 """
 import os
@@ -18,7 +19,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["pa_kernels.hip", "pagedattn_api.cpp"]
+SOURCES = ["pa_kernels.hip", "kv_write.hip", "pagedattn_api.cpp"]
 
 
 def source_digest() -> str:

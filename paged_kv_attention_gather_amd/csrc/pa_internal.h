@@ -77,6 +77,23 @@ struct GatherParams {
   int32_t t_max;
 };
 
+// One launch of the KV-cache append write (kv_write.hip).  Grid (token
+// slices of tokens_per_block, B); dv = 0 writes K rows only (shared layout).
+struct KvWriteParams {
+  const void* k_new;            // [total_new, H_kv, dk] bf16 bits or fp32
+  const void* v_new;            // [total_new, H_kv, dv] or null
+  const int32_t* cu_seqlens_new;
+  const int32_t* seq_lens_kv;
+  const int32_t* block_table;
+  const float* k_scale;
+  const float* v_scale;
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  int64_t k_stride_page, k_stride_head, k_stride_token;
+  int64_t v_stride_page, v_stride_head, v_stride_token;
+  int32_t num_kv_heads, dk, dv, page_shift, max_pages_per_seq, scale_mode, tokens_per_block;
+};
+
 // Compiled attention specializations.
 struct AttnConfig {
   int dqk, dv;      // head dims
@@ -98,6 +115,8 @@ hipError_t launch_attention(const AttnConfig& cfg, const AttnParams& p, dim3 gri
 hipError_t launch_merge(int dv, const MergeParams& p, int batch, int max_q_len,
                         hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, int batch, hipStream_t stream);
+hipError_t launch_kv_write(const KvWriteParams& p, bool fp8, bool f32_in, int batch, int max_new,
+                           hipStream_t stream);
 bool attention_supported(const AttnConfig& cfg);
 
 }  // namespace pa

@@ -427,6 +427,71 @@ int32_t pa_gather_debug(const pa_problem* prob, const void* k_cache, const int32
   return ok();
 }
 
+int32_t paged_kv_write(const pa_problem* prob, int32_t total_new, const void* k_new, const void* v_new,
+                       const int32_t* cu_seqlens_new, const int32_t* seq_lens_kv,
+                       const int32_t* block_table, const float* k_scale, const float* v_scale,
+                       void* k_cache, void* v_cache, void* stream) {
+  int32_t st = check_problem(prob);
+  if (st != PA_OK) return st;
+  if (total_new < 0) return fail(PA_ERR_INVALID_ARG, "total_new %d < 0", total_new);
+  if (prob->batch == 0 || total_new == 0 || prob->max_q_len == 0) return ok();
+  const bool shared = prob->head_dim_qk == 576;
+  if (!k_new || !cu_seqlens_new || !seq_lens_kv || !block_table || !k_scale || !k_cache)
+    return fail(PA_ERR_INVALID_ARG, "a required device pointer is NULL");
+  if (shared) {
+    if (v_new) return fail(PA_ERR_INVALID_ARG, "the shared latent layout writes K rows only: v_new must be NULL");
+  } else if (!v_new || !v_scale || !v_cache) {
+    return fail(PA_ERR_INVALID_ARG, "v_new, v_scale and v_cache are required");
+  }
+  if (prob->q_dtype != PA_DTYPE_BF16 && prob->q_dtype != PA_DTYPE_F32)
+    return fail(PA_ERR_UNSUPPORTED, "q_dtype %d: new rows must be BF16 or F32", prob->q_dtype);
+  if (prob->kv_dtype != PA_DTYPE_I8 && prob->kv_dtype != PA_DTYPE_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "kv_dtype %d: only I8 and FP8_E4M3 caches", prob->kv_dtype);
+  if (prob->scale_mode < PA_SCALE_PER_TENSOR || prob->scale_mode > PA_SCALE_PER_CHANNEL)
+    return fail(PA_ERR_INVALID_ARG, "scale_mode %d", prob->scale_mode);
+  if (!aligned16(k_new) || (v_new && !aligned16(v_new)) || !aligned16(k_cache) || (!shared && !aligned16(v_cache)))
+    return fail(PA_ERR_INVALID_ARG, "k_new, v_new and the caches must be 16-byte aligned");
+  const int64_t ks[3] = {prob->k_stride_page, prob->k_stride_head, prob->k_stride_token};
+  const int64_t vs[3] = {prob->v_stride_page, prob->v_stride_head, prob->v_stride_token};
+  for (int i = 0; i < 3; ++i)
+    if (ks[i] <= 0 || ks[i] % 16 || (!shared && (vs[i] <= 0 || vs[i] % 16)))
+      return fail(PA_ERR_INVALID_ARG, "cache strides must be positive multiples of 16 bytes");
+  if (prob->k_stride_token < prob->head_dim_qk || (!shared && prob->v_stride_token < prob->head_dim_v))
+    return fail(PA_ERR_INVALID_ARG, "token stride shorter than the head dim");
+
+  pa::KvWriteParams kp{};
+  kp.k_new = k_new;
+  kp.v_new = shared ? nullptr : v_new;
+  kp.cu_seqlens_new = cu_seqlens_new;
+  kp.seq_lens_kv = seq_lens_kv;
+  kp.block_table = block_table;
+  kp.k_scale = k_scale;
+  kp.v_scale = shared ? k_scale : v_scale;
+  kp.k_cache = static_cast<uint8_t*>(k_cache);
+  kp.v_cache = shared ? nullptr : static_cast<uint8_t*>(v_cache);
+  kp.k_stride_page = prob->k_stride_page;
+  kp.k_stride_head = prob->k_stride_head;
+  kp.k_stride_token = prob->k_stride_token;
+  kp.v_stride_page = prob->v_stride_page;
+  kp.v_stride_head = prob->v_stride_head;
+  kp.v_stride_token = prob->v_stride_token;
+  kp.num_kv_heads = prob->num_kv_heads;
+  kp.dk = prob->head_dim_qk;
+  kp.dv = shared ? 0 : prob->head_dim_v;
+  kp.page_shift = log2_exact(prob->page_size);
+  kp.max_pages_per_seq = prob->max_pages_per_seq;
+  kp.scale_mode = prob->scale_mode;
+  // about 1024 eight-channel items per workgroup
+  const int per_tok = prob->num_kv_heads * (kp.dk + kp.dv) / 8;
+  kp.tokens_per_block = std::max(1, 1024 / std::max(1, per_tok));
+  if ((int64_t)ceil_div(prob->max_q_len, kp.tokens_per_block) > 0x7fffffffLL)
+    return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  hipError_t e = pa::launch_kv_write(kp, prob->kv_dtype == PA_DTYPE_FP8_E4M3, prob->q_dtype == PA_DTYPE_F32,
+                                     prob->batch, prob->max_q_len, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "cache write launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* pa_status_string(int32_t status) {
   switch (status) {
     case PA_OK: return "PA_OK";

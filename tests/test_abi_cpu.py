@@ -174,6 +174,33 @@ def test_tree_decode_row_limit_and_mla(lib):
     assert _tree(mla, q_len=2, mask_len=2) == L.PA_ERR_UNSUPPORTED
 
 
+def _kvw(prob, total_new=4, **ptrs):
+    p = dict(k=FAKE, v=FAKE, cu=FAKE, lens=FAKE, table=FAKE, ks=FAKE, vs=FAKE, kc=FAKE, vc=FAKE)
+    p.update(ptrs)
+    return L.lib().paged_kv_write(ctypes.byref(prob) if prob is not None else None, total_new, p["k"], p["v"],
+                                  p["cu"], p["lens"], p["table"], p["ks"], p["vs"], p["kc"], p["vc"], None)
+
+
+def test_kv_write_validation(lib):
+    prob = base_problem(chunk_size=0)
+    assert _kvw(None) == L.PA_ERR_INVALID_ARG
+    assert _kvw(prob, total_new=-1) == L.PA_ERR_INVALID_ARG
+    assert _kvw(prob, k=None) == L.PA_ERR_INVALID_ARG
+    assert _kvw(prob, v=None) == L.PA_ERR_INVALID_ARG
+    assert _kvw(prob, cu=None) == L.PA_ERR_INVALID_ARG
+    assert _kvw(prob, k=FAKE + 8) == L.PA_ERR_INVALID_ARG            # misaligned rows
+    assert _kvw(base_problem(chunk_size=0, q_dtype=7)) == L.PA_ERR_UNSUPPORTED
+    assert _kvw(base_problem(chunk_size=0, kv_dtype=L.DTYPE_BF16)) == L.PA_ERR_UNSUPPORTED
+    assert _kvw(base_problem(chunk_size=0, page_size=48)) == L.PA_ERR_UNSUPPORTED
+    mla = base_problem(head_dim_qk=576, head_dim_v=512, num_q_heads=16, num_kv_heads=1,
+                       q_row_stride=16 * 576, k_stride_page=64 * 576, k_stride_head=64 * 576,
+                       k_stride_token=576, v_stride_page=64 * 576, v_stride_head=64 * 576,
+                       v_stride_token=576, chunk_size=0)
+    assert _kvw(mla) == L.PA_ERR_INVALID_ARG                          # v_new must be NULL there
+    assert _kvw(base_problem(batch=0)) == L.PA_OK
+    assert _kvw(prob, total_new=0) == L.PA_OK
+
+
 def test_empty_batch_is_a_no_op(lib):
     assert _decode(base_problem(batch=0)) == L.PA_OK
     assert _append(base_problem(batch=0), total_q=0) == L.PA_OK
