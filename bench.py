@@ -143,6 +143,61 @@ def hbm_traffic(config, chunk):
     return int(round(fetch + write)), "profiles/hbm_traffic_counters.md"
 
 
+def bench_kv_write(args):
+    """One JSON line for paged_kv_write: quantize + scatter the appended tokens
+    of workload ``args.config`` (bf16 rows in, int8/fp8 bytes out)."""
+    import torch
+    import paged_kv_attention_gather_amd as P
+    from paged_kv_attention_gather_amd.harness import problem_for
+    from workloads import config_workload, kv_write_inputs
+    w = config_workload(args.config)
+    _, _, k_in, v_in = kv_write_inputs(w, spread=1.2, in_dtype="bf16")
+    dev = "cuda"
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a.astype(dt))).to(dev)
+    kn = torch.from_numpy(np.ascontiguousarray(k_in).view(np.int16)).to(dev)
+    vn = None if v_in is None else torch.from_numpy(np.ascontiguousarray(v_in).view(np.int16)).to(dev)
+    kc = torch.from_numpy(np.ascontiguousarray(w.k_cache)).to(dev)
+    vc = None if w.shared_kv else torch.from_numpy(np.ascontiguousarray(w.v_cache)).to(dev)
+    from paged_kv_attention_gather_amd import _lib as L
+    prob = problem_for(w)
+    prob.q_dtype = L.DTYPE_BF16   # the new rows are bf16
+    args_dev = (t(w.cu_seqlens_q, np.int32), t(w.seq_lens_kv, np.int32), t(w.block_table, np.int32),
+                t(w.k_scale, np.float32), t(w.v_scale, np.float32))
+    elems = int(w.total_q) * w.num_kv_heads * (w.head_dim_qk + (0 if w.shared_kv else w.head_dim_v))
+    nbytes = elems * 3 + int(w.batch) * 4 * 2   # bf16 in, one byte out, lengths
+    stream = torch.cuda.current_stream()
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+
+    def call():
+        P.paged_kv_write(prob, int(w.total_q), kn, vn, args_dev[0], args_dev[1], args_dev[2], args_dev[3],
+                         args_dev[4], kc, vc)
+
+    for _ in range(args.warmup):
+        flush.max()
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        flush.max()
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    line = {"metric": "kv cache append write: HBM GB/s (bf16 rows in, quantized bytes scattered to pages)",
+            "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": w.kv_dtype, "data": "synthetic",
+            "config": {"workload": WORKLOAD_TEXT[args.config] + " (its appended tokens)",
+                       "tokens": int(w.total_q), "elements": elems, "bytes": nbytes},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "traffic_source": "no counters taken for the write kernel",
+                         "kernel": "kv_write_kernel", "kernel_ms": round(ms, 5)}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +208,9 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="skip the per-step cache flush")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--kv-write", action="store_true",
+                    help="time the cache append write (paged_kv_write) of the workload's appended "
+                         "tokens instead of attention")
     ap.add_argument("--tree", action="store_true",
                     help="spec-decode workload (config 4) with a random draft tree per request, "
                          "through paged_attn_decode_tree")
@@ -183,6 +241,9 @@ def main():
     from paged_kv_attention_gather_amd.harness import DeviceProblem
     from workloads import config_workload
 
+    if args.kv_write:
+        bench_kv_write(args)
+        return
     if args.tree and args.config != 4:
         print("--tree applies to the spec-decode workload (--config 4)", file=sys.stderr)
         sys.exit(2)

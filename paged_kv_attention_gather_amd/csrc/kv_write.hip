@@ -10,9 +10,10 @@
 // (ties to even, saturating at 448) for fp8, with x / s one correctly rounded
 // binary32 division.
 //
-// Memory-bound scatter: a workgroup takes TPB tokens of one request; each
-// thread step handles 8 consecutive channels of one (token, head, matrix) row:
-// one 16-byte (bf16) or two 16-byte (fp32) loads, one 8-byte store.
+// Memory-bound scatter: a workgroup takes the tokens of one request that make
+// about 256 items; an item is 8 consecutive channels of one (token, head,
+// matrix) row: one 16-byte (bf16) or two 16-byte (fp32) loads, one 8-byte
+// store.  Wide rows (more than 256 items per token) loop.
 #include <hip/hip_runtime.h>
 
 #include "pa_internal.h"
