@@ -231,8 +231,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print("bench.py runs on one GPU: the paged attention path has no multi-GPU leg in this "
-              "build (sharding by request or KV head needs no communication; see DESIGN.md).",
+        print("bench.py runs on one GPU: the paged attention path has no multi-GPU leg (sharding by request "
+              "or by KV head needs no communication between GPUs).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -33,13 +33,13 @@ WORKLOADS = {
 }
 
 KT_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
-          "-d $R/gpurun_out/prof/kt_c{c} -o run -- python3 $R/bench.py --config {c} --steps 10 "
+          "-d $OUT/kt_c{c} -o run -- python3 $R/bench.py --config {c} --steps 10 "
           "--warmup 3 --no-cpu-baseline")
 PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} --output-format csv "
-           "-d $R/gpurun_out/prof/pmc_c{c}_{ctr} -o run -- python3 $R/bench.py --config {c} --steps 3 "
+           "-d $OUT/pmc_c{c}_{ctr} -o run -- python3 $R/bench.py --config {c} --steps 3 "
            "--warmup 1 --no-cpu-baseline")
 COPY_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} --output-format csv "
-            "-d $R/gpurun_out/prof/pmc_copy_{ctr} -o run -- python3 $R/bench.py --copy-probe-mib {mib}")
+            "-d $OUT/pmc_copy_{ctr} -o run -- python3 $R/bench.py --copy-probe-mib {mib}")
 
 
 def _short(name: str) -> str:
@@ -87,7 +87,7 @@ def summarize(root: str, out: str, copy_mib: int) -> None:
         att = [r for r in rows if _short(r["Name"]).startswith("pa::" + kname)]
         lines = [f"# {kname} on {wname} (bench.py --config {c})", "",
                  f"Kernel sources: `{digest}` (build.source_digest()).", "",
-                 "Command (R = repository root):", "", "```", KT_CMD.format(c=c), "```", "",
+                 "Command (R = repository root, OUT = the profile output directory):", "", "```", KT_CMD.format(c=c), "```", "",
                  "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
         for r in rows:
             lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -126,7 +126,7 @@ def summarize(root: str, out: str, copy_mib: int) -> None:
              f"{copy_mib} MiB (reads and writes {copy_mib} MiB) reads FETCH_SIZE {copy['FETCH_SIZE']:.0f} KiB "
              f"and WRITE_SIZE {copy['WRITE_SIZE']:.0f} KiB, so HBM bytes = FETCH_SIZE x {fetch_factor} + "
              f"WRITE_SIZE x {write_factor} (KiB).", "",
-             "Commands (R = repository root), one pass per counter:", "", "```",
+             "Commands (R = repository root, OUT = the profile output directory), one pass per counter:", "", "```",
              COPY_CMD.format(ctr="FETCH_SIZE", mib=copy_mib), COPY_CMD.format(ctr="WRITE_SIZE", mib=copy_mib)]
     for c in table:
         lines += [PMC_CMD.format(ctr="FETCH_SIZE", c=c), PMC_CMD.format(ctr="WRITE_SIZE", c=c)]
