@@ -86,7 +86,9 @@ __device__ __forceinline__ void i8x4_to_f16_off(uint32_t w, uint32_t& lo, uint32
 }
 
 // Eight cache bytes -> eight f16 MFMA operand values: e4m3fn exactly, or int8
-// as 1152 + x.
+// as 1152 + x.  Only V operands take the offset form: on K it would add
+// 1152 * sum(q) to every logit, and the fp32 accumulator of S would round at
+// that magnitude instead of the logit's (K uses bytes8_to_f16).
 template <bool FP8>
 __device__ __forceinline__ half8_t bytes8_to_op(uint32_t w0, uint32_t w1) {
   if constexpr (FP8) {
@@ -1018,7 +1020,8 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
   constexpr int K_DMA = (KCH + 64 * NW - 1) / (64 * NW);
   constexpr int V_DMA = (VCH + 64 * NW - 1) / (64 * NW);
   constexpr int DMA_PER_TILE = K_DMA + V_DMA;     // exact for NW == 1
-  // int8 operands reach the MFMA as 1152 + x (see i8x4_to_f16_off)
+  // int8 V operands reach the MFMA as 1152 + x (see i8x4_to_f16_off); K
+  // operands are exact (bytes8_to_f16), so the query carries no logit bias
   constexpr float KV_OFF = FP8 ? 0.f : 1152.f;
   static_assert(DQK % 64 == 0 && DV % 16 == 0, "head dims");
   static_assert(KCH % 64 == 0 && VCH % 64 == 0, "tile chunks");
@@ -1156,7 +1159,7 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
     query_fetch<DQK, NT>(p, u, g, u.row0 + wave * ROWS_W, lane, qraw);
     query_finish_i8<DQK, NT>(p, u, g, u.row0 + wave * ROWS_W, lane, qraw, q);
   } else {
-    load_query<DQK, NT, HILO>(p, u, g, u.row0 + wave * ROWS_W, lane, KV_OFF, q);
+    load_query<DQK, NT, HILO>(p, u, g, u.row0 + wave * ROWS_W, lane, 0.f, q);
   }
   __shared__ uint32_t tree_lds[TREE ? NW * NT * 32 : 1];
   uint32_t* const tb = tree_lds + (TREE ? wave * NT * 32 : 0);
@@ -1205,7 +1208,7 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
         const int dst = key * FROW + kf_swz(hc, key) * 16;
         *(half8_t*)(f16t + VF16 + dst) = bytes8_to_op<FP8>((uint32_t)raw[0][i][0], (uint32_t)raw[0][i][1]);
         if constexpr (NM == 2)
-          *(half8_t*)(f16t + dst) = bytes8_to_op<FP8>((uint32_t)raw[1][i][0], (uint32_t)raw[1][i][1]);
+          *(half8_t*)(f16t + dst) = bytes8_to_f16<FP8>((uint32_t)raw[1][i][0], (uint32_t)raw[1][i][1]);
       }
       __syncthreads();   // f16 tiles complete (the next B0 orders their reuse)
 
@@ -1315,7 +1318,7 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
       for (int hk = 0; hk < 2; ++hk) {
         half8_t a[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) a[mt] = bytes8_to_op<FP8>(raw[mt][2 * hk], raw[mt][2 * hk + 1]);
+        for (int mt = 0; mt < 4; ++mt) a[mt] = bytes8_to_f16<FP8>(raw[mt][2 * hk], raw[mt][2 * hk + 1]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -1532,7 +1535,7 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
       for (int hk = 0; hk < 2; ++hk) {
         half8_t a[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) a[mt] = bytes8_to_op<FP8>(raw[mt][2 * hk], raw[mt][2 * hk + 1]);
+        for (int mt = 0; mt < 4; ++mt) a[mt] = bytes8_to_f16<FP8>(raw[mt][2 * hk], raw[mt][2 * hk + 1]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -1652,7 +1655,9 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
   constexpr int K_BLK = TK * KCPR / 64;           // 36 DMA instructions per tile
   constexpr int K_DMA = (K_BLK + NW - 1) / NW;    // per wave (waves below K_BLK % NW issue one more)
   constexpr int FROW = DV * 2;                    // 1024-byte f16 row
-  constexpr float KV_OFF = FP8 ? 0.f : 1152.f;
+  // K and V share the f16 tile, so int8 rows are converted exactly (an
+  // operand offset on K would put the fp32 logit accumulator at 1152 * sum(q))
+  constexpr float KV_OFF = 0.f;
   static_assert(K_BLK * 64 == TK * KCPR, "raw tile is whole DMA blocks");
   static_assert(K_BLK % NW == 0 || K_BLK % NW == NW / 2, "per-wave DMA count is K_DMA or K_DMA - 1");
 
@@ -1791,7 +1796,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
 #pragma unroll
       for (int i = 0; i < TK / NW; ++i)
         *(half8_t*)(kf + cv_wr[i % CV_WP] + (i / CV_WP) * (CV_WP * NW * FROW)) =
-            bytes8_to_op<FP8>((uint32_t)raw[i][0], (uint32_t)raw[i][1]);
+            bytes8_to_f16<FP8>((uint32_t)raw[i][0], (uint32_t)raw[i][1]);
     }
     __syncthreads();  // B1: f16 tile complete
 
@@ -1845,8 +1850,8 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
       constexpr int sp = SPF;   // rope dims 512..575, converted from the raw tile
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const half8_t a0 = bytes8_to_op<FP8>(rope_raw[mt][0], rope_raw[mt][1]);
-        const half8_t a1 = bytes8_to_op<FP8>(rope_raw[mt][2], rope_raw[mt][3]);
+        const half8_t a0 = bytes8_to_f16<FP8>(rope_raw[mt][0], rope_raw[mt][1]);
+        const half8_t a1 = bytes8_to_f16<FP8>(rope_raw[mt][2], rope_raw[mt][3]);
 #pragma unroll
         for (int nt = 0; nt < NTA; ++nt) {
           s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, q.hi[nt][2 * sp], s[mt][nt], 0, 0, 0);
