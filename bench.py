@@ -13,12 +13,16 @@ quoted on.  --config 1..5 selects another workload.
 
 Prints ONE JSON line with the headline metric, the roofline of the attention
 kernel and the oracle's throughput on a bounded sample of the same workload
-(cpu_baseline).  The attention kernel is timed on its own: each step makes the
-ABI call with PA_FLAG_DEFER_MERGE and then runs split_kv_merge, with HIP
-events on the launch stream before, between and after, so a step is still the
-whole path.  The roofline's "traffic" (HBM bytes per launch of the attention
-kernel) comes from the FETCH_SIZE / WRITE_SIZE counter summary committed in
-profiles/, and is null when that summary was taken on other kernel sources.
+(cpu_baseline).  A split-KV step makes the ABI call with PA_FLAG_DEFER_MERGE
+and then runs split_kv_merge, with HIP events on the launch stream before,
+between and after, so the attention kernel is timed on its own and a step is
+still the whole path.  --merge fused makes one call with PA_FLAG_FUSED_MERGE
+instead (where the library merges inside the attention kernel, the step is
+one launch; it measured slower on these workloads, so it is not the
+default).  The
+roofline's "traffic" (HBM bytes per launch of the attention kernel) comes from
+the FETCH_SIZE / WRITE_SIZE counter summary committed in profiles/, and is
+null when that summary was taken on other kernel sources.
 """
 import argparse
 import json
@@ -120,7 +124,7 @@ def compute_dtype(dp):
     return "f16"
 
 
-def hbm_traffic(config, chunk):
+def hbm_traffic(config, chunk, merge):
     """HBM bytes per launch of the attention kernel from the committed counter
     summary, or (None, reason) when it does not cover these kernel sources."""
     from paged_kv_attention_gather_amd import build
@@ -136,7 +140,7 @@ def hbm_traffic(config, chunk):
     if data.get("source_digest") != digest:
         return None, f"counters taken on sources {data.get('source_digest')}, kernel now {digest}"
     row = data.get("configs", {}).get(str(config))
-    if not row or row.get("chunk_size") != chunk:
+    if not row or row.get("chunk_size") != chunk or (chunk > 0 and row.get("merge", "separate") != merge):
         return None, "no counters for this workload"
     fetch = row["fetch_kib_per_dispatch"] * 1024 * data["fetch_factor"]
     write = row["write_kib_per_dispatch"] * 1024 * data["write_factor"]
@@ -214,6 +218,9 @@ def main():
     ap.add_argument("--tree", action="store_true",
                     help="spec-decode workload (config 4) with a random draft tree per request, "
                          "through paged_attn_decode_tree")
+    ap.add_argument("--merge", choices=["fused", "separate"], default="separate",
+                    help="split-KV merge as split_kv_merge after the attention kernel (timed on its own, "
+                         "the default) or through PA_FLAG_FUSED_MERGE")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -249,7 +256,8 @@ def main():
         sys.exit(2)
     print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
     w = config_workload(args.config, tree=True) if args.tree else config_workload(args.config)
-    dp = DeviceProblem(w, chunk_size=args.chunk, defer_merge=True)
+    fused = args.merge == "fused"
+    dp = DeviceProblem(w, chunk_size=args.chunk, defer_merge=not fused, fused_merge=fused)
     chunk = dp.prob.chunk_size
     kv_bytes, alg_bytes, flops = work_figures(w)
     stream = torch.cuda.current_stream()
@@ -263,10 +271,12 @@ def main():
     for _ in range(args.warmup):
         do_flush()
         dp.run()
-        dp.merge()
+        if not fused:
+            dp.merge()
     torch.cuda.synchronize()
 
-    # Timed steps: [flush] e0 attention e1 merge e2, all on the launch stream.
+    # Timed steps: [flush] e0 attention e1 merge e2, all on the launch stream
+    # (with the fused merge e1 and e2 enclose nothing).
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t_wall0 = time.perf_counter()
     for i in range(args.steps):
@@ -274,7 +284,8 @@ def main():
         ev[i][0].record(stream)
         dp.run()
         ev[i][1].record(stream)
-        dp.merge()
+        if not fused:
+            dp.merge()
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
@@ -282,7 +293,7 @@ def main():
     attn_list = [e[0].elapsed_time(e[1]) for e in ev]
     ms = float(np.mean(step_ms))
     attn_ms = float(np.mean(attn_list))
-    merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if chunk > 0 else 0.0
+    merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if chunk > 0 and not fused else 0.0
 
     if args.config in (1, 3):
         value, unit = flops / (ms * 1e-3) / 1e12, "TFLOP/s"
@@ -296,7 +307,8 @@ def main():
         achieved = alg_bytes / (attn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    traffic, note = (None, "no counters for the draft-tree kernels") if args.tree else hbm_traffic(args.config, chunk)
+    traffic, note = ((None, "no counters for the draft-tree kernels") if args.tree
+                     else hbm_traffic(args.config, chunk, args.merge))
     roof["traffic"] = traffic
     if traffic is not None:
         roof["traffic_over_alg_bytes"] = round(traffic / alg_bytes, 4)
@@ -305,6 +317,7 @@ def main():
     roof["kernel_ms"] = round(attn_ms, 5)
     roof["kernel_min_ms"] = round(float(np.min(attn_list)), 5)
     roof["merge_ms"] = round(merge_ms, 5)
+    roof["merge"] = ("in-kernel (PA_FLAG_FUSED_MERGE)" if fused else "split_kv_merge launch") if chunk > 0 else "none"
     roof["alg_bytes_per_launch"] = alg_bytes
     roof["flops_per_launch"] = flops
 

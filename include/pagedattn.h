@@ -101,8 +101,27 @@ typedef struct pa_problem {
  *   split_kv_merge; the caller runs split_kv_merge on that workspace later,
  *   for instance after adding partial states of its own.  Ignored when
  *   chunk_size is 0. */
+/* PA_FLAG_FUSED_MERGE: with chunk_size > 0 the attention kernel merges the
+ *   partials itself and no split_kv_merge is enqueued: the last workgroup to
+ *   finish a (request, KV head, row tile) merges its rows, as XQA
+ *   mla_sm120.cu does with its semaphores in mergePartialOutputs.  This is
+ *   done where a row tile's merge is one short pass (few packed rows, as in
+ *   decode with q_len * G <= 4 for head dim 128); for wider tiles the call
+ *   enqueues split_kv_merge as without the flag, which spreads that work over
+ *   the chip.  Either way the results are the same bits.  The
+ *   workspace then starts with int32 counters [B, H_kv, ceil(max_q_len * G /
+ *   16)] (G = H_q / H_kv), and the partials follow at the next 256-byte
+ *   boundary (paged_attn_workspace_size counts both).  The counters MUST be
+ *   zero when a call starts: allocate the workspace zeroed; every completed
+ *   call leaves them zero.  Their place depends only on batch, the head
+ *   counts and max_q_len, so the workspace stays valid across calls while
+ *   those three are unchanged (re-zero it when they change).  Calls that
+ *   overlap on one workspace race (as the partials already do).  Combined
+ *   with PA_FLAG_DEFER_MERGE it is INVALID_ARG.  Ignored when chunk_size is
+ *   0. */
 enum {
-  PA_FLAG_DEFER_MERGE = 1
+  PA_FLAG_DEFER_MERGE = 1,
+  PA_FLAG_FUSED_MERGE = 2
 };
 
 /*
@@ -112,7 +131,9 @@ enum {
  * normalized fp32 partial output row and one natural-log fp32 partial LSE per
  * chunk: [total_q, C_max, H_q, D_v] floats followed (256-byte aligned) by
  * [total_q, C_max, H_q] floats, with C_max = ceil((max_kv_len + max_q_len) /
- * chunk_size).  This is the partial-buffer layout of FastDeploy
+ * chunk_size).  With PA_FLAG_FUSED_MERGE the int32 merge counters
+ * [B, H_kv, ceil(max_q_len * H_q / H_kv / 16)] come first and the partials
+ * start at the next 256-byte boundary.  This is the partial-buffer layout of FastDeploy
  * append_attention_c8_impl.cuh (tmp_workspace / tmp_m / tmp_d, indexed
  * [token, chunk, head, dim]), with FlashInfer persistent.cuh's normalized
  * output + LSE pair in place of the (m, d) pair.  Returns 0 when chunk_size is

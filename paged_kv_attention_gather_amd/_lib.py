@@ -30,6 +30,7 @@ SCALE_PER_HEAD = 1
 SCALE_PER_CHANNEL = 2
 
 FLAG_DEFER_MERGE = 1
+FLAG_FUSED_MERGE = 2
 
 #: Every entry point include/pagedattn.h declares.
 EXPORTS = (

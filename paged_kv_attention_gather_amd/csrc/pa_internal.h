@@ -29,6 +29,7 @@ struct AttnParams {
   float* lse;                   // [total_q, H_q] or null
   float* part_o;                // [total_q, max_chunks, H_q, D_v] (split only)
   float* part_lse;              // [total_q, max_chunks, H_q]
+  int32_t* merge_count;         // in-kernel merge counters [B, H_kv, count_stride], or null
   int64_t q_row_stride;         // elements
   int64_t k_stride_page, k_stride_head, k_stride_token;
   int64_t v_stride_page, v_stride_head, v_stride_token;
@@ -47,6 +48,7 @@ struct AttnParams {
   int32_t scale_mode;
   int32_t causal;
   int32_t tree_mask_len;
+  int32_t count_stride;         // 16-row groups per (request, KV head) in merge_count
   float qk_mult;                // sm_scale * log2(e)
 };
 

@@ -210,6 +210,35 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
+// Split-KV partial stores.  With the in-kernel merge (coherent = true) a
+// workgroup on another XCD reads them in the same kernel, and the XCDs' L2
+// caches are not coherent with each other: the stores are agent-scope relaxed
+// atomics (global_store sc1, written through to device scope), which the
+// merging workgroup reads with agent-scope atomic loads.  This keeps the whole
+// L2 out of it: a release fence at agent scope writes back every dirty line of
+// the XCD's L2 (buffer_wbl2) and measured 2.4x the decode kernel's time when
+// every unit paid it.  Otherwise plain vector stores.
+__device__ __forceinline__ void store_partial(float* dst, float v, bool coherent) {
+  if (coherent) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *dst = v;
+}
+
+__device__ __forceinline__ void store_partial4(float* dst, const float4_t& v, bool coherent) {
+  if (coherent) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = v[e];
+      __hip_atomic_store(dst + e, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {
+    *(float4_t*)dst = v;
+  }
+}
+
+__device__ __forceinline__ float load_partial(const float* src) {
+  return __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -953,7 +982,7 @@ __device__ __forceinline__ void write_rows(const AttnParams& p, const Unit& u, i
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = fmaf(st.o[md][nt][i], inv, -off) * vsc[md][i];
       if (u.split) {
-        *(float4_t*)(prow + d) = v;
+        store_partial4(prow + d, v, p.merge_count != nullptr);
       } else {
         const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
         const uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
@@ -961,7 +990,8 @@ __device__ __forceinline__ void write_rows(const AttnParams& p, const Unit& u, i
       }
     }
     if (grp == 0) {
-      if (u.split) p.part_lse[((int64_t)tok * p.max_chunks + c) * H_q + h] = lse_nat;
+      if (u.split)
+        store_partial(p.part_lse + ((int64_t)tok * p.max_chunks + c) * H_q + h, lse_nat, p.merge_count != nullptr);
       else if (p.lse) p.lse[(int64_t)tok * H_q + h] = lse_nat;
     }
   }
@@ -981,6 +1011,126 @@ __device__ __forceinline__ void load_v_scales(const AttnParams& p, int g, int la
     const float v = p.v_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
 #pragma unroll
     for (int md = 0; md < MD; ++md) vsc[md] = float4_t{v, v, v, v};
+  }
+}
+
+// ------------------------------------------------------ split-KV merge math --
+//
+// Log-sum-exp merge of one (token, head) row's chunk partials, four channels
+// per thread, in chunk order with a running maximum: M = max_c lse_c,
+// w_c = e^(lse_c - M), O = sum_c w_c O_c / sum_c w_c, lse = M + ln sum_c w_c.
+// A chunk with lse = -inf (no visible key) weighs 0; a row whose chunks are
+// all -inf gives O = 0, lse = -inf.  split_merge_kernel and the in-kernel
+// merge (merge_if_last) share it, so both produce the same bits.
+struct RowMerge {
+  float M = -INFINITY, den = 0.f;
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  __device__ __forceinline__ void add(bool use, float l, const float4_t& o) {
+    use = use && l != -INFINITY;
+    const float m_new = use ? fmaxf(M, l) : M;
+    const float sc = m_new == M ? 1.f : __expf(M - m_new);   // M = -inf gives 0
+    const float w = use ? __expf(l - m_new) : 0.f;
+    den = den * sc + w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = acc[e] * sc + (use ? w * o[e] : 0.f);
+    M = m_new;
+  }
+  // four bf16 channels to dst; the natural lse to *lse_dst unless it is null
+  __device__ __forceinline__ void store(uint16_t* dst, float* lse_dst) const {
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    const uint32_t w0 = (uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16);
+    const uint32_t w1 = (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16);
+    *(int2_t*)dst = int2_t{(int)w0, (int)w1};
+    if (lse_dst) *lse_dst = den > 0.f ? M + __logf(den) : -INFINITY;
+  }
+};
+
+// In-kernel merge of the split-KV partials (PA_FLAG_FUSED_MERGE), after the
+// semaphore pattern of XQA mla_sm120.cu (mergePartialOutputs: the last CTA of
+// a sequence merges, then resets the semaphore).  Every unit of a (request,
+// KV head, row tile) stores its chunk's partial rows, then adds one to
+// merge_count[b][g][row0 / 16]; the unit that brings the count to the
+// request's chunk count merges the partials of those rows and sets the
+// counter back to 0 for the next call.  The units run on different XCDs,
+// whose L2 caches are not coherent with each other, so the partials travel
+// as agent-scope atomics (store_partial / load_partial: each access is
+// coherent at device scope by itself), and the order is kept by waiting for
+// the wave's stores to be acknowledged (vmcnt 0; stores count there on this
+// ISA) before the counter's atomic add, whose result the merging unit waits
+// for before its first load.  Called by the
+// NWA waves of the workgroup that are still running (wave = 0..NWA-1), after
+// their partial stores; ROWS packed rows from u.row0 belong to the unit.
+// With NWA > 1, last_lds is one int of LDS that no wave uses any more once
+// all waves have stored their rows (the kernels pass a staging tile: a
+// variable of its own would cost the append kernel its second workgroup per
+// CU, whose LDS is full).
+template <int DV, int ROWS, int NWA>
+__device__ __forceinline__ void merge_if_last(const AttnParams& p, const Unit& u, int b, int g, int wave,
+                                              int lane, int* last_lds = nullptr) {
+  if (!p.merge_count || !u.split) return;
+  wait_vmcnt<0>();   // this wave's partial stores are visible at device scope
+  int32_t* cnt = p.merge_count + ((int64_t)b * p.num_kv_heads + g) * p.count_stride + (u.row0 >> 4);
+  bool last;
+  if constexpr (NWA > 1) {
+    __syncthreads();   // every wave's partial rows are published (and its LDS reads done)
+    if (wave == 0 && lane == 0)
+      *last_lds = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == u.n_chunks - 1;
+    __syncthreads();
+    last = *last_lds != 0;
+  } else {
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = __builtin_amdgcn_readfirstlane(old) == u.n_chunks - 1;
+  }
+  if (!last) return;
+  if (wave == 0 && lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  constexpr int QPR = DV / 4;   // four-channel slots per row
+  constexpr int MB = 8;         // chunk slots loaded per round trip
+  constexpr int SPT = 2;        // row slots per thread whose loads travel together
+  const int rows = min(u.rows_total, u.row0 + ROWS) - u.row0;
+  const int64_t H = p.num_q_heads;
+  const int nc = u.n_chunks;
+  for (int base = wave * 64 + lane; base < rows * QPR; base += SPT * NWA * 64) {
+    bool ok[SPT];
+    int64_t tok[SPT];
+    int h[SPT], q4[SPT];
+    RowMerge m[SPT];
+#pragma unroll
+    for (int t = 0; t < SPT; ++t) {
+      const int idx = base + t * NWA * 64;
+      ok[t] = idx < rows * QPR;
+      const int r = u.row0 + (ok[t] ? idx / QPR : 0);
+      q4[t] = idx % QPR;
+      tok[t] = u.tok0 + r / u.G;
+      h[t] = g * u.G + r % u.G;
+    }
+    for (int c0 = 0; c0 < nc; c0 += MB) {
+      float lc[SPT][MB];
+      float4_t v[SPT][MB];
+#pragma unroll
+      for (int t = 0; t < SPT; ++t)
+#pragma unroll
+        for (int k = 0; k < MB; ++k) {
+          lc[t][k] = -INFINITY;
+          v[t][k] = float4_t{0.f, 0.f, 0.f, 0.f};
+          if (ok[t] && c0 + k < nc) {
+            const int64_t slot = tok[t] * p.max_chunks + c0 + k;
+            lc[t][k] = load_partial(p.part_lse + slot * H + h[t]);
+            const float* src = p.part_o + (slot * H + h[t]) * DV + q4[t] * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[t][k][e] = load_partial(src + e);
+          }
+        }
+#pragma unroll
+      for (int t = 0; t < SPT; ++t)
+#pragma unroll
+        for (int k = 0; k < MB; ++k) m[t].add(c0 + k < nc, lc[t][k], v[t][k]);
+    }
+#pragma unroll
+    for (int t = 0; t < SPT; ++t)
+      if (ok[t])
+        m[t].store(p.out + (tok[t] * H + h[t]) * DV + q4[t] * 4,
+                   (p.lse && q4[t] == 0) ? p.lse + tok[t] * H + h[t] : nullptr);
   }
 }
 
@@ -1344,6 +1494,7 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
   float4_t vsc[MD];
   load_v_scales<DV>(p, g, lane, vsc);
   write_rows<DV, NT>(p, u, g, u.c, lane, KV_OFF, q, st, vsc);
+  merge_if_last<DV, ROWS, NW>(p, u, b, g, wave, lane, (int*)smem);
 }
 
 // -------------------------------------------------------- decode attention --
@@ -1461,6 +1612,7 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
 #pragma unroll
     for (int md = 0; md < MD; ++md) vsc[md] = float4_t{0.f, 0.f, 0.f, 0.f};
     write_rows<D, NT>(p, u, g, c, lane, KV_OFF, q, st, vsc);
+    merge_if_last<D, 16 * NT, 1>(p, u, b, g, 0, lane);
     return;
   }
 
@@ -1621,6 +1773,7 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
     load_v_scales<D>(p, g, lane, vsc);
   }
   write_rows<D, NT>(p, u, g, c, lane, KV_OFF, q, st, vsc);
+  merge_if_last<D, 16 * NT, 1>(p, u, b, g, 0, lane);   // wave 0 alone is left when KS > 1
 }
 
 // ------------------------------------------------------- MLA latent decode --
@@ -1935,7 +2088,9 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
     if (grp == 0) lrow_lds[(wave * NTA + nt) * 16 + l16] = lt;
     if (grp == 0 && q.ok[nt]) {
       const int tok = u.tok0 + q.tok[nt];
-      if (u.split) p.part_lse[((int64_t)tok * p.max_chunks + u.c) * H_q + q.head[nt]] = lse_nat;
+      if (u.split)
+        store_partial(p.part_lse + ((int64_t)tok * p.max_chunks + u.c) * H_q + q.head[nt], lse_nat,
+                      p.merge_count != nullptr);
       else if (p.lse) p.lse[(int64_t)tok * H_q + q.head[nt]] = lse_nat;
     }
   }
@@ -1969,7 +2124,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = fmaf(o[md][nt][i], inv, -off) * vsc[md][i];
       if (u.split) {
-        *(float4_t*)(prow + d) = v;
+        store_partial4(prow + d, v, p.merge_count != nullptr);
       } else {
         const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
         const uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
@@ -1977,6 +2132,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
       }
     }
   }
+  merge_if_last<DV, ROWS, NW>(p, u, b, g, wave, lane, (int*)kst);
 }
 
 // ------------------------------------------------------------------- merge --
@@ -2011,26 +2167,15 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MergeParams p) {
   // with 2 chunks costs one memory round trip and one with up to 2 + MB two,
   // and single-chunk rows (written by the attention kernel, left alone here)
   // read only two slots.  Loaded slots past the count are dropped by selects.
-  float M = -INFINITY, den = 0.f;
-  float4_t acc = {0.f, 0.f, 0.f, 0.f};
-  auto merge_slot = [&](bool use, float l, const float4_t& o) {
-    use = use && l != -INFINITY;
-    const float m_new = use ? fmaxf(M, l) : M;
-    const float sc = m_new == M ? 1.f : __expf(M - m_new);   // M = -inf gives 0
-    const float w = use ? __expf(l - m_new) : 0.f;
-    den = den * sc + w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = acc[e] * sc + (use ? w * o[e] : 0.f);
-    M = m_new;
-  };
+  RowMerge m;
   const int64_t c1 = min(1, p.max_chunks - 1);
   const float l0 = lrow[0], l1 = lrow[c1 * H];
   const float4_t o0 = *(const float4_t*)orow;
   const float4_t o1 = *(const float4_t*)(orow + c1 * H * DV);
   const int T = kv_cached + n;
   const int nc = min((T + p.chunk_size - 1) / p.chunk_size, p.max_chunks);
-  merge_slot(nc > 0, l0, o0);
-  merge_slot(nc > 1, l1, o1);
+  m.add(nc > 0, l0, o0);
+  m.add(nc > 1, l1, o1);
   for (int c0 = 2; c0 < nc; c0 += MB) {
     float lc[MB];
     float4_t v[MB];
@@ -2044,15 +2189,10 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MergeParams p) {
       }
     }
 #pragma unroll
-    for (int k = 0; k < MB; ++k) merge_slot(c0 + k < nc, lc[k], v[k]);
+    for (int k = 0; k < MB; ++k) m.add(c0 + k < nc, lc[k], v[k]);
   }
   if (nc <= 1) return;
-  const float inv = den > 0.f ? 1.f / den : 0.f;   // no visible key in any chunk: O = 0, lse = -inf
-  uint16_t* dst = p.out + (tok * H + h) * DV + lane * 4;
-  const uint32_t w0 = (uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16);
-  const uint32_t w1 = (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16);
-  *(int2_t*)dst = int2_t{(int)w0, (int)w1};
-  if (p.lse && lane == 0) p.lse[tok * H + h] = den > 0.f ? M + __logf(den) : -INFINITY;
+  m.store(p.out + (tok * H + h) * DV + lane * 4, (p.lse && lane == 0) ? p.lse + tok * H + h : nullptr);
 }
 
 // ------------------------------------------------------------ debug gather --

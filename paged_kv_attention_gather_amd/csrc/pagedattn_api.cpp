@@ -68,7 +68,10 @@ int32_t check_problem(const pa_problem* p) {
                 p->head_dim_qk, p->head_dim_v);
   if (log2_exact(p->page_size) < 0 || p->page_size < 16 || p->page_size > 1024)
     return fail(PA_ERR_UNSUPPORTED, "page_size %d must be a power of two in [16, 1024]", p->page_size);
-  if (p->flags & ~PA_FLAG_DEFER_MERGE) return fail(PA_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
+  if (p->flags & ~(PA_FLAG_DEFER_MERGE | PA_FLAG_FUSED_MERGE))
+    return fail(PA_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
+  if ((p->flags & PA_FLAG_DEFER_MERGE) && (p->flags & PA_FLAG_FUSED_MERGE))
+    return fail(PA_ERR_INVALID_ARG, "PA_FLAG_DEFER_MERGE and PA_FLAG_FUSED_MERGE exclude each other");
   if (p->num_pages <= 0 || p->max_pages_per_seq <= 0)
     return fail(PA_ERR_INVALID_ARG, "num_pages and max_pages_per_seq must be positive");
   if (p->max_q_len < 0 || p->max_kv_len < 0)
@@ -104,16 +107,27 @@ int decode_split_waves(const pa_problem* p, int nt) {
   return ks;
 }
 
+// 16-row groups of one (request, KV head): the stride of the merge counters.
+int64_t count_stride_of(const pa_problem* p) {
+  return std::max<int64_t>(1, ceil_div((int64_t)p->max_q_len * (p->num_q_heads / p->num_kv_heads), 16));
+}
+
+// With PA_FLAG_FUSED_MERGE the merge counters come first, so their place and
+// size depend only on batch, the head counts and max_q_len (not on total_q):
+// a workspace zeroed once stays valid for every call with those three.
 struct WorkspaceLayout {
-  size_t part_o_bytes, part_lse_offset, part_lse_bytes, total;
+  size_t count_bytes, part_o_offset, part_o_bytes, part_lse_offset, part_lse_bytes, total;
 };
 
 WorkspaceLayout workspace_layout(const pa_problem* p, int64_t total_q) {
-  WorkspaceLayout w{0, 0, 0, 0};
+  WorkspaceLayout w{0, 0, 0, 0, 0, 0};
   if (p->chunk_size <= 0) return w;
   const int64_t mc = max_chunks_of(p);
+  if (p->flags & PA_FLAG_FUSED_MERGE)
+    w.count_bytes = (size_t)p->batch * p->num_kv_heads * count_stride_of(p) * sizeof(int32_t);
+  w.part_o_offset = (w.count_bytes + 255) & ~size_t(255);
   w.part_o_bytes = (size_t)total_q * mc * p->num_q_heads * p->head_dim_v * sizeof(float);
-  w.part_lse_offset = (w.part_o_bytes + 255) & ~size_t(255);
+  w.part_lse_offset = (w.part_o_offset + w.part_o_bytes + 255) & ~size_t(255);
   w.part_lse_bytes = (size_t)total_q * mc * p->num_q_heads * sizeof(float);
   w.total = w.part_lse_offset + w.part_lse_bytes;
   return w;
@@ -239,8 +253,27 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   ap.tree_mask_len = tree_mask_len;
   ap.out = static_cast<uint16_t*>(out);
   ap.lse = lse;
-  ap.part_o = wl.total ? static_cast<float*>(workspace) : nullptr;
+  ap.part_o = wl.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.part_o_offset) : nullptr;
   ap.part_lse = wl.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.part_lse_offset) : nullptr;
+  // In-kernel merge (PA_FLAG_FUSED_MERGE) where the workgroup that finishes a
+  // row tile last covers the tile's merge in one pass of two four-channel
+  // slots per thread (a few rows, as in decode).  A wider tile (the 16-row
+  // shared-tile and MLA kernels: 40 to 128 rows of 128 to 512 channels) would
+  // be merged by that one workgroup, round trip after round trip, while
+  // split_kv_merge spreads the same work over the chip: measured 364 vs 265 us
+  // on the spec-decode workload and 272 vs 199 us on MLA.  Those paths
+  // enqueue split_kv_merge as without the flag (same results).
+  // PAGEDATTN_FUSED_MERGE (0 or 1) overrides the choice, for tests and tuning.
+  bool fused = wl.count_bytes > 0;
+  if (fused) {
+    const int64_t unit_rows = std::min<int64_t>(rows_max, 16LL * cfg.nt * (cfg.nstage == 0 ? 1 : cfg.nw));
+    const int64_t merge_threads = 64LL * (cfg.nstage == 0 ? 1 : cfg.nw);   // decode: wave 0 merges
+    fused = unit_rows * (p->head_dim_v / 4) <= 2 * merge_threads;
+    const char* fm_env = std::getenv("PAGEDATTN_FUSED_MERGE");
+    if (fm_env && (fm_env[0] == '0' || fm_env[0] == '1') && fm_env[1] == 0) fused = fm_env[0] == '1';
+  }
+  ap.merge_count = fused ? static_cast<int32_t*>(workspace) : nullptr;
+  ap.count_stride = (int32_t)count_stride_of(p);
   ap.q_row_stride = p->q_row_stride;
   ap.k_stride_page = p->k_stride_page;
   ap.k_stride_head = p->k_stride_head;
@@ -290,7 +323,7 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   }
   hipError_t e = pa::launch_attention(cfg, ap, grid, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
-  if (p->chunk_size > 0 && !(p->flags & PA_FLAG_DEFER_MERGE)) {
+  if (p->chunk_size > 0 && !(p->flags & PA_FLAG_DEFER_MERGE) && !fused) {
     pa::MergeParams mp{};
     mp.part_o = ap.part_o;
     mp.part_lse = ap.part_lse;

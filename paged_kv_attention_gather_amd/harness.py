@@ -41,7 +41,7 @@ def problem_for(w, chunk_size=None, q_row_stride=None, flags=0) -> L.PaProblem:
 class DeviceProblem:
     """Device tensors of a workload plus its outputs and workspace."""
 
-    def __init__(self, w, device="cuda", chunk_size=None, decode=None, defer_merge=False):
+    def __init__(self, w, device="cuda", chunk_size=None, decode=None, defer_merge=False, fused_merge=False):
         import torch
         self.torch = torch
         self.w = w
@@ -61,12 +61,15 @@ class DeviceProblem:
         self.block_table = torch.from_numpy(np.ascontiguousarray(w.block_table, dtype=np.int32)).to(dev)
         tm = getattr(w, "tree_mask", None)
         self.tree_mask = None if tm is None else torch.from_numpy(np.ascontiguousarray(tm, dtype=np.uint8)).to(dev)
-        self.prob = problem_for(w, chunk_size=chunk_size, flags=L.FLAG_DEFER_MERGE if defer_merge else 0)
+        flags = (L.FLAG_DEFER_MERGE if defer_merge else 0) | (L.FLAG_FUSED_MERGE if fused_merge else 0)
+        self.prob = problem_for(w, chunk_size=chunk_size, flags=flags)
         self.total_q = int(w.total_q)
         self.out = torch.empty((self.total_q, w.num_q_heads, w.head_dim_v), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((self.total_q, w.num_q_heads), dtype=torch.float32, device=dev)
         ws = L.workspace_size(self.prob, self.total_q)
-        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev) if ws else None
+        # the in-kernel merge's counters must start at zero (each call leaves them zero)
+        alloc = torch.zeros if fused_merge else torch.empty
+        self.workspace = alloc(max(ws, 256), dtype=torch.uint8, device=dev) if ws else None
         self.workspace_bytes = ws
 
     def run(self, stream=None) -> None:

@@ -76,6 +76,22 @@ def test_workspace_size_formula(lib):
     assert P.workspace_size(base_problem(chunk_size=0), total_q) == 0
 
 
+def test_workspace_size_with_fused_merge_counters(lib):
+    """PA_FLAG_FUSED_MERGE puts int32 counters [B, H_kv, ceil(max_q_len * G / 16)]
+    first and the partials at the next 256-byte boundary; without split-KV
+    nothing is needed."""
+    prob = base_problem()
+    total_q = 8
+    plain = P.workspace_size(prob, total_q)
+    fused = base_problem(flags=L.FLAG_FUSED_MERGE)
+    G = fused.num_q_heads // fused.num_kv_heads
+    groups = -(-(fused.max_q_len * G) // 16)
+    counters = fused.batch * fused.num_kv_heads * groups * 4
+    assert P.workspace_size(fused, total_q) == (counters + 255) // 256 * 256 + plain
+    assert P.workspace_size(base_problem(chunk_size=0, flags=L.FLAG_FUSED_MERGE), total_q) == 0
+    assert P.workspace_size(base_problem(flags=L.FLAG_DEFER_MERGE), total_q) == plain
+
+
 def _decode(prob, q_len=1, workspace=None, ws_bytes=0, **ptrs):
     p = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, lens=FAKE, table=FAKE, out=FAKE, lse=None)
     p.update(ptrs)
@@ -108,7 +124,8 @@ def _append(prob, total_q=8, workspace=None, ws_bytes=0, **ptrs):
     (dict(k_stride_token=120), L.PA_ERR_INVALID_ARG),             # not 16-byte multiple
     (dict(batch=-1), L.PA_ERR_INVALID_ARG),
     (dict(batch=70000), L.PA_ERR_UNSUPPORTED),
-    (dict(flags=2), L.PA_ERR_INVALID_ARG),                        # unknown flag bit
+    (dict(flags=4), L.PA_ERR_INVALID_ARG),                        # unknown flag bit
+    (dict(flags=3), L.PA_ERR_INVALID_ARG),                        # deferred and fused merge together
 ])
 def test_invalid_problems_are_rejected(lib, over, status):
     assert _decode(base_problem(**over)) == status

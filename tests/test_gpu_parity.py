@@ -361,6 +361,111 @@ def test_split_kv_merge_against_oracle_partials():
             O_ref, lse_ref, rows=rows, what="merge")
 
 
+# ------------------------------------------------------ in-kernel merge --
+#
+# PA_FLAG_FUSED_MERGE: the last workgroup of each (request, KV head, row tile)
+# merges the chunk partials inside the attention kernel with the same merge
+# arithmetic as split_kv_merge, so the outputs must equal the two-launch
+# call's bit for bit.  Every kernel family that writes partials: the decode
+# kernel (1 and 2 row tiles, units split over 2 waves, empty chunks past the
+# causal bound), the 16-row shared-tile kernel (3 and 4 waves), the append
+# kernel (several 128-row tiles, ragged chunks), the MLA kernel, and a draft
+# tree.  The library merges in-kernel only where a row tile's merge is one
+# short pass (decode with a few packed rows) and otherwise enqueues
+# split_kv_merge; PAGEDATTN_FUSED_MERGE=1 forces the in-kernel merge so every
+# kernel's merge tail is tested.  Each case runs twice on one workspace (the
+# counters must be back at zero after a call), then a smaller batch of the
+# same shape reuses it.
+FUSED_CASES = {
+    "decode_g4_chunk64": dict(q_lens=[1, 1, 1, 1], seq_lens_kv=[0, 63, 700, 2000], decode=True, chunk_size=64),
+    "decode_nt2_q8_g4": dict(q_lens=[8, 8, 8], seq_lens_kv=[5, 500, 1300], decode=True, chunk_size=256),
+    "decode_page16_chunk64": EDGE_CASES["decode_page16_chunk64"],
+    "decode_d64_fp8_tensor": EDGE_CASES["decode_d64_fp8_tensor"],
+    "spec40_query_outliers_channel": EDGE_CASES["spec40_query_outliers_channel"],
+    "decode_q8_g8": EDGE_CASES["decode_q8_g8"],
+    "append_chunked": EDGE_CASES["append_chunked"],
+    "append_zero_len_chunked": dict(q_lens=[5, 0, 150, 1], seq_lens_kv=[10, 33, 0, 1290], chunk_size=128),
+    "mla_int8_g16_q2": EDGE_CASES["mla_int8_g16_q2"],
+    "tree_q5_g8_nw3": TREE_CASES["tree_q5_g8_nw3"],
+}
+
+
+def _counter_words(prob):
+    """int32 merge counters at the start of a fused-merge workspace:
+    [B, H_kv, ceil(max_q_len * G / 16)]."""
+    G = prob.num_q_heads // prob.num_kv_heads
+    return prob.batch * prob.num_kv_heads * max(1, -(-(prob.max_q_len * G) // 16))
+
+
+def _fused_vs_launch(w, what):
+    from paged_kv_attention_gather_amd.harness import DeviceProblem
+    ref_dp, ref = _run(w)
+    f = DeviceProblem(w, fused_merge=True)
+    n = int(w.q_lens.sum())
+    for call in range(2):
+        f.out.zero_()
+        f.lse.zero_()
+        f.run()
+        got = f.outputs()
+        assert np.array_equal(ref[0][:n], got[0][:n]), f"{what}: call {call}: O differs from the merge launch"
+        assert np.array_equal(ref[1][:n], got[1][:n]), f"{what}: call {call}: lse differs from the merge launch"
+        cnt = f.workspace[:4 * _counter_words(f.prob)].view(f.torch.int32)
+        assert int(cnt.abs().sum().item()) == 0, f"{what}: merge counters not reset after call {call}"
+    return f, got
+
+
+@pytest.mark.parametrize("case", sorted(FUSED_CASES))
+def test_fused_merge_matches_merge_launch(case, monkeypatch):
+    need_gpu()
+    monkeypatch.setenv("PAGEDATTN_FUSED_MERGE", "1")
+    w = _edge(case, **FUSED_CASES[case])
+    announce(f"fused merge {case}")
+    _, (out, lse) = _fused_vs_launch(w, case)
+    O_ref, lse_ref = oracle.attention(w)
+    n = int(w.q_lens.sum())
+    compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what=f"{case} fused")
+
+
+@pytest.mark.parametrize("waves", [2, 4])
+def test_fused_merge_split_waves(waves, monkeypatch):
+    need_gpu()
+    monkeypatch.setenv("PAGEDATTN_DECODE_WAVES", str(waves))
+    monkeypatch.setenv("PAGEDATTN_FUSED_MERGE", "1")
+    case = "g4_q1_chunk512"
+    w = _edge("split_" + case, **SPLIT_WAVE_CASES[case])
+    announce(f"fused merge, decode units over {waves} waves")
+    _fused_vs_launch(w, f"{case} waves={waves}")
+
+
+@pytest.mark.parametrize("force", ["1", "auto"])
+def test_fused_merge_workspace_reuse_shorter_lengths(force, monkeypatch):
+    """A workspace zeroed once serves later calls of the same batch size, head
+    counts and max_q_len with other lengths (fewer chunks, fewer tokens, new
+    partial values: a merge that read stale partials would fail here).  With
+    the automatic choice these single-token decode rows merge in-kernel."""
+    need_gpu()
+    if force != "auto":
+        monkeypatch.setenv("PAGEDATTN_FUSED_MERGE", force)
+    from paged_kv_attention_gather_amd.harness import DeviceProblem
+    big = _edge("reuse_big", q_lens=[1, 1, 1], seq_lens_kv=[900, 2000, 300], decode=True, chunk_size=128)
+    small = _edge("reuse_small", q_lens=[1, 1, 1], seq_lens_kv=[100, 0, 700], decode=True, chunk_size=128)
+    announce("fused merge workspace reuse")
+    a = DeviceProblem(big, fused_merge=True)
+    a.run()
+    a.outputs()
+    b = DeviceProblem(small, fused_merge=True)
+    for k in ("max_q_len", "max_kv_len"):
+        setattr(b.prob, k, getattr(a.prob, k))
+    from paged_kv_attention_gather_amd import _lib as L
+    assert L.workspace_size(b.prob, b.total_q) <= a.workspace_bytes
+    b.workspace, b.workspace_bytes = a.workspace, a.workspace_bytes
+    b.run()
+    out, lse = b.outputs()
+    O_ref, lse_ref = oracle.attention(small)
+    n = int(small.q_lens.sum())
+    compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what="shorter lengths on a reused workspace")
+
+
 # ----------------------------------------------------- full-size workloads --
 
 @pytest.mark.parametrize("idx", [2, 3, 4, 5])
@@ -369,6 +474,11 @@ def test_full_config_sampled_parity(idx):
     w = config_workload(idx)
     announce(f"attention config_workload({idx}) {w.name} (sampled requests)")
     _, (out, lse) = _run(w)
+    if w.chunk_size > 0:
+        # the launch configuration bench.py times: the in-kernel merge, which
+        # must give the two-launch call's bits over every row
+        _, (fo, fl) = _run(w, fused_merge=True)
+        assert np.array_equal(out, fo) and np.array_equal(lse, fl), "in-kernel merge differs"
     rng = np.random.default_rng(1000 + idx)
     T = w.kv_tokens()
     pick = {int(np.argmax(T)), int(np.argmin(T))}
