@@ -124,7 +124,7 @@ def compute_dtype(dp):
     return "f16"
 
 
-def hbm_traffic(config, chunk, merge):
+def hbm_traffic(config, chunk, merge, balanced=False):
     """HBM bytes per launch of the attention kernel from the committed counter
     summary, or (None, reason) when it does not cover these kernel sources."""
     from paged_kv_attention_gather_amd import build
@@ -140,7 +140,8 @@ def hbm_traffic(config, chunk, merge):
     if data.get("source_digest") != digest:
         return None, f"counters taken on sources {data.get('source_digest')}, kernel now {digest}"
     row = data.get("configs", {}).get(str(config))
-    if not row or row.get("chunk_size") != chunk or (chunk > 0 and row.get("merge", "separate") != merge):
+    if (not row or row.get("chunk_size") != chunk or (chunk > 0 and row.get("merge", "separate") != merge)
+            or bool(row.get("balanced", False)) != balanced):
         return None, "no counters for this workload"
     fetch = row["fetch_kib_per_dispatch"] * 1024 * data["fetch_factor"]
     write = row["write_kib_per_dispatch"] * 1024 * data["write_factor"]
@@ -221,6 +222,9 @@ def main():
     ap.add_argument("--merge", choices=["fused", "separate"], default="separate",
                     help="split-KV merge as split_kv_merge after the attention kernel (timed on its own, "
                          "the default) or through PA_FLAG_FUSED_MERGE")
+    ap.add_argument("--balanced", action="store_true",
+                    help="PA_FLAG_BALANCED_SPLIT: KV items sized on the device to fill one round "
+                         "(chunk_size, or --chunk, is then the shortest item)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -257,7 +261,12 @@ def main():
     print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
     w = config_workload(args.config, tree=True) if args.tree else config_workload(args.config)
     fused = args.merge == "fused"
-    dp = DeviceProblem(w, chunk_size=args.chunk, defer_merge=not fused, fused_merge=fused)
+    if args.balanced and not fused:
+        # a balanced split's chunks are not split_kv_merge's: the call merges
+        # itself, so the step is timed whole (attention kernel + merge)
+        print("[bench] --balanced: the merge runs inside the ABI call", file=sys.stderr, flush=True)
+    dp = DeviceProblem(w, chunk_size=args.chunk, defer_merge=not fused and not args.balanced,
+                       fused_merge=fused, balanced=args.balanced)
     chunk = dp.prob.chunk_size
     kv_bytes, alg_bytes, flops = work_figures(w)
     stream = torch.cuda.current_stream()
@@ -268,10 +277,11 @@ def main():
             flush.max()  # read-only pass over 1 GiB
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    separate = not fused and not args.balanced   # merge launched here, timed apart
     for _ in range(args.warmup):
         do_flush()
         dp.run()
-        if not fused:
+        if separate:
             dp.merge()
     torch.cuda.synchronize()
 
@@ -284,7 +294,7 @@ def main():
         ev[i][0].record(stream)
         dp.run()
         ev[i][1].record(stream)
-        if not fused:
+        if separate:
             dp.merge()
         ev[i][2].record(stream)
     torch.cuda.synchronize()
@@ -293,7 +303,7 @@ def main():
     attn_list = [e[0].elapsed_time(e[1]) for e in ev]
     ms = float(np.mean(step_ms))
     attn_ms = float(np.mean(attn_list))
-    merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if chunk > 0 and not fused else 0.0
+    merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if chunk > 0 and separate else 0.0
 
     if args.config in (1, 3):
         value, unit = flops / (ms * 1e-3) / 1e12, "TFLOP/s"
@@ -308,7 +318,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
     traffic, note = ((None, "no counters for the draft-tree kernels") if args.tree
-                     else hbm_traffic(args.config, chunk, args.merge))
+                     else hbm_traffic(args.config, chunk, args.merge, args.balanced))
     roof["traffic"] = traffic
     if traffic is not None:
         roof["traffic_over_alg_bytes"] = round(traffic / alg_bytes, 4)
@@ -317,7 +327,11 @@ def main():
     roof["kernel_ms"] = round(attn_ms, 5)
     roof["kernel_min_ms"] = round(float(np.min(attn_list)), 5)
     roof["merge_ms"] = round(merge_ms, 5)
-    roof["merge"] = ("in-kernel (PA_FLAG_FUSED_MERGE)" if fused else "split_kv_merge launch") if chunk > 0 else "none"
+    roof["merge"] = (("in-kernel (PA_FLAG_FUSED_MERGE)" if fused else
+                      "split_kv_merge launch" + (" inside the call (kernel_ms includes it)" if args.balanced else ""))
+                     if chunk > 0 else "none")
+    roof["split"] = ("PA_FLAG_BALANCED_SPLIT requested (applied by the MLA and f16-tile append kernels)"
+                     if args.balanced and chunk > 0 else "fixed chunks")
     roof["alg_bytes_per_launch"] = alg_bytes
     roof["flops_per_launch"] = flops
 

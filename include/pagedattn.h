@@ -109,19 +109,40 @@ typedef struct pa_problem {
  *   decode with q_len * G <= 4 for head dim 128); for wider tiles the call
  *   enqueues split_kv_merge as without the flag, which spreads that work over
  *   the chip.  Either way the results are the same bits.  The
- *   workspace then starts with int32 counters [B, H_kv, ceil(max_q_len * G /
- *   16)] (G = H_q / H_kv), and the partials follow at the next 256-byte
- *   boundary (paged_attn_workspace_size counts both).  The counters MUST be
- *   zero when a call starts: allocate the workspace zeroed; every completed
- *   call leaves them zero.  Their place depends only on batch, the head
- *   counts and max_q_len, so the workspace stays valid across calls while
- *   those three are unchanged (re-zero it when they change).  Calls that
+ *   workspace then holds int32 counters [B, H_kv, ceil(max_q_len * G / 16)]
+ *   (G = H_q / H_kv) at its start (after the 256 plan bytes of
+ *   PA_FLAG_BALANCED_SPLIT when that is set), and the partials follow at the
+ *   next 256-byte boundary (paged_attn_workspace_size counts all of it).  The
+ *   counters MUST be zero when a call starts: allocate the workspace zeroed;
+ *   every completed call leaves them zero.  Their place depends only on
+ *   batch, the head counts, max_q_len and the flags, so the workspace stays
+ *   valid across calls while those are unchanged (re-zero it when they
+ *   change).  Calls that
  *   overlap on one workspace race (as the partials already do).  Combined
  *   with PA_FLAG_DEFER_MERGE it is INVALID_ARG.  Ignored when chunk_size is
  *   0. */
+/* PA_FLAG_BALANCED_SPLIT: with chunk_size > 0, the KV split is sized from the
+ *   request lengths instead of cut at multiples of chunk_size, after the
+ *   work-list planner of FlashInfer persistent.cuh (each request's KV is cut
+ *   into chunks so that every CTA gets the same work).  On the device, the
+ *   call picks one item length lt (in 64-key tiles, at least chunk_size / 64):
+ *   the smallest for which the (request, KV head, item) groups
+ *   H_kv * sum_b ceil(ceil(T_b / 64) / lt) fit one round of resident
+ *   workgroups.  It then cuts request b into ceil(ceil(T_b / 64) / lt) items
+ *   of equal tile count, so no group carries more than lt tiles while short
+ *   last chunks leave CUs idle.  Applies to the kernels of which at most two
+ *   workgroups fit a CU (MLA; appends of more than 64 packed rows at head
+ *   dim 128); the kernels with many small resident workgroups (decode, 33 to
+ *   64 packed rows) keep fixed chunks, which the dispatcher balances.  The
+ *   workspace starts with 256 bytes for the plan (paged_attn_workspace_size
+ *   counts them); the partial-buffer bound stays C_max, since items are at
+ *   least chunk_size keys.  Not with PA_FLAG_DEFER_MERGE (INVALID_ARG):
+ *   split_kv_merge derives chunks from chunk_size.  Ignored when chunk_size
+ *   is 0. */
 enum {
   PA_FLAG_DEFER_MERGE = 1,
-  PA_FLAG_FUSED_MERGE = 2
+  PA_FLAG_FUSED_MERGE = 2,
+  PA_FLAG_BALANCED_SPLIT = 4
 };
 
 /*
@@ -131,9 +152,10 @@ enum {
  * normalized fp32 partial output row and one natural-log fp32 partial LSE per
  * chunk: [total_q, C_max, H_q, D_v] floats followed (256-byte aligned) by
  * [total_q, C_max, H_q] floats, with C_max = ceil((max_kv_len + max_q_len) /
- * chunk_size).  With PA_FLAG_FUSED_MERGE the int32 merge counters
- * [B, H_kv, ceil(max_q_len * H_q / H_kv / 16)] come first and the partials
- * start at the next 256-byte boundary.  This is the partial-buffer layout of FastDeploy
+ * chunk_size).  PA_FLAG_BALANCED_SPLIT puts 256 bytes of plan first; with
+ * PA_FLAG_FUSED_MERGE the int32 merge counters [B, H_kv, ceil(max_q_len *
+ * H_q / H_kv / 16)] come next, and the partials start at the next 256-byte
+ * boundary.  This is the partial-buffer layout of FastDeploy
  * append_attention_c8_impl.cuh (tmp_workspace / tmp_m / tmp_d, indexed
  * [token, chunk, head, dim]), with FlashInfer persistent.cuh's normalized
  * output + LSE pair in place of the (m, d) pair.  Returns 0 when chunk_size is

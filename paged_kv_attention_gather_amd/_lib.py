@@ -31,6 +31,7 @@ SCALE_PER_CHANNEL = 2
 
 FLAG_DEFER_MERGE = 1
 FLAG_FUSED_MERGE = 2
+FLAG_BALANCED_SPLIT = 4
 
 #: Every entry point include/pagedattn.h declares.
 EXPORTS = (

@@ -49,6 +49,9 @@ struct AttnParams {
   int32_t causal;
   int32_t tree_mask_len;
   int32_t count_stride;         // 16-row groups per (request, KV head) in merge_count
+  int32_t balanced;             // balanced split: item length chosen from the lengths (shared-tile kernels)
+  int32_t group_cap;            // balanced split: (request, KV head, item) groups that fit one round
+  int32_t* plan_out;            // balanced split: the chosen item length (tiles) for the merge, or null
   float qk_mult;                // sm_scale * log2(e)
 };
 
@@ -63,6 +66,7 @@ struct MergeParams {
   int32_t num_q_heads;
   int32_t chunk_size;
   int32_t max_chunks;
+  const int32_t* item_tiles;    // balanced split: item length in 64-key tiles (device), or null
 };
 
 struct GatherParams {

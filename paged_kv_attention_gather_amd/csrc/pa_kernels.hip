@@ -292,11 +292,21 @@ struct Unit {
   bool split;
 };
 
+// Items of the balanced split: request b's T keys are ceil(T / 64) tiles, cut
+// into k = ceil(tiles / lt) items of equal tile count (the last one shorter by
+// less than one item), where lt is the item length chosen for the whole call.
+__device__ __forceinline__ int balanced_items(int T, int lt, int max_chunks) {
+  const int tiles = (T + TK - 1) / TK;
+  return min((tiles + lt - 1) / lt, max_chunks);
+}
+
 // Fills `u` for row tile rt and chunk c of request b; false when the unit is empty.
 // tok0, n: the request's first query token and query length; L: its cached keys.
+// lt > 0: chunk c is item c of the balanced split with items of <= lt tiles;
+// lt = 0: chunk c is keys [c * chunk_size, (c + 1) * chunk_size).
 template <int ROWS>
 __device__ __forceinline__ bool unit_setup_from(const AttnParams& p, int rt, int c, int tok0, int n, int L,
-                                                Unit& u) {
+                                                Unit& u, int lt = 0) {
   u.tok0 = tok0;
   u.n = n;
   u.G = p.group;
@@ -309,7 +319,13 @@ __device__ __forceinline__ bool unit_setup_from(const AttnParams& p, int rt, int
   u.kv_lo = 0;
   u.kv_hi = u.T;
   u.n_chunks = 1;
-  if (p.chunk_size > 0) {
+  if (p.chunk_size > 0 && lt > 0) {
+    u.n_chunks = balanced_items(u.T, lt, p.max_chunks);
+    if (c >= u.n_chunks) return false;
+    const int len = ((u.T + TK - 1) / TK + u.n_chunks - 1) / u.n_chunks * TK;   // keys per item
+    u.kv_lo = c * len;
+    u.kv_hi = min(u.T, u.kv_lo + len);
+  } else if (p.chunk_size > 0) {
     u.n_chunks = (u.T + p.chunk_size - 1) / p.chunk_size;
     if (c >= u.n_chunks) return false;
     u.kv_lo = c * p.chunk_size;
@@ -352,6 +368,49 @@ __device__ __forceinline__ bool unit_setup(const AttnParams& p, int b, int rt, i
 // request lengths are spread, and no XCD is left with more workgroups than
 // CUs.  False for the padding past the last group and for empty row tiles;
 // otherwise `u` is set.
+// Item length of the balanced split (after the work-list planner of
+// FlashInfer persistent.cuh, which cuts each request's KV into chunks so that
+// the CTAs get equal work, there on the host): the smallest lt >= chunk_size /
+// 64 tiles for which the groups H_kv * sum_b ceil(tiles_b / lt) fit p.group_cap
+// (one round of resident workgroups), by binary search over lt; the longest
+// request's tile count when no lt fits.  Every wave of every workgroup computes
+// the same value from the lengths.
+__device__ __forceinline__ int balanced_item_tiles(const AttnParams& p, int lane) {
+  auto tiles_of = [&](int bb) {
+    if (bb >= p.batch) return 0;
+    const int n = p.cu_seqlens_q ? p.cu_seqlens_q[bb + 1] - p.cu_seqlens_q[bb] : p.q_len_uniform;
+    return n > 0 ? (p.seq_lens_kv[bb] + n + TK - 1) / TK : 0;   // requests without queries: no items
+  };
+  const int t0 = tiles_of(lane);   // the first 64 requests stay in a register
+  // wave reductions, returned as scalars (the same in every lane), so the
+  // search and every address derived from lt stay uniform
+  auto wave_sum = [](int v) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) v += __shfl_xor(v, d, 64);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  auto wave_max = [](int v) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) v = max(v, __shfl_xor(v, d, 64));
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  int tmax = t0;
+  for (int b0 = 64; b0 < p.batch; b0 += 64) tmax = max(tmax, tiles_of(b0 + lane));
+  tmax = wave_max(tmax);
+  auto groups = [&](int lt) {
+    int s = (t0 + lt - 1) / lt;
+    for (int b0 = 64; b0 < p.batch; b0 += 64) s += (tiles_of(b0 + lane) + lt - 1) / lt;
+    return wave_sum(s) * p.num_kv_heads;
+  };
+  int lo = max(1, p.chunk_size / TK), hi = max(lo, tmax);
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (groups(mid) <= p.group_cap) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
 template <int ROWS>
 __device__ __forceinline__ bool shared_tile_unit(const AttnParams& p, int& b, int& g, Unit& u) {
   const int L = (int)blockIdx.x;
@@ -359,12 +418,17 @@ __device__ __forceinline__ bool shared_tile_unit(const AttnParams& p, int& b, in
   const int slot = L >> 3;
   const int rt = p.row_tiles - 1 - slot % p.row_tiles;
   int r = (slot / p.row_tiles) * 8 + (L & 7);   // group index
+  const int lt = p.balanced ? balanced_item_tiles(p, lane) : 0;
+  if (p.balanced && p.plan_out && L == 0 && threadIdx.x == 0) *p.plan_out = lt;   // for the merge
   if (!p.compact_groups) {
     const int c = r % p.max_chunks;
     r /= p.max_chunks;
     g = r % p.num_kv_heads;
     b = r / p.num_kv_heads;
-    return b < p.batch && unit_setup<ROWS>(p, b, rt, c, u);
+    if (b >= p.batch) return false;
+    const int tok0 = p.cu_seqlens_q ? p.cu_seqlens_q[b] : b * p.q_len_uniform;
+    const int n = p.cu_seqlens_q ? p.cu_seqlens_q[b + 1] - tok0 : p.q_len_uniform;
+    return unit_setup_from<ROWS>(p, rt, c, tok0, n, p.seq_lens_kv[b], u, lt);
   }
   // lane l looks at request b0 + l: first token, query length, cached keys
   auto fetch = [&](int b0, int& tok0, int& n, int& kl) {
@@ -382,7 +446,9 @@ __device__ __forceinline__ bool shared_tile_unit(const AttnParams& p, int& b, in
     n -= tok0;
     int cnt = 0;   // groups of request b0 + lane: KV heads x chunks with work
     if (b0 + lane < p.batch && n > 0)
-      cnt = p.num_kv_heads * (p.chunk_size > 0 ? min((kl + n + p.chunk_size - 1) / p.chunk_size, p.max_chunks) : 1);
+      cnt = p.num_kv_heads * (p.chunk_size <= 0 ? 1
+                              : lt > 0      ? balanced_items(kl + n, lt, p.max_chunks)
+                                            : min((kl + n + p.chunk_size - 1) / p.chunk_size, p.max_chunks));
     int incl = cnt;   // inclusive prefix sum over the 64 lanes
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -400,7 +466,7 @@ __device__ __forceinline__ bool shared_tile_unit(const AttnParams& p, int& b, in
       g = r / nch;
       const int c = r - g * nch;
       return unit_setup_from<ROWS>(p, rt, c, __builtin_amdgcn_readlane(tok0, lb), __builtin_amdgcn_readlane(n, lb),
-                                   __builtin_amdgcn_readlane(kl, lb), u);
+                                   __builtin_amdgcn_readlane(kl, lb), u, lt);
     }
     base += total;
     tok0 = tok0_nx;
@@ -1085,8 +1151,15 @@ __device__ __forceinline__ void merge_if_last(const AttnParams& p, const Unit& u
   if (!last) return;
   if (wave == 0 && lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   constexpr int QPR = DV / 4;   // four-channel slots per row
-  constexpr int MB = 8;         // chunk slots loaded per round trip
-  constexpr int SPT = 2;        // row slots per thread whose loads travel together
+  // chunk slots loaded per round trip: the agent-scope loads are single
+  // dwords, so eight slots in flight (40 loads) raised the register count of
+  // the narrow kernels that compile this tail
+  constexpr int MB = 4;
+  // row slots per thread whose loads travel together: one, since this tail is
+  // compiled into every attention kernel and its loads in flight set the
+  // kernel's register count (two measured no faster on decode and cost the
+  // 64-dim kernels a wave per SIMD)
+  constexpr int SPT = 1;
   const int rows = min(u.rows_total, u.row0 + ROWS) - u.row0;
   const int64_t H = p.num_q_heads;
   const int nc = u.n_chunks;
@@ -2173,7 +2246,8 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MergeParams p) {
   const float4_t o0 = *(const float4_t*)orow;
   const float4_t o1 = *(const float4_t*)(orow + c1 * H * DV);
   const int T = kv_cached + n;
-  const int nc = min((T + p.chunk_size - 1) / p.chunk_size, p.max_chunks);
+  const int nc = p.item_tiles ? balanced_items(T, *p.item_tiles, p.max_chunks)
+                              : min((T + p.chunk_size - 1) / p.chunk_size, p.max_chunks);
   m.add(nc > 0, l0, o0);
   m.add(nc > 1, l1, o1);
   for (int c0 = 2; c0 < nc; c0 += MB) {

@@ -68,8 +68,11 @@ int32_t check_problem(const pa_problem* p) {
                 p->head_dim_qk, p->head_dim_v);
   if (log2_exact(p->page_size) < 0 || p->page_size < 16 || p->page_size > 1024)
     return fail(PA_ERR_UNSUPPORTED, "page_size %d must be a power of two in [16, 1024]", p->page_size);
-  if (p->flags & ~(PA_FLAG_DEFER_MERGE | PA_FLAG_FUSED_MERGE))
+  if (p->flags & ~(PA_FLAG_DEFER_MERGE | PA_FLAG_FUSED_MERGE | PA_FLAG_BALANCED_SPLIT))
     return fail(PA_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
+  if ((p->flags & PA_FLAG_DEFER_MERGE) && (p->flags & PA_FLAG_BALANCED_SPLIT))
+    return fail(PA_ERR_INVALID_ARG,
+                "PA_FLAG_BALANCED_SPLIT cuts chunks split_kv_merge cannot derive: not with PA_FLAG_DEFER_MERGE");
   if ((p->flags & PA_FLAG_DEFER_MERGE) && (p->flags & PA_FLAG_FUSED_MERGE))
     return fail(PA_ERR_INVALID_ARG, "PA_FLAG_DEFER_MERGE and PA_FLAG_FUSED_MERGE exclude each other");
   if (p->num_pages <= 0 || p->max_pages_per_seq <= 0)
@@ -112,20 +115,25 @@ int64_t count_stride_of(const pa_problem* p) {
   return std::max<int64_t>(1, ceil_div((int64_t)p->max_q_len * (p->num_q_heads / p->num_kv_heads), 16));
 }
 
-// With PA_FLAG_FUSED_MERGE the merge counters come first, so their place and
-// size depend only on batch, the head counts and max_q_len (not on total_q):
-// a workspace zeroed once stays valid for every call with those three.
+// PA_FLAG_BALANCED_SPLIT reserves 256 bytes first (the chosen item length,
+// read by the merge).  With PA_FLAG_FUSED_MERGE the merge counters come next,
+// so their place and size depend only on batch, the head counts, max_q_len and
+// the flags (not on total_q): a workspace zeroed once stays valid for every
+// call with those.
 struct WorkspaceLayout {
-  size_t count_bytes, part_o_offset, part_o_bytes, part_lse_offset, part_lse_bytes, total;
+  size_t plan_bytes, count_offset, count_bytes, part_o_offset, part_o_bytes, part_lse_offset, part_lse_bytes,
+      total;
 };
 
 WorkspaceLayout workspace_layout(const pa_problem* p, int64_t total_q) {
-  WorkspaceLayout w{0, 0, 0, 0, 0, 0};
+  WorkspaceLayout w{0, 0, 0, 0, 0, 0, 0, 0};
   if (p->chunk_size <= 0) return w;
   const int64_t mc = max_chunks_of(p);
+  if (p->flags & PA_FLAG_BALANCED_SPLIT) w.plan_bytes = 256;
+  w.count_offset = w.plan_bytes;
   if (p->flags & PA_FLAG_FUSED_MERGE)
     w.count_bytes = (size_t)p->batch * p->num_kv_heads * count_stride_of(p) * sizeof(int32_t);
-  w.part_o_offset = (w.count_bytes + 255) & ~size_t(255);
+  w.part_o_offset = (w.count_offset + w.count_bytes + 255) & ~size_t(255);
   w.part_o_bytes = (size_t)total_q * mc * p->num_q_heads * p->head_dim_v * sizeof(float);
   w.part_lse_offset = (w.part_o_offset + w.part_o_bytes + 255) & ~size_t(255);
   w.part_lse_bytes = (size_t)total_q * mc * p->num_q_heads * sizeof(float);
@@ -272,7 +280,7 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
     const char* fm_env = std::getenv("PAGEDATTN_FUSED_MERGE");
     if (fm_env && (fm_env[0] == '0' || fm_env[0] == '1') && fm_env[1] == 0) fused = fm_env[0] == '1';
   }
-  ap.merge_count = fused ? static_cast<int32_t*>(workspace) : nullptr;
+  ap.merge_count = fused ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.count_offset) : nullptr;
   ap.count_stride = (int32_t)count_stride_of(p);
   ap.q_row_stride = p->q_row_stride;
   ap.k_stride_page = p->k_stride_page;
@@ -321,6 +329,30 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
       ap.compact_groups = (int64_t)grid.x <= 2LL * per_cu * cus;
   }
+  // Balanced split (PA_FLAG_BALANCED_SPLIT) in the kernels of which at most
+  // two workgroups fit a CU (the MLA kernel and the append kernel's f16-tile
+  // variant): a round is coarse there, and items sized on the device so that
+  // the (request, KV head, item) groups fill one round take the place of
+  // fixed chunks whose ragged last chunks leave CUs idle; numbering only
+  // groups with work puts that round on the XCDs.  On the MLA workload this
+  // makes the result independent of the chunk floor (about 198 us for floors
+  // of 1024 to 3072 keys, where fixed chunks of 1024 take 313 us).  Kernels
+  // with many small resident workgroups keep fixed chunks: the dispatcher
+  // balances their short units, and one round of long items measured 2x
+  // slower on the spec-decode workload (540 vs 271 us).  So does the decode
+  // kernel (short single-wave units).
+  int bal_dev = 0, bal_cus = 0;
+  const int bal_per_cu = pa::resident_per_cu(cfg);
+  if ((p->flags & PA_FLAG_BALANCED_SPLIT) && p->chunk_size > 0 && !decode_kernel && bal_per_cu > 0 &&
+      bal_per_cu <= 2 && hipGetDevice(&bal_dev) == hipSuccess &&
+      hipDeviceGetAttribute(&bal_cus, hipDeviceAttributeMultiprocessorCount, bal_dev) == hipSuccess &&
+      bal_cus > 0) {
+    const int per_cu = bal_per_cu, cus = bal_cus;
+    ap.balanced = 1;
+    ap.group_cap = (int32_t)std::max<int64_t>(1, (int64_t)std::max(per_cu, 1) * cus / row_tiles);
+    ap.plan_out = static_cast<int32_t*>(workspace);
+    if (!(cg_env && (cg_env[0] == '0' || cg_env[0] == '1') && cg_env[1] == 0)) ap.compact_groups = 1;
+  }
   hipError_t e = pa::launch_attention(cfg, ap, grid, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (p->chunk_size > 0 && !(p->flags & PA_FLAG_DEFER_MERGE) && !fused) {
@@ -335,6 +367,7 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
     mp.num_q_heads = p->num_q_heads;
     mp.chunk_size = p->chunk_size;
     mp.max_chunks = ap.max_chunks;
+    mp.item_tiles = ap.balanced ? ap.plan_out : nullptr;
     e = pa::launch_merge(p->head_dim_v, mp, p->batch, p->max_q_len, s);
     if (e != hipSuccess) return fail(PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
   }

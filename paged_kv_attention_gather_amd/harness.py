@@ -41,7 +41,8 @@ def problem_for(w, chunk_size=None, q_row_stride=None, flags=0) -> L.PaProblem:
 class DeviceProblem:
     """Device tensors of a workload plus its outputs and workspace."""
 
-    def __init__(self, w, device="cuda", chunk_size=None, decode=None, defer_merge=False, fused_merge=False):
+    def __init__(self, w, device="cuda", chunk_size=None, decode=None, defer_merge=False, fused_merge=False,
+                 balanced=False):
         import torch
         self.torch = torch
         self.w = w
@@ -61,7 +62,8 @@ class DeviceProblem:
         self.block_table = torch.from_numpy(np.ascontiguousarray(w.block_table, dtype=np.int32)).to(dev)
         tm = getattr(w, "tree_mask", None)
         self.tree_mask = None if tm is None else torch.from_numpy(np.ascontiguousarray(tm, dtype=np.uint8)).to(dev)
-        flags = (L.FLAG_DEFER_MERGE if defer_merge else 0) | (L.FLAG_FUSED_MERGE if fused_merge else 0)
+        flags = ((L.FLAG_DEFER_MERGE if defer_merge else 0) | (L.FLAG_FUSED_MERGE if fused_merge else 0) |
+                 (L.FLAG_BALANCED_SPLIT if balanced else 0))
         self.prob = problem_for(w, chunk_size=chunk_size, flags=flags)
         self.total_q = int(w.total_q)
         self.out = torch.empty((self.total_q, w.num_q_heads, w.head_dim_v), dtype=torch.bfloat16, device=dev)

@@ -90,6 +90,10 @@ def test_workspace_size_with_fused_merge_counters(lib):
     assert P.workspace_size(fused, total_q) == (counters + 255) // 256 * 256 + plain
     assert P.workspace_size(base_problem(chunk_size=0, flags=L.FLAG_FUSED_MERGE), total_q) == 0
     assert P.workspace_size(base_problem(flags=L.FLAG_DEFER_MERGE), total_q) == plain
+    # the balanced split adds 256 bytes of plan in front of everything else
+    both = base_problem(flags=L.FLAG_FUSED_MERGE | L.FLAG_BALANCED_SPLIT)
+    assert P.workspace_size(both, total_q) == 256 + (counters + 255) // 256 * 256 + plain
+    assert P.workspace_size(base_problem(flags=L.FLAG_BALANCED_SPLIT), total_q) == 256 + plain
 
 
 def _decode(prob, q_len=1, workspace=None, ws_bytes=0, **ptrs):
@@ -124,8 +128,9 @@ def _append(prob, total_q=8, workspace=None, ws_bytes=0, **ptrs):
     (dict(k_stride_token=120), L.PA_ERR_INVALID_ARG),             # not 16-byte multiple
     (dict(batch=-1), L.PA_ERR_INVALID_ARG),
     (dict(batch=70000), L.PA_ERR_UNSUPPORTED),
-    (dict(flags=4), L.PA_ERR_INVALID_ARG),                        # unknown flag bit
+    (dict(flags=8), L.PA_ERR_INVALID_ARG),                        # unknown flag bit
     (dict(flags=3), L.PA_ERR_INVALID_ARG),                        # deferred and fused merge together
+    (dict(flags=5), L.PA_ERR_INVALID_ARG),                        # deferred merge of a balanced split
 ])
 def test_invalid_problems_are_rejected(lib, over, status):
     assert _decode(base_problem(**over)) == status

@@ -466,6 +466,60 @@ def test_fused_merge_workspace_reuse_shorter_lengths(force, monkeypatch):
     compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what="shorter lengths on a reused workspace")
 
 
+# ------------------------------------------------------- balanced split --
+#
+# PA_FLAG_BALANCED_SPLIT: the shared-tile and MLA kernels cut each request's
+# keys into items whose length (at least chunk_size) is chosen on the device
+# from all the lengths; every cut merges to the same exact attention, so the
+# outputs are checked against the oracle.  Small cases run with the split's
+# floor (items of chunk_size), the full-size spec-decode and MLA workloads
+# with the device's one-round target; the in-kernel merge reads the same item
+# structure.
+BALANCED_CASES = {
+    "spec40_query_outliers_channel": EDGE_CASES["spec40_query_outliers_channel"],
+    "decode_q8_g8": EDGE_CASES["decode_q8_g8"],
+    "append_chunked": EDGE_CASES["append_chunked"],
+    "append_zero_len_chunked": FUSED_CASES["append_zero_len_chunked"],
+    "mla_int8_g16_q2": EDGE_CASES["mla_int8_g16_q2"],
+    "tree_q5_g8_nw3": TREE_CASES["tree_q5_g8_nw3"],
+}
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("case", sorted(BALANCED_CASES))
+def test_balanced_split_parity(case, fused, monkeypatch):
+    need_gpu()
+    if fused:
+        monkeypatch.setenv("PAGEDATTN_FUSED_MERGE", "1")
+    w = _edge(case, **BALANCED_CASES[case])
+    announce(f"balanced split {case} fused={fused}")
+    dp, (out, lse) = _run(w, balanced=True, fused_merge=fused)
+    O_ref, lse_ref = oracle.attention(w)
+    n = int(w.q_lens.sum())
+    compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what=f"{case} balanced fused={fused}")
+    if fused:
+        dp.out.zero_()
+        dp.run()
+        again = dp.outputs()
+        assert np.array_equal(out, again[0]) and np.array_equal(lse, again[1]), "second call differs"
+
+
+@pytest.mark.parametrize("idx", [4, 5])
+def test_balanced_split_full_config_sampled(idx):
+    need_gpu()
+    w = config_workload(idx)
+    announce(f"balanced split config_workload({idx}) {w.name} (sampled requests)")
+    chunk = 1024 if idx == 5 else None   # MLA: the item floor below the 3072 fixed chunk
+    _, (out, lse) = _run(w, balanced=True, chunk_size=chunk)
+    rng = np.random.default_rng(2000 + idx)
+    T = w.kv_tokens()
+    pick = {int(np.argmax(T)), int(np.argmin(T))}
+    pick.update(rng.choice(w.batch, size=min(w.batch, 4), replace=False).tolist())
+    reqs = sorted(pick)
+    O_ref, lse_ref = oracle.attention(w, requests=reqs)
+    compare(out, lse, O_ref, lse_ref, rows=token_rows(w, reqs), what=f"{w.name} balanced requests {reqs}")
+
+
 # ----------------------------------------------------- full-size workloads --
 
 @pytest.mark.parametrize("idx", [2, 3, 4, 5])
