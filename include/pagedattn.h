@@ -105,10 +105,10 @@ typedef struct pa_problem {
  *   partials itself and no split_kv_merge is enqueued: the last workgroup to
  *   finish a (request, KV head, row tile) merges its rows, as XQA
  *   mla_sm120.cu does with its semaphores in mergePartialOutputs.  This is
- *   done where a row tile's merge is one short pass (few packed rows, as in
- *   decode with q_len * G <= 4 for head dim 128); for wider tiles the call
- *   enqueues split_kv_merge as without the flag, which spreads that work over
- *   the chip.  Either way the results are the same bits.  The
+ *   done in the decode kernel (at most 32 packed rows) where a row tile's
+ *   merge is one short pass (q_len * G <= 4 for head dim 128); elsewhere the
+ *   call enqueues split_kv_merge as without the flag, which spreads that work
+ *   over the chip.  Either way the results are the same bits.  The
  *   workspace then holds int32 counters [B, H_kv, ceil(max_q_len * G / 16)]
  *   (G = H_q / H_kv) at its start (after the 256 plan bytes of
  *   PA_FLAG_BALANCED_SPLIT when that is set), and the partials follow at the
@@ -130,10 +130,10 @@ typedef struct pa_problem {
  *   H_kv * sum_b ceil(ceil(T_b / 64) / lt) fit one round of resident
  *   workgroups.  It then cuts request b into ceil(ceil(T_b / 64) / lt) items
  *   of equal tile count, so no group carries more than lt tiles while short
- *   last chunks leave CUs idle.  Applies to the kernels of which at most two
- *   workgroups fit a CU (MLA; appends of more than 64 packed rows at head
- *   dim 128); the kernels with many small resident workgroups (decode, 33 to
- *   64 packed rows) keep fixed chunks, which the dispatcher balances.  The
+ *   last chunks leave CUs idle.  Applies to the MLA layout (one workgroup per
+ *   CU); the other kernels keep fixed chunks (the dispatcher balances their
+ *   many small resident workgroups, and an unchunked append is faster than
+ *   either split).  The
  *   workspace starts with 256 bytes for the plan (paged_attn_workspace_size
  *   counts them); the partial-buffer bound stays C_max, since items are at
  *   least chunk_size keys.  Not with PA_FLAG_DEFER_MERGE (INVALID_ARG):

@@ -411,15 +411,20 @@ __device__ __forceinline__ int balanced_item_tiles(const AttnParams& p, int lane
   return lo;
 }
 
-template <int ROWS>
+// BAL: the balanced split's planner is compiled in (a variant of the MLA
+// kernel of its own: in the kernels' main loops it cost SGPR spills).
+template <int ROWS, bool BAL = false>
 __device__ __forceinline__ bool shared_tile_unit(const AttnParams& p, int& b, int& g, Unit& u) {
   const int L = (int)blockIdx.x;
   const int lane = (int)threadIdx.x & 63;
   const int slot = L >> 3;
   const int rt = p.row_tiles - 1 - slot % p.row_tiles;
   int r = (slot / p.row_tiles) * 8 + (L & 7);   // group index
-  const int lt = p.balanced ? balanced_item_tiles(p, lane) : 0;
-  if (p.balanced && p.plan_out && L == 0 && threadIdx.x == 0) *p.plan_out = lt;   // for the merge
+  int lt = 0;
+  if constexpr (BAL) {
+    if (p.balanced) lt = balanced_item_tiles(p, lane);
+    if (p.balanced && p.plan_out && L == 0 && threadIdx.x == 0) *p.plan_out = lt;   // for the merge
+  }
   if (!p.compact_groups) {
     const int c = r % p.max_chunks;
     r /= p.max_chunks;
@@ -1123,33 +1128,21 @@ struct RowMerge {
 // coherent at device scope by itself), and the order is kept by waiting for
 // the wave's stores to be acknowledged (vmcnt 0; stores count there on this
 // ISA) before the counter's atomic add, whose result the merging unit waits
-// for before its first load.  Called by the
-// NWA waves of the workgroup that are still running (wave = 0..NWA-1), after
-// their partial stores; ROWS packed rows from u.row0 belong to the unit.
-// With NWA > 1, last_lds is one int of LDS that no wave uses any more once
-// all waves have stored their rows (the kernels pass a staging tile: a
-// variable of its own would cost the append kernel its second workgroup per
-// CU, whose LDS is full).
-template <int DV, int ROWS, int NWA>
-__device__ __forceinline__ void merge_if_last(const AttnParams& p, const Unit& u, int b, int g, int wave,
-                                              int lane, int* last_lds = nullptr) {
+// for before its first load.  Called by the decode kernel's wave that writes
+// the unit's rows (ROWS packed rows from u.row0), after its partial stores; the
+// wider shared-tile and MLA tiles merge in split_merge_kernel instead (merged
+// here by one workgroup they measured slower, and the tail cost their main
+// loops SGPR spills).
+template <int DV, int ROWS>
+__device__ __forceinline__ void merge_if_last(const AttnParams& p, const Unit& u, int b, int g, int lane) {
   if (!p.merge_count || !u.split) return;
   wait_vmcnt<0>();   // this wave's partial stores are visible at device scope
   int32_t* cnt = p.merge_count + ((int64_t)b * p.num_kv_heads + g) * p.count_stride + (u.row0 >> 4);
-  bool last;
-  if constexpr (NWA > 1) {
-    __syncthreads();   // every wave's partial rows are published (and its LDS reads done)
-    if (wave == 0 && lane == 0)
-      *last_lds = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == u.n_chunks - 1;
-    __syncthreads();
-    last = *last_lds != 0;
-  } else {
-    int old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last = __builtin_amdgcn_readfirstlane(old) == u.n_chunks - 1;
-  }
+  int old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool last = __builtin_amdgcn_readfirstlane(old) == u.n_chunks - 1;
   if (!last) return;
-  if (wave == 0 && lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   constexpr int QPR = DV / 4;   // four-channel slots per row
   // chunk slots loaded per round trip: the agent-scope loads are single
   // dwords, so eight slots in flight (40 loads) raised the register count of
@@ -1163,14 +1156,14 @@ __device__ __forceinline__ void merge_if_last(const AttnParams& p, const Unit& u
   const int rows = min(u.rows_total, u.row0 + ROWS) - u.row0;
   const int64_t H = p.num_q_heads;
   const int nc = u.n_chunks;
-  for (int base = wave * 64 + lane; base < rows * QPR; base += SPT * NWA * 64) {
+  for (int base = lane; base < rows * QPR; base += SPT * 64) {
     bool ok[SPT];
     int64_t tok[SPT];
     int h[SPT], q4[SPT];
     RowMerge m[SPT];
 #pragma unroll
     for (int t = 0; t < SPT; ++t) {
-      const int idx = base + t * NWA * 64;
+      const int idx = base + t * 64;
       ok[t] = idx < rows * QPR;
       const int r = u.row0 + (ok[t] ? idx / QPR : 0);
       q4[t] = idx % QPR;
@@ -1567,7 +1560,7 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
   float4_t vsc[MD];
   load_v_scales<DV>(p, g, lane, vsc);
   write_rows<DV, NT>(p, u, g, u.c, lane, KV_OFF, q, st, vsc);
-  merge_if_last<DV, ROWS, NW>(p, u, b, g, wave, lane, (int*)smem);
+
 }
 
 // -------------------------------------------------------- decode attention --
@@ -1685,7 +1678,7 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
 #pragma unroll
     for (int md = 0; md < MD; ++md) vsc[md] = float4_t{0.f, 0.f, 0.f, 0.f};
     write_rows<D, NT>(p, u, g, c, lane, KV_OFF, q, st, vsc);
-    merge_if_last<D, 16 * NT, 1>(p, u, b, g, 0, lane);
+    merge_if_last<D, 16 * NT>(p, u, b, g, lane);
     return;
   }
 
@@ -1846,7 +1839,7 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
     load_v_scales<D>(p, g, lane, vsc);
   }
   write_rows<D, NT>(p, u, g, c, lane, KV_OFF, q, st, vsc);
-  merge_if_last<D, 16 * NT, 1>(p, u, b, g, 0, lane);   // wave 0 alone is left when KS > 1
+  merge_if_last<D, 16 * NT>(p, u, b, g, lane);   // wave 0 alone is left when KS > 1
 }
 
 // ------------------------------------------------------- MLA latent decode --
@@ -1868,7 +1861,7 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
 
 constexpr int MLA_WAVES = 4;  // waves (= 16-row tiles) per MLA workgroup
 
-template <bool FP8, bool HILO>
+template <bool FP8, bool HILO, bool BAL>
 __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams p) {
   constexpr int DQK = 576, DV = 512, NW = MLA_WAVES;
   constexpr int NTA = 1;                          // 16-row tiles per wave in phase A
@@ -1899,7 +1892,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
   const int grp = lane >> 4;
   int b, g;
   Unit u;
-  if (!shared_tile_unit<ROWS>(p, b, g, u)) return;   // a chunk's row tiles share an XCD
+  if (!shared_tile_unit<ROWS, BAL>(p, b, g, u)) return;   // a chunk's row tiles share an XCD
   const int32_t* table_row = p.block_table + (int64_t)b * p.max_pages_per_seq;
   const int key_end = u.key_end, kv_lo = u.kv_lo, n_tiles = u.n_tiles;
   const int page_shift = p.page_shift;
@@ -2161,9 +2154,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
     if (grp == 0) lrow_lds[(wave * NTA + nt) * 16 + l16] = lt;
     if (grp == 0 && q.ok[nt]) {
       const int tok = u.tok0 + q.tok[nt];
-      if (u.split)
-        store_partial(p.part_lse + ((int64_t)tok * p.max_chunks + u.c) * H_q + q.head[nt], lse_nat,
-                      p.merge_count != nullptr);
+      if (u.split) p.part_lse[((int64_t)tok * p.max_chunks + u.c) * H_q + q.head[nt]] = lse_nat;
       else if (p.lse) p.lse[(int64_t)tok * H_q + q.head[nt]] = lse_nat;
     }
   }
@@ -2197,7 +2188,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = fmaf(o[md][nt][i], inv, -off) * vsc[md][i];
       if (u.split) {
-        store_partial4(prow + d, v, p.merge_count != nullptr);
+        *(float4_t*)(prow + d) = v;
       } else {
         const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
         const uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
@@ -2205,7 +2196,6 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
       }
     }
   }
-  merge_if_last<DV, ROWS, NW>(p, u, b, g, wave, lane, (int*)kst);
 }
 
 // ------------------------------------------------------------------- merge --
@@ -2297,7 +2287,12 @@ hipError_t launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
 
 template <bool FP8, bool HILO>
 hipError_t launch_mla(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((paged_mla_kernel<FP8, HILO>), grid, dim3(MLA_WAVES * 64), 0, stream, p);
+  // the balanced split's planner is a variant of its own (it costs the main
+  // loop SGPR spills)
+  if (p.balanced)
+    hipLaunchKernelGGL((paged_mla_kernel<FP8, HILO, true>), grid, dim3(MLA_WAVES * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((paged_mla_kernel<FP8, HILO, false>), grid, dim3(MLA_WAVES * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -2323,7 +2318,7 @@ int occ_one() {
 }
 template <bool FP8, bool HILO>
 int occ_mla() {
-  return occupancy_of(paged_mla_kernel<FP8, HILO>, MLA_WAVES * 64);
+  return occupancy_of(paged_mla_kernel<FP8, HILO, false>, MLA_WAVES * 64);
 }
 template <int D, bool FP8, int NT, bool HILO, int KS, bool TREE>
 int occ_decode() {

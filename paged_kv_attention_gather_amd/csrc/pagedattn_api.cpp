@@ -271,7 +271,10 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   // split_kv_merge spreads the same work over the chip: measured 364 vs 265 us
   // on the spec-decode workload and 272 vs 199 us on MLA.  Those paths
   // enqueue split_kv_merge as without the flag (same results).
-  // PAGEDATTN_FUSED_MERGE (0 or 1) overrides the choice, for tests and tuning.
+  // PAGEDATTN_FUSED_MERGE (0 or 1) overrides the choice, for tests and tuning,
+  // within the decode kernel, the one that compiles the merge tail (in the
+  // shared-tile and MLA kernels it cost SGPR spills in the main loop, and
+  // the host never picks the in-kernel merge for their wide tiles).
   bool fused = wl.count_bytes > 0;
   if (fused) {
     const int64_t unit_rows = std::min<int64_t>(rows_max, 16LL * cfg.nt * (cfg.nstage == 0 ? 1 : cfg.nw));
@@ -279,6 +282,7 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
     fused = unit_rows * (p->head_dim_v / 4) <= 2 * merge_threads;
     const char* fm_env = std::getenv("PAGEDATTN_FUSED_MERGE");
     if (fm_env && (fm_env[0] == '0' || fm_env[0] == '1') && fm_env[1] == 0) fused = fm_env[0] == '1';
+    fused = fused && cfg.nstage == 0;
   }
   ap.merge_count = fused ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.count_offset) : nullptr;
   ap.count_stride = (int32_t)count_stride_of(p);
@@ -329,9 +333,8 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
       ap.compact_groups = (int64_t)grid.x <= 2LL * per_cu * cus;
   }
-  // Balanced split (PA_FLAG_BALANCED_SPLIT) in the kernels of which at most
-  // two workgroups fit a CU (the MLA kernel and the append kernel's f16-tile
-  // variant): a round is coarse there, and items sized on the device so that
+  // Balanced split (PA_FLAG_BALANCED_SPLIT) in the MLA kernel, of which one
+  // workgroup fits a CU: a round is coarse there, and items sized on the device so that
   // the (request, KV head, item) groups fill one round take the place of
   // fixed chunks whose ragged last chunks leave CUs idle; numbering only
   // groups with work puts that round on the XCDs.  On the MLA workload this
@@ -340,11 +343,14 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   // with many small resident workgroups keep fixed chunks: the dispatcher
   // balances their short units, and one round of long items measured 2x
   // slower on the spec-decode workload (540 vs 271 us).  So does the decode
-  // kernel (short single-wave units).
+  // kernel (short single-wave units).  The append kernel (two workgroups per
+  // CU) keeps fixed chunks as well: a balanced chunked append measured 219 us
+  // against 246 us with fixed 1024-key chunks, but an unchunked append takes
+  // 187 us, and the planner cost that kernel SGPR spills in its main loop.
   int bal_dev = 0, bal_cus = 0;
   const int bal_per_cu = pa::resident_per_cu(cfg);
-  if ((p->flags & PA_FLAG_BALANCED_SPLIT) && p->chunk_size > 0 && !decode_kernel && bal_per_cu > 0 &&
-      bal_per_cu <= 2 && hipGetDevice(&bal_dev) == hipSuccess &&
+  if ((p->flags & PA_FLAG_BALANCED_SPLIT) && p->chunk_size > 0 && cfg.nstage == 1 && bal_per_cu > 0 &&
+      hipGetDevice(&bal_dev) == hipSuccess &&
       hipDeviceGetAttribute(&bal_cus, hipDeviceAttributeMultiprocessorCount, bal_dev) == hipSuccess &&
       bal_cus > 0) {
     const int per_cu = bal_per_cu, cus = bal_cus;

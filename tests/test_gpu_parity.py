@@ -364,18 +364,16 @@ def test_split_kv_merge_against_oracle_partials():
 # ------------------------------------------------------ in-kernel merge --
 #
 # PA_FLAG_FUSED_MERGE: the last workgroup of each (request, KV head, row tile)
-# merges the chunk partials inside the attention kernel with the same merge
+# merges the chunk partials inside the decode kernel with the same merge
 # arithmetic as split_kv_merge, so the outputs must equal the two-launch
-# call's bit for bit.  Every kernel family that writes partials: the decode
-# kernel (1 and 2 row tiles, units split over 2 waves, empty chunks past the
-# causal bound), the 16-row shared-tile kernel (3 and 4 waves), the append
-# kernel (several 128-row tiles, ragged chunks), the MLA kernel, and a draft
-# tree.  The library merges in-kernel only where a row tile's merge is one
-# short pass (decode with a few packed rows) and otherwise enqueues
-# split_kv_merge; PAGEDATTN_FUSED_MERGE=1 forces the in-kernel merge so every
-# kernel's merge tail is tested.  Each case runs twice on one workspace (the
-# counters must be back at zero after a call), then a smaller batch of the
-# same shape reuses it.
+# call's bit for bit.  The library merges in-kernel only where a row tile's
+# merge is one short pass (decode with a few packed rows);
+# PAGEDATTN_FUSED_MERGE=1 forces it for every decode-kernel case (1 and 2 row
+# tiles, units split over 2 or 4 waves, empty chunks past the causal bound,
+# page size 16, fp8, a draft tree).  The wider kernels (16-row shared tiles,
+# append, MLA) enqueue split_kv_merge under the flag, which these cases check
+# too.  Each case runs twice on one workspace (the counters must be back at
+# zero after a call), then a workspace is reused with other lengths.
 FUSED_CASES = {
     "decode_g4_chunk64": dict(q_lens=[1, 1, 1, 1], seq_lens_kv=[0, 63, 700, 2000], decode=True, chunk_size=64),
     "decode_nt2_q8_g4": dict(q_lens=[8, 8, 8], seq_lens_kv=[5, 500, 1300], decode=True, chunk_size=256),
@@ -387,6 +385,7 @@ FUSED_CASES = {
     "append_zero_len_chunked": dict(q_lens=[5, 0, 150, 1], seq_lens_kv=[10, 33, 0, 1290], chunk_size=128),
     "mla_int8_g16_q2": EDGE_CASES["mla_int8_g16_q2"],
     "tree_q5_g8_nw3": TREE_CASES["tree_q5_g8_nw3"],
+    "tree_q4_g4_nt1": TREE_CASES["tree_q4_g4_nt1"],
 }
 
 
@@ -468,13 +467,12 @@ def test_fused_merge_workspace_reuse_shorter_lengths(force, monkeypatch):
 
 # ------------------------------------------------------- balanced split --
 #
-# PA_FLAG_BALANCED_SPLIT: the shared-tile and MLA kernels cut each request's
-# keys into items whose length (at least chunk_size) is chosen on the device
-# from all the lengths; every cut merges to the same exact attention, so the
-# outputs are checked against the oracle.  Small cases run with the split's
-# floor (items of chunk_size), the full-size spec-decode and MLA workloads
-# with the device's one-round target; the in-kernel merge reads the same item
-# structure.
+# PA_FLAG_BALANCED_SPLIT: the MLA kernel cuts each request's keys into items
+# whose length (at least chunk_size) is chosen on the device from all the
+# lengths; every cut merges to the same exact attention, so the outputs are
+# checked against the oracle.  The small MLA case runs at the split's floor,
+# the full-size MLA workload with the device's one-round target; the other
+# kernels keep fixed chunks under the flag, which the remaining cases check.
 BALANCED_CASES = {
     "spec40_query_outliers_channel": EDGE_CASES["spec40_query_outliers_channel"],
     "decode_q8_g8": EDGE_CASES["decode_q8_g8"],
