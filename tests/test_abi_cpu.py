@@ -66,6 +66,14 @@ def test_problem_struct_matches_header():
     assert names == [f for f, _ in L.PaProblem._fields_]
 
 
+def test_flag_values_match_header():
+    """The binding's PA_FLAG_* values are the header's."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    flags = dict((k, int(v)) for k, v in re.findall(r"PA_FLAG_([A-Z_]+)\s*=\s*(\d+)", text))
+    assert flags == {"DEFER_MERGE": L.FLAG_DEFER_MERGE, "FUSED_MERGE": L.FLAG_FUSED_MERGE,
+                     "BALANCED_SPLIT": L.FLAG_BALANCED_SPLIT}
+
+
 def test_workspace_size_formula(lib):
     prob = base_problem()
     total_q = 8
