@@ -334,30 +334,26 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
       ap.compact_groups = (int64_t)grid.x <= 2LL * per_cu * cus;
   }
   // Balanced split (PA_FLAG_BALANCED_SPLIT) in the MLA kernel, of which one
-  // workgroup fits a CU: a round is coarse there, and items sized on the device so that
-  // the (request, KV head, item) groups fill one round take the place of
-  // fixed chunks whose ragged last chunks leave CUs idle; numbering only
-  // groups with work puts that round on the XCDs.  On the MLA workload this
-  // makes the result independent of the chunk floor (about 198 us for floors
-  // of 1024 to 3072 keys, where fixed chunks of 1024 take 313 us).  Kernels
-  // with many small resident workgroups keep fixed chunks: the dispatcher
-  // balances their short units, and one round of long items measured 2x
-  // slower on the spec-decode workload (540 vs 271 us).  So does the decode
-  // kernel (short single-wave units).  The append kernel (two workgroups per
-  // CU) keeps fixed chunks as well: a balanced chunked append measured 219 us
-  // against 246 us with fixed 1024-key chunks, but an unchunked append takes
-  // 187 us, and the planner cost that kernel SGPR spills in its main loop.
-  int bal_dev = 0, bal_cus = 0;
-  const int bal_per_cu = pa::resident_per_cu(cfg);
-  if ((p->flags & PA_FLAG_BALANCED_SPLIT) && p->chunk_size > 0 && cfg.nstage == 1 && bal_per_cu > 0 &&
-      hipGetDevice(&bal_dev) == hipSuccess &&
-      hipDeviceGetAttribute(&bal_cus, hipDeviceAttributeMultiprocessorCount, bal_dev) == hipSuccess &&
-      bal_cus > 0) {
-    const int per_cu = bal_per_cu, cus = bal_cus;
-    ap.balanced = 1;
-    ap.group_cap = (int32_t)std::max<int64_t>(1, (int64_t)std::max(per_cu, 1) * cus / row_tiles);
-    ap.plan_out = static_cast<int32_t*>(workspace);
-    if (!(cg_env && (cg_env[0] == '0' || cg_env[0] == '1') && cg_env[1] == 0)) ap.compact_groups = 1;
+  // workgroup fits a CU: a round is coarse there, so items sized on the
+  // device to fill one round replace fixed chunks whose ragged last chunks
+  // leave CUs idle, and numbering only groups with work puts that round on
+  // the XCDs.  On the MLA workload this makes the time independent of the
+  // chunk floor (about 195 us for floors of 1024 to 3072 keys; fixed chunks
+  // of 1024 keys take 313 us).  The other kernels keep fixed chunks: the
+  // dispatcher balances their many short units (one round of long items
+  // measured 2x slower on the spec-decode workload, 540 vs 271 us), and an
+  // unchunked append is faster than either split (187 us; balanced 219 us,
+  // fixed 1024-key chunks 246 us).
+  if ((p->flags & PA_FLAG_BALANCED_SPLIT) && p->chunk_size > 0 && cfg.nstage == 1) {
+    int dev = 0, cus = 0;
+    const int per_cu = pa::resident_per_cu(cfg);
+    if (per_cu > 0 && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0) {
+      ap.balanced = 1;
+      ap.group_cap = (int32_t)std::max<int64_t>(1, (int64_t)per_cu * cus / row_tiles);
+      ap.plan_out = static_cast<int32_t*>(workspace);
+      if (!(cg_env && (cg_env[0] == '0' || cg_env[0] == '1') && cg_env[1] == 0)) ap.compact_groups = 1;
+    }
   }
   hipError_t e = pa::launch_attention(cfg, ap, grid, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
