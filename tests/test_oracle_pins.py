@@ -230,6 +230,42 @@ def test_p6_split_merge_equals_unsplit(C):
     np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-12)
 
 
+def _merge_over_cuts(w, b, cuts):
+    """Partials of request b over the key ranges [cuts[i], cuts[i+1]), merged."""
+    n = int(w.q_lens[b])
+    k = len(cuts) - 1
+    Oc = np.zeros((n, k, w.num_q_heads, w.head_dim_v))
+    lc = np.full((n, k, w.num_q_heads), -np.inf)
+    for i in range(k):
+        Oc[:, i], lc[:, i] = oa.request_attention(w, b, cuts[i], cuts[i + 1])
+    return oa.merge_partials(Oc, lc)
+
+
+def test_p6_merge_over_any_partition_equals_unsplit():
+    """The LSE merge is exact for any cut of the keys into contiguous ranges,
+    not only for fixed-size chunks: ranges of one key, ranges that straddle
+    pages, ranges past every visible key (lse = -inf), and the equal-tile items
+    of a device-planned split (request cut into ceil(tiles / lt) items of
+    ceil(tiles / items) 4-key tiles)."""
+    w = tiny(seed=13, q_lens=(3, 1, 5), seq_lens_kv=(33, 0, 14), P=4)
+    rng = np.random.default_rng(5)
+    for b in range(w.batch):
+        T = int(w.seq_lens_kv[b]) + int(w.q_lens[b])
+        O, lse = oa.request_attention(w, b, 0, T)
+        partitions = [list(range(T + 1)),                                  # one key each
+                      [0] + sorted(rng.choice(np.arange(1, T), size=min(3, T - 1), replace=False).tolist()) + [T]
+                      if T > 1 else [0, T]]
+        tiles = -(-T // 4)
+        for lt in (1, 2, 3):
+            items = -(-tiles // lt)
+            per = -(-tiles // items) * 4
+            partitions.append([min(T, i * per) for i in range(items)] + [T])
+        for cuts in partitions:
+            O2, lse2 = _merge_over_cuts(w, b, cuts)
+            np.testing.assert_allclose(O2, O, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-12)
+
+
 def test_p6_empty_chunks_have_minus_inf_lse():
     # token 0 of a request with L=2, n=6 sees keys 0..2; chunk [4, 8) is invisible to it
     w = tiny(seed=4, q_lens=(6,), seq_lens_kv=(2,), P=4)
@@ -515,6 +551,7 @@ def test_planted_unweighted_merge_is_caught(monkeypatch):
         return O, np.max(lc, axis=1)
     monkeypatch.setattr(oa, "merge_partials", bad_merge)
     assert _fails(lambda: test_p6_split_merge_equals_unsplit(4))
+    assert _fails(test_p6_merge_over_any_partition_equals_unsplit)
 
 
 def test_planted_transposed_tree_mask_is_caught(monkeypatch):
