@@ -525,9 +525,9 @@ def test_full_config_sampled_parity(idx):
     need_gpu()
     w = config_workload(idx)
     announce(f"attention config_workload({idx}) {w.name} (sampled requests)")
-    _, (out, lse) = _run(w)
+    _, (out, lse) = _run(w)   # the kernels and merge bench.py times
     if w.chunk_size > 0:
-        # the launch configuration bench.py times: the in-kernel merge, which
+        # the one-launch form (PA_FLAG_FUSED_MERGE, bench.py --merge fused)
         # must give the two-launch call's bits over every row
         _, (fo, fl) = _run(w, fused_merge=True)
         assert np.array_equal(out, fo) and np.array_equal(lse, fl), "in-kernel merge differs"
