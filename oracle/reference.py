@@ -18,7 +18,6 @@ from typing import Dict, Iterable, Optional, Tuple
 
 import numpy as np
 
-LN2 = math.log(2.0)
 
 
 # ---------------------------------------------------------------- decoding ---
@@ -274,9 +273,3 @@ def attention_split(w, chunk_size: int, requests: Optional[Iterable[int]] = None
             O[q0:q1], lse[q0:q1] = merge_partials(Oc, lc)
     return O, lse
 
-
-def to_natural_lse_from_log2(m_log2: np.ndarray, d: np.ndarray) -> np.ndarray:
-    """Helper for readers comparing with base-2 conventions: FlashInfer's
-    partial LSE is ``log2(d) + m`` with m in log2 units; its natural-log value
-    is that times ln 2."""
-    return (np.log2(d) + m_log2) * LN2

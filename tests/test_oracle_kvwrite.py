@@ -41,6 +41,37 @@ def test_int8_nearest_code_property():
     assert np.all(q[~inside] == np.sign(r[~inside]) * 127)
 
 
+# Codes decided by the binary32 quotient, where exact division would decide
+# otherwise: x / s rounds (once, in binary32) onto a tie k + 0.5 that the exact
+# quotient misses by a few parts in 1e8, so the tie rule picks the even
+# integer while the exact value's nearest integer is the other one.  Values
+# are binary32 numbers written as hex floats; the test first checks the premise
+# (binary32 quotient on the tie, exact quotient off it) with exact fractions.
+INT8_FP32_TIES = [  # (x, s, binary32 quotient, code, exact quotient's nearest integer)
+    (float.fromhex("0x1.963824p-5"), float.fromhex("0x1.44f9b6p-6"), 2.5, 2, 3),
+    (float.fromhex("-0x1.86e436p-3"), float.fromhex("0x1.42ccfap-9"), -77.5, -78, -77),
+    (float.fromhex("0x1.e95dbap-1"), float.fromhex("0x1.1a2834p-6"), 55.5, 56, 55),
+]
+
+
+def _premise(x, s, q32):
+    from fractions import Fraction
+    xs, ss = np.float32(x), np.float32(s)
+    assert float(xs) == x and float(ss) == s, "pin values must be binary32 numbers"
+    assert float(xs / ss) == q32, "binary32 quotient is not the stated value"
+    exact = Fraction(x) / Fraction(s)
+    assert exact != Fraction(q32), "exact quotient must miss the tie"
+    return exact
+
+
+def test_int8_code_follows_the_binary32_quotient():
+    for x, s, q32, code, exact_code in INT8_FP32_TIES:
+        exact = _premise(x, s, q32)
+        assert round(exact) == exact_code          # Fraction rounding: nearest integer
+        got = int(kw.int8_quantize(np.array([x], np.float32), np.array([s], np.float32)).view(np.int8)[0])
+        assert got == code, (x, s, got, code)
+
+
 # ---------------------------------------------------------------- e4m3fn ---
 
 def test_e4m3_roundtrip_of_every_finite_code():
@@ -82,6 +113,25 @@ def test_e4m3_agrees_with_torch_in_range():
     assert np.array_equal(kw.e4m3fn_encode(x), t)
 
 
+# The same for e4m3fn: the binary32 quotient lands on the midpoint of two
+# e4m3fn neighbours (54 between 52 = 0x65 and 56 = 0x66; 50 between 48 = 0x64
+# and 52 = 0x65), the tie goes to the even mantissa, while the exact quotient
+# lies just on the other side of the midpoint.
+E4M3_FP32_TIES = [  # (x, s, binary32 quotient, code, exact quotient's nearest code)
+    (float.fromhex("0x1.15ac06p-1"), float.fromhex("0x1.4917bcp-7"), 54.0, 0x66, 0x65),
+    (float.fromhex("0x1.3176fap+0"), float.fromhex("0x1.86feb0p-6"), 50.0, 0x64, 0x65),
+]
+
+
+def test_e4m3_code_follows_the_binary32_quotient():
+    for x, s, q32, code, exact_code in E4M3_FP32_TIES:
+        exact = _premise(x, s, q32)
+        lo, hi = sorted((e4m3fn_decode(np.array([code], np.uint8))[0], e4m3fn_decode(np.array([exact_code], np.uint8))[0]))
+        assert (lo + hi) / 2 == q32                # the quotient is their midpoint
+        got = int(kw.quantize(np.array([x], np.float32), np.array([s], np.float32), "fp8_e4m3")[0])
+        assert got == code, (x, s, hex(got), hex(code))
+
+
 # --------------------------------------------------------------- scatter ---
 
 def test_scatter_to_hand_placed_slots():
@@ -101,6 +151,38 @@ def test_scatter_to_hand_placed_slots():
         for h in range(H):
             want[page, h, slot, :D] = rows[r, h].astype(np.int8).view(np.uint8)
     assert np.array_equal(out, want)
+
+
+def test_per_head_scales_hand_codes():
+    """Two KV heads with scales 0.5 and 0.25 (PER_HEAD): the same row values
+    give different codes per head.  Head 0: [1, -0.75, 0.25, 63] / 0.5 =
+    [2, -1.5, 0.5, 126] -> [2, -2, 0, 126] (ties to even); head 1:
+    [1, -0.75, 0.25, 63] / 0.25 = [4, -3, 1, 252] -> [4, -3, 1, 127] (clamped).
+    One token at position 2 of a request (P = 4, page 3)."""
+    H, D, P = 2, 4, 4
+    cache = np.zeros((4, H, P, D), np.uint8)
+    row = np.array([[1.0, -0.75, 0.25, 63.0]] * H, np.float32)[None]
+    out = kw.kv_write(cache, row, np.array([0.5, 0.25], np.float32), "head", "i8",
+                      np.array([[3]], np.int32), np.array([2], np.int32), np.array([0, 1], np.int32), P)
+    assert out[3, 0, 2].view(np.int8).tolist() == [2, -2, 0, 126]
+    assert out[3, 1, 2].view(np.int8).tolist() == [4, -3, 1, 127]
+    assert np.count_nonzero(out) == np.count_nonzero(out[3, :, 2])
+
+
+def test_per_channel_scales_hand_codes():
+    """PER_CHANNEL scales [H, D]: channel d of head g divides by s[g, d].
+    Head 0 scales [1, 0.5, 0.25, 2], head 1 [0.1, 4, 1, 0.5] (binary32) on the
+    row [1.5, 1.5, 1.5, 1.5]: head 0 -> [2, 3, 6, 1] (1.5 and 0.75 round to
+    even / nearest), head 1 -> [15, 0, 2, 3] (1.5 / 0.1 = 15.0000002 in
+    binary32, 0.375 -> 0, 1.5 -> 2)."""
+    H, D, P = 2, 4, 4
+    cache = np.zeros((2, H, P, D), np.uint8)
+    sc = np.array([[1.0, 0.5, 0.25, 2.0], [0.1, 4.0, 1.0, 0.5]], np.float32)
+    row = np.full((1, H, D), 1.5, np.float32)
+    out = kw.kv_write(cache, row, sc, "channel", "i8", np.array([[1]], np.int32), np.array([0], np.int32),
+                      np.array([0, 1], np.int32), P)
+    assert out[1, 0, 0].view(np.int8).tolist() == [2, 3, 6, 1]
+    assert out[1, 1, 0].view(np.int8).tolist() == [15, 0, 2, 3]
 
 
 def test_written_rows_decode_back_within_half_a_step():
@@ -161,3 +243,31 @@ def test_planted_off_by_one_slot_is_caught(monkeypatch):
         return real(cache, rows, scale, mode, kv_dtype, table, np.asarray(lens) + 1, cu, P)
     monkeypatch.setattr(kw, "kv_write", shifted)
     assert _fails(test_scatter_to_hand_placed_slots)
+
+
+def test_planted_fp64_ratio_is_caught(monkeypatch):
+    """Dividing in fp64 instead of binary32 changes the int8 codes of the tie
+    pins.  (The e4m3fn encoder takes binary32 input by definition, so there an
+    fp64 quotient is rounded to the binary32 one before encoding.)"""
+    monkeypatch.setattr(kw, "fp32_ratio", lambda x, s: np.asarray(x, np.float32).astype(np.float64) /
+                        np.asarray(s, np.float32).astype(np.float64))
+    assert _fails(test_int8_code_follows_the_binary32_quotient)
+
+
+def test_planted_first_scale_for_every_head_is_caught(monkeypatch):
+    real = kw.scale_table
+    def first_only(scale, mode, H, D):
+        t = real(scale, mode, H, D)
+        return np.broadcast_to(t[:1], t.shape).copy()
+    monkeypatch.setattr(kw, "scale_table", first_only)
+    assert _fails(test_per_head_scales_hand_codes)
+    assert _fails(test_per_channel_scales_hand_codes)
+
+
+def test_planted_per_channel_transposed_is_caught(monkeypatch):
+    real = kw.scale_table
+    def transposed(scale, mode, H, D):
+        t = real(scale, mode, H, D)
+        return t[:, ::-1].copy() if mode == "channel" else t
+    monkeypatch.setattr(kw, "scale_table", transposed)
+    assert _fails(test_per_channel_scales_hand_codes)
