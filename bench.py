@@ -330,7 +330,7 @@ def main():
     roof["merge"] = (("in-kernel (PA_FLAG_FUSED_MERGE)" if fused else
                       "split_kv_merge launch" + (" inside the call (kernel_ms includes it)" if args.balanced else ""))
                      if chunk > 0 else "none")
-    roof["split"] = ("PA_FLAG_BALANCED_SPLIT requested (applied by the MLA and f16-tile append kernels)"
+    roof["split"] = ("PA_FLAG_BALANCED_SPLIT requested (applied by the MLA kernel; the others keep fixed chunks)"
                      if args.balanced and chunk > 0 else "fixed chunks")
     roof["alg_bytes_per_launch"] = alg_bytes
     roof["flops_per_launch"] = flops

@@ -24,10 +24,14 @@
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
  *    Calls are stateless and re-entrant and never synchronize the host.
  *  - All arguments are validated before anything is enqueued: a call that
- *    returns a non-zero status has enqueued nothing.  A kernel launch failure
- *    is reported as PA_ERR_HIP.  The contents of device arrays (lengths, page
- *    ids) are the caller's contract and are not checked: page ids must be valid
- *    for every key j < T_b, entries past ceil(T_b / page_size) are never read.
+ *    returns PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED or
+ *    PA_ERR_WORKSPACE_TOO_SMALL has enqueued nothing.  A kernel launch failure
+ *    is reported as PA_ERR_HIP; a call that enqueues two kernels (attention,
+ *    then split_kv_merge) and fails to launch the second returns PA_ERR_HIP
+ *    with the first already enqueued (the outputs are then undefined).  The
+ *    contents of device arrays (lengths, page ids) are the caller's contract
+ *    and are not checked: page ids must be valid for every key j < T_b,
+ *    entries past ceil(T_b / page_size) are never read.
  *  - pa_last_error() returns a thread-local description of the last failure.
  */
 #ifndef PAGEDATTN_H_
@@ -92,6 +96,20 @@ typedef struct pa_problem {
   float sm_scale;             /* softmax scale on q . k (> 0) */
   int32_t chunk_size;         /* 0: no split-KV; else a multiple of 64 keys */
   int32_t flags;              /* PA_FLAG_* bits, 0 for the default behaviour */
+  /* Schedule overrides.  0 (the value for normal use) lets the library choose;
+   * the other values fix one choice of how the work is laid out on the GPU,
+   * for tuning and for tests that must reach every code path.  They never
+   * change what is computed: outputs stay within the same rounding of the
+   * exact result (decode_waves changes the order of the softmax merge, so the
+   * bits may differ; the other two leave the bits unchanged).  Any other value
+   * is INVALID_ARG. */
+  int32_t decode_waves;       /* 1, 2 or 4: waves that split the keys of one unit of the
+                                 decode kernel (<= 32 packed rows), merged in LDS */
+  int32_t group_order;        /* shared-tile and MLA kernels: 1 = workgroup L takes slot L
+                                 of the (request, KV head, chunk) grid, 2 = only the
+                                 groups that hold work are numbered */
+  int32_t merge_in_kernel;    /* with PA_FLAG_FUSED_MERGE: 1 = the decode kernel merges
+                                 every row tile itself, 2 = never (split_kv_merge runs) */
 } pa_problem;
 
 /* pa_problem.flags bits.
@@ -290,7 +308,7 @@ int32_t paged_kv_write(const pa_problem* prob, int32_t total_new, const void* k_
  *  cu_seqlens_q int32 [B+1], or NULL with q_len_uniform > 0 (token b*q_len + t).
  *  seq_lens_kv  int32 [B] cached tokens L_b.
  *  out          bf16 [total_q, H_q, D_v]; lse fp32 [total_q, H_q] or NULL.
- * D_v must be a multiple of 4 and at most 1024.
+ * D_v must be 64, 128, 256, 512 or 1024 (other values are UNSUPPORTED).
  */
 int32_t split_kv_merge(const float* partial_o, const float* partial_lse,
                        const int32_t* cu_seqlens_q, const int32_t* seq_lens_kv,

@@ -74,7 +74,13 @@ class PaProblem(ctypes.Structure):
         ("sm_scale", ctypes.c_float),
         ("chunk_size", ctypes.c_int32),
         ("flags", ctypes.c_int32),
+        ("decode_waves", ctypes.c_int32),
+        ("group_order", ctypes.c_int32),
+        ("merge_in_kernel", ctypes.c_int32),
     ]
+
+#: Schedule-override fields of ``pa_problem`` (0 = the library's choice).
+SCHEDULE_FIELDS = ("decode_waves", "group_order", "merge_in_kernel")
 
 
 class PagedAttnError(RuntimeError):
@@ -158,8 +164,11 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_problem(**fields) -> PaProblem:
-    """Build a PaProblem from keyword fields (every field but ``flags`` is required)."""
+    """Build a PaProblem from keyword fields (every field but ``flags`` and the
+    schedule overrides, which default to 0, is required)."""
     fields.setdefault("flags", 0)
+    for f in SCHEDULE_FIELDS:
+        fields.setdefault(f, 0)
     names = [f for f, _ in PaProblem._fields_]
     missing = [n for n in names if n not in fields]
     extra = [k for k in fields if k not in names]

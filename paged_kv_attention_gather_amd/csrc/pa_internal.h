@@ -113,9 +113,10 @@ struct AttnConfig {
   bool tree;        // draft-tree mask over the appended keys (decode-path kernels)
 };
 
+// Workgroups of the kernel `cfg` selects that fit on one CU of device `dev` at
+// once (0: unknown); asked once per (device, kernel) and cached.
+int resident_per_cu(const AttnConfig& cfg, int dev);
 // Returns hipSuccess, hipErrorInvalidValue when no specialization matches.
-// Workgroups of the kernel `cfg` selects that fit on one CU at once (0: unknown).
-int resident_per_cu(const AttnConfig& cfg);
 hipError_t launch_attention(const AttnConfig& cfg, const AttnParams& p, dim3 grid,
                             hipStream_t stream);
 hipError_t launch_merge(int dv, const MergeParams& p, int batch, int max_q_len,

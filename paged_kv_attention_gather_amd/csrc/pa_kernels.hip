@@ -26,6 +26,8 @@
 // scales multiply Q, V scales multiply the final O).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -1142,6 +1144,13 @@ __device__ __forceinline__ void merge_if_last(const AttnParams& p, const Unit& u
   if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const bool last = __builtin_amdgcn_readfirstlane(old) == u.n_chunks - 1;
   if (!last) return;
+  // Reader side: an agent-scope acquire orders the partial loads below after
+  // the counter's read-modify-write in the memory model (one unit per row tile
+  // pays for it).  The writer side has no release fence: at agent scope it
+  // would write back the XCD's whole L2 in every unit; the partials are
+  // agent-scope atomic stores instead, each coherent by itself, and the
+  // vmcnt(0) wait above makes them complete before the counter's atomic issues.
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   constexpr int QPR = DV / 4;   // four-channel slots per row
   // chunk slots loaded per round trip: the agent-scope loads are single
@@ -2392,9 +2401,20 @@ hipError_t launch_attention(const AttnConfig& cfg, const AttnParams& p, dim3 gri
   return e->fn(p, grid, stream);
 }
 
-int resident_per_cu(const AttnConfig& cfg) {
+int resident_per_cu(const AttnConfig& cfg, int dev) {
+  constexpr int kMaxDevices = 64;
+  constexpr int kEntries = sizeof(kTable) / sizeof(kTable[0]);
+  static std::atomic<int> cache[kMaxDevices][kEntries];   // value + 1; 0 = not asked yet
   const Entry* e = find_entry(cfg);
-  return e ? e->occ() : 0;
+  if (!e) return 0;
+  if (dev < 0 || dev >= kMaxDevices) return e->occ();
+  std::atomic<int>& slot = cache[dev][e - kTable];
+  int v = slot.load(std::memory_order_relaxed);
+  if (v == 0) {
+    v = e->occ() + 1;   // the occupancy query runs on the current device
+    slot.store(v, std::memory_order_relaxed);
+  }
+  return v - 1;
 }
 
 hipError_t launch_merge(int dv, const MergeParams& p, int batch, int max_q_len,

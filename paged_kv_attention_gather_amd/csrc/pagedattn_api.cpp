@@ -4,11 +4,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
-#include <cstdlib>
 #include <string>
 
 #include "pa_internal.h"
@@ -82,7 +82,35 @@ int32_t check_problem(const pa_problem* p) {
   if (p->chunk_size < 0 || p->chunk_size % kTileKeys != 0)
     return fail(PA_ERR_UNSUPPORTED, "chunk_size %d must be 0 or a positive multiple of %d",
                 p->chunk_size, kTileKeys);
+  if (p->decode_waves != 0 && p->decode_waves != 1 && p->decode_waves != 2 && p->decode_waves != 4)
+    return fail(PA_ERR_INVALID_ARG, "decode_waves %d: 0 (automatic), 1, 2 or 4", p->decode_waves);
+  if (p->group_order < 0 || p->group_order > 2)
+    return fail(PA_ERR_INVALID_ARG, "group_order %d: 0 (automatic), 1 or 2", p->group_order);
+  if (p->merge_in_kernel < 0 || p->merge_in_kernel > 2)
+    return fail(PA_ERR_INVALID_ARG, "merge_in_kernel %d: 0 (automatic), 1 or 2", p->merge_in_kernel);
   return PA_OK;
+}
+
+// Compute units of a device, asked once per device and kept (0: unknown).
+int device_cus(int dev) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  if (dev < 0 || dev >= kMaxDevices) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return 0;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Resident workgroups of the whole device for the kernel `cfg` selects (0: unknown).
+int64_t device_capacity(const pa::AttnConfig& cfg) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const int per_cu = pa::resident_per_cu(cfg, dev);
+  const int cus = device_cus(dev);
+  return (int64_t)per_cu * cus;
 }
 
 int64_t max_chunks_of(const pa_problem* p) {
@@ -95,12 +123,9 @@ int64_t max_chunks_of(const pa_problem* p) {
 // the unit's start-up latency (lengths, page ids, first tile), so a unit is
 // split only when the units cannot fill the 2048 (NT = 1) or 1024 (NT = 2)
 // resident waves, and while every wave keeps at least four tiles.
-// PAGEDATTN_DECODE_WAVES (1, 2 or 4) overrides the choice, for tuning.
+// pa_problem.decode_waves (1, 2 or 4) fixes the choice instead.
 int decode_split_waves(const pa_problem* p, int nt) {
-  if (const char* env = std::getenv("PAGEDATTN_DECODE_WAVES")) {
-    const int v = std::atoi(env);
-    if (v == 1 || v == 2 || v == 4) return v;
-  }
+  if (p->decode_waves != 0) return p->decode_waves;
   const int64_t keys = p->chunk_size > 0 ? p->chunk_size : (int64_t)p->max_kv_len + p->max_q_len;
   const int64_t tiles = ceil_div(keys, 64);
   const int64_t units = (int64_t)p->batch * p->num_kv_heads * max_chunks_of(p);
@@ -271,8 +296,8 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   // split_kv_merge spreads the same work over the chip: measured 364 vs 265 us
   // on the spec-decode workload and 272 vs 199 us on MLA.  Those paths
   // enqueue split_kv_merge as without the flag (same results).
-  // PAGEDATTN_FUSED_MERGE (0 or 1) overrides the choice, for tests and tuning,
-  // within the decode kernel, the one that compiles the merge tail (in the
+  // pa_problem.merge_in_kernel (1 = always, 2 = never) fixes the choice within
+  // the decode kernel, the one that compiles the merge tail (in the
   // shared-tile and MLA kernels it cost SGPR spills in the main loop, and
   // the host never picks the in-kernel merge for their wide tiles).
   bool fused = wl.count_bytes > 0;
@@ -280,8 +305,7 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
     const int64_t unit_rows = std::min<int64_t>(rows_max, 16LL * cfg.nt * (cfg.nstage == 0 ? 1 : cfg.nw));
     const int64_t merge_threads = 64LL * (cfg.nstage == 0 ? 1 : cfg.nw);   // decode: wave 0 merges
     fused = unit_rows * (p->head_dim_v / 4) <= 2 * merge_threads;
-    const char* fm_env = std::getenv("PAGEDATTN_FUSED_MERGE");
-    if (fm_env && (fm_env[0] == '0' || fm_env[0] == '1') && fm_env[1] == 0) fused = fm_env[0] == '1';
+    if (p->merge_in_kernel != 0) fused = p->merge_in_kernel == 1;
     fused = fused && cfg.nstage == 0;
   }
   ap.merge_count = fused ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.count_offset) : nullptr;
@@ -321,17 +345,14 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   // Number only the groups with work when the whole grid is at most two rounds
   // of resident workgroups (then an XCD that drew more workgroups than it has
   // CUs would run a second, mostly idle round); deeper grids balance by dispatch.
-  // PAGEDATTN_COMPACT_GROUPS (0 or 1) overrides the choice, for tuning and tests.
+  // pa_problem.group_order (1 = grid slots, 2 = compact) fixes the choice.
+  // The device's capacity is asked once per device and kernel, then cached.
+  const int64_t capacity = decode_kernel ? 0 : device_capacity(cfg);
   ap.compact_groups = 0;
-  const char* cg_env = std::getenv("PAGEDATTN_COMPACT_GROUPS");
-  if (cg_env && (cg_env[0] == '0' || cg_env[0] == '1') && cg_env[1] == 0) {
-    ap.compact_groups = cg_env[0] == '1';
+  if (p->group_order != 0) {
+    ap.compact_groups = p->group_order == 2;
   } else if (!decode_kernel) {
-    int dev = 0, cus = 0;
-    const int per_cu = pa::resident_per_cu(cfg);
-    if (per_cu > 0 && hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-      ap.compact_groups = (int64_t)grid.x <= 2LL * per_cu * cus;
+    ap.compact_groups = capacity > 0 && (int64_t)grid.x <= 2LL * capacity;
   }
   // Balanced split (PA_FLAG_BALANCED_SPLIT) in the MLA kernel, of which one
   // workgroup fits a CU: a round is coarse there, so items sized on the
@@ -344,16 +365,11 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   // measured 2x slower on the spec-decode workload, 540 vs 271 us), and an
   // unchunked append is faster than either split (187 us; balanced 219 us,
   // fixed 1024-key chunks 246 us).
-  if ((p->flags & PA_FLAG_BALANCED_SPLIT) && p->chunk_size > 0 && cfg.nstage == 1) {
-    int dev = 0, cus = 0;
-    const int per_cu = pa::resident_per_cu(cfg);
-    if (per_cu > 0 && hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0) {
-      ap.balanced = 1;
-      ap.group_cap = (int32_t)std::max<int64_t>(1, (int64_t)per_cu * cus / row_tiles);
-      ap.plan_out = static_cast<int32_t*>(workspace);
-      if (!(cg_env && (cg_env[0] == '0' || cg_env[0] == '1') && cg_env[1] == 0)) ap.compact_groups = 1;
-    }
+  if ((p->flags & PA_FLAG_BALANCED_SPLIT) && p->chunk_size > 0 && cfg.nstage == 1 && capacity > 0) {
+    ap.balanced = 1;
+    ap.group_cap = (int32_t)std::max<int64_t>(1, capacity / row_tiles);
+    ap.plan_out = static_cast<int32_t*>(workspace);
+    if (p->group_order == 0) ap.compact_groups = 1;
   }
   hipError_t e = pa::launch_attention(cfg, ap, grid, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));

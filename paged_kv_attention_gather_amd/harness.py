@@ -42,7 +42,7 @@ class DeviceProblem:
     """Device tensors of a workload plus its outputs and workspace."""
 
     def __init__(self, w, device="cuda", chunk_size=None, decode=None, defer_merge=False, fused_merge=False,
-                 balanced=False):
+                 balanced=False, schedule=None):
         import torch
         self.torch = torch
         self.w = w
@@ -65,6 +65,10 @@ class DeviceProblem:
         flags = ((L.FLAG_DEFER_MERGE if defer_merge else 0) | (L.FLAG_FUSED_MERGE if fused_merge else 0) |
                  (L.FLAG_BALANCED_SPLIT if balanced else 0))
         self.prob = problem_for(w, chunk_size=chunk_size, flags=flags)
+        for k, v in (schedule or {}).items():   # pa_problem schedule overrides
+            if k not in L.SCHEDULE_FIELDS:
+                raise KeyError(k)
+            setattr(self.prob, k, int(v))
         self.total_q = int(w.total_q)
         self.out = torch.empty((self.total_q, w.num_q_heads, w.head_dim_v), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((self.total_q, w.num_q_heads), dtype=torch.float32, device=dev)

@@ -214,17 +214,16 @@ GROUP_NUMBERING_CASES = ["append_zero_len_request", "append_chunked", "spec40_qu
                          "mla_int8_g16_q2"]
 
 
-@pytest.mark.parametrize("compact", ["0", "1"])
+@pytest.mark.parametrize("order", [1, 2])
 @pytest.mark.parametrize("case", GROUP_NUMBERING_CASES)
-def test_group_numbering_parity(case, compact, monkeypatch):
+def test_group_numbering_parity(case, order):
     need_gpu()
-    monkeypatch.setenv("PAGEDATTN_COMPACT_GROUPS", compact)
     w = _edge(case, **EDGE_CASES[case])
-    announce(f"edge case {case} compact_groups={compact}")
-    _, (out, lse) = _run(w)
+    announce(f"edge case {case} group_order={order}")
+    _, (out, lse) = _run(w, schedule={"group_order": order})
     O_ref, lse_ref = oracle.attention(w)
     n = int(w.q_lens.sum())
-    compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what=f"{case} compact={compact}")
+    compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what=f"{case} group_order={order}")
 
 
 # Draft trees (paged_attn_decode_tree): every tree kernel (decode kernel with
@@ -287,7 +286,7 @@ def test_tree_decode_full_spec_workload_sampled():
 
 # Decode units whose key range is split across 2 or 4 waves of a workgroup
 # (states merged in LDS), forced through the tuning override; a request with
-# fewer tiles than waves leaves some waves empty.
+# fewer tiles than waves leaves some waves empty (pa_problem.decode_waves).
 SPLIT_WAVE_CASES = {
     "g4_q1_chunk512": dict(num_q_heads=8, num_kv_heads=2, q_lens=[1, 1, 1], seq_lens_kv=[1000, 64, 2],
                            decode=True, chunk_size=512),
@@ -300,12 +299,11 @@ SPLIT_WAVE_CASES = {
 
 @pytest.mark.parametrize("waves", [2, 4])
 @pytest.mark.parametrize("case", sorted(SPLIT_WAVE_CASES))
-def test_decode_split_waves_parity(case, waves, monkeypatch):
+def test_decode_split_waves_parity(case, waves):
     need_gpu()
-    monkeypatch.setenv("PAGEDATTN_DECODE_WAVES", str(waves))
     w = _edge("split_" + case, **SPLIT_WAVE_CASES[case])
     announce(f"decode split waves={waves} {case}")
-    _, (out, lse) = _run(w)
+    _, (out, lse) = _run(w, schedule={"decode_waves": waves})
     O_ref, lse_ref = oracle.attention(w)
     n = int(w.q_lens.sum())
     compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what=f"{case} waves={waves}")
@@ -368,7 +366,7 @@ def test_split_kv_merge_against_oracle_partials():
 # arithmetic as split_kv_merge, so the outputs must equal the two-launch
 # call's bit for bit.  The library merges in-kernel only where a row tile's
 # merge is one short pass (decode with a few packed rows);
-# PAGEDATTN_FUSED_MERGE=1 forces it for every decode-kernel case (1 and 2 row
+# pa_problem.merge_in_kernel = 1 forces it for every decode-kernel case (1 and 2 row
 # tiles, units split over 2 or 4 waves, empty chunks past the causal bound,
 # page size 16, fp8, a draft tree).  The wider kernels (16-row shared tiles,
 # append, MLA) enqueue split_kv_merge under the flag, which these cases check
@@ -396,10 +394,10 @@ def _counter_words(prob):
     return prob.batch * prob.num_kv_heads * max(1, -(-(prob.max_q_len * G) // 16))
 
 
-def _fused_vs_launch(w, what):
+def _fused_vs_launch(w, what, schedule=None):
     from paged_kv_attention_gather_amd.harness import DeviceProblem
-    ref_dp, ref = _run(w)
-    f = DeviceProblem(w, fused_merge=True)
+    ref_dp, ref = _run(w, schedule={k: v for k, v in (schedule or {}).items() if k != "merge_in_kernel"})
+    f = DeviceProblem(w, fused_merge=True, schedule=schedule)
     n = int(w.q_lens.sum())
     for call in range(2):
         f.out.zero_()
@@ -414,45 +412,41 @@ def _fused_vs_launch(w, what):
 
 
 @pytest.mark.parametrize("case", sorted(FUSED_CASES))
-def test_fused_merge_matches_merge_launch(case, monkeypatch):
+def test_fused_merge_matches_merge_launch(case):
     need_gpu()
-    monkeypatch.setenv("PAGEDATTN_FUSED_MERGE", "1")
     w = _edge(case, **FUSED_CASES[case])
     announce(f"fused merge {case}")
-    _, (out, lse) = _fused_vs_launch(w, case)
+    _, (out, lse) = _fused_vs_launch(w, case, schedule={"merge_in_kernel": 1})
     O_ref, lse_ref = oracle.attention(w)
     n = int(w.q_lens.sum())
     compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what=f"{case} fused")
 
 
 @pytest.mark.parametrize("waves", [2, 4])
-def test_fused_merge_split_waves(waves, monkeypatch):
+def test_fused_merge_split_waves(waves):
     need_gpu()
-    monkeypatch.setenv("PAGEDATTN_DECODE_WAVES", str(waves))
-    monkeypatch.setenv("PAGEDATTN_FUSED_MERGE", "1")
     case = "g4_q1_chunk512"
     w = _edge("split_" + case, **SPLIT_WAVE_CASES[case])
     announce(f"fused merge, decode units over {waves} waves")
-    _fused_vs_launch(w, f"{case} waves={waves}")
+    _fused_vs_launch(w, f"{case} waves={waves}", schedule={"decode_waves": waves, "merge_in_kernel": 1})
 
 
-@pytest.mark.parametrize("force", ["1", "auto"])
-def test_fused_merge_workspace_reuse_shorter_lengths(force, monkeypatch):
+@pytest.mark.parametrize("force", [1, 0])
+def test_fused_merge_workspace_reuse_shorter_lengths(force):
     """A workspace zeroed once serves later calls of the same batch size, head
     counts and max_q_len with other lengths (fewer chunks, fewer tokens, new
     partial values: a merge that read stale partials would fail here).  With
     the automatic choice these single-token decode rows merge in-kernel."""
     need_gpu()
-    if force != "auto":
-        monkeypatch.setenv("PAGEDATTN_FUSED_MERGE", force)
+    sched = {"merge_in_kernel": force}
     from paged_kv_attention_gather_amd.harness import DeviceProblem
     big = _edge("reuse_big", q_lens=[1, 1, 1], seq_lens_kv=[900, 2000, 300], decode=True, chunk_size=128)
     small = _edge("reuse_small", q_lens=[1, 1, 1], seq_lens_kv=[100, 0, 700], decode=True, chunk_size=128)
     announce("fused merge workspace reuse")
-    a = DeviceProblem(big, fused_merge=True)
+    a = DeviceProblem(big, fused_merge=True, schedule=sched)
     a.run()
     a.outputs()
-    b = DeviceProblem(small, fused_merge=True)
+    b = DeviceProblem(small, fused_merge=True, schedule=sched)
     for k in ("max_q_len", "max_kv_len"):
         setattr(b.prob, k, getattr(a.prob, k))
     from paged_kv_attention_gather_amd import _lib as L
@@ -485,13 +479,11 @@ BALANCED_CASES = {
 
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("case", sorted(BALANCED_CASES))
-def test_balanced_split_parity(case, fused, monkeypatch):
+def test_balanced_split_parity(case, fused):
     need_gpu()
-    if fused:
-        monkeypatch.setenv("PAGEDATTN_FUSED_MERGE", "1")
     w = _edge(case, **BALANCED_CASES[case])
     announce(f"balanced split {case} fused={fused}")
-    dp, (out, lse) = _run(w, balanced=True, fused_merge=fused)
+    dp, (out, lse) = _run(w, balanced=True, fused_merge=fused, schedule={"merge_in_kernel": 1} if fused else None)
     O_ref, lse_ref = oracle.attention(w)
     n = int(w.q_lens.sum())
     compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what=f"{case} balanced fused={fused}")
