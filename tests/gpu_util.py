@@ -47,3 +47,53 @@ def token_rows(w, requests):
     for b in requests:
         rows.extend(range(int(w.cu_seqlens_q[b]), int(w.cu_seqlens_q[b + 1])))
     return np.array(rows, dtype=np.int64)
+
+
+# --------------------------------------------------- oracle over every request --
+
+def _oracle_requests(idx, kw, reqs):
+    """Worker: the oracle on the listed requests of config_workload(idx, **kw)
+    (regenerated from its seed in this process)."""
+    import oracle
+    from workloads import config_workload
+    w = config_workload(idx, **kw)
+    O, lse = oracle.attention(w, requests=reqs)
+    rows = token_rows(w, reqs)
+    return rows, O[rows], lse[rows]
+
+
+_ORACLE_CACHE = {}
+
+
+def oracle_every_request(idx, workers=8, **kw):
+    """Oracle outputs of every request of a full-size workload, computed in
+    `workers` CPU processes (spawned fresh: they never touch the GPU), each
+    regenerating the seeded workload and taking every `workers`-th request.
+    Cached per (workload, options) for the session."""
+    key = (idx, tuple(sorted(kw.items())))
+    if key in _ORACLE_CACHE:
+        return _ORACLE_CACHE[key]
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import os
+    from workloads import config_workload
+    w = config_workload(idx, **kw)
+    parts = [list(range(i, w.batch, workers)) for i in range(min(workers, w.batch))]
+    O = np.full((w.total_q, w.num_q_heads, w.head_dim_v), np.nan)
+    lse = np.full((w.total_q, w.num_q_heads), np.nan)
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "2"
+    try:
+        with cf.ProcessPoolExecutor(max_workers=len(parts), mp_context=mp.get_context("spawn")) as ex:
+            for rows, o, l in ex.map(_oracle_requests, [idx] * len(parts), [kw] * len(parts), parts):
+                O[rows], lse[rows] = o, l
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    assert np.isfinite(O).all() and np.isfinite(lse).all(), "oracle left rows unset"
+    _ORACLE_CACHE[key] = (O, lse)
+    return O, lse
