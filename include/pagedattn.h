@@ -290,6 +290,35 @@ int32_t paged_kv_write(const pa_problem* prob, int32_t total_new, const void* k_
                        void* k_cache, void* v_cache, void* stream);
 
 /*
+ * paged_attn_decode_scratch - paged_attn_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *
+ * Same operation, arguments and results as paged_attn_decode, without the
+ * workspace: the split-KV partials (and, with PA_FLAG_FUSED_MERGE, the merge
+ * counters) live in a static device array of PA_DECODE_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends.  The call
+ * allocates nothing (no hipMalloc, no allocating library routine); on the
+ * first call on a device it looks the array's address up once.
+ *   - A problem whose paged_attn_workspace_size(prob, B * q_len) exceeds
+ *     PA_DECODE_SCRATCH_BYTES is PA_ERR_WORKSPACE_TOO_SMALL (checked before
+ *     anything else happens on the GPU).
+ *   - PA_FLAG_DEFER_MERGE is INVALID_ARG: the partials are not reachable by
+ *     the caller.  The merge counters of PA_FLAG_FUSED_MERGE are cleared by
+ *     the call itself (a fill kernel on `stream`).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents: calls that overlap on one GPU (other streams, other
+ *     threads, graph replays in flight together) race and must be ordered by
+ *     the caller.
+ */
+#define PA_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+
+int32_t paged_attn_decode_scratch(const pa_problem* prob, int32_t q_len, const void* q,
+                                  const void* k_cache, const void* v_cache, const float* k_scale,
+                                  const float* v_scale, const int32_t* seq_lens_kv,
+                                  const int32_t* block_table, void* out, float* lse, void* stream);
+
+/*
  * split_kv_merge - log-sum-exp merge of split-KV partials.
  *
  * For every query token t of request b and head h, with C_b = ceil((L_b + n_b)

@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     make_problem,
     paged_attn_append,
     paged_attn_decode,
+    paged_attn_decode_scratch,
     paged_attn_decode_tree,
     paged_kv_write,
     pa_gather_debug,

@@ -33,12 +33,16 @@ FLAG_DEFER_MERGE = 1
 FLAG_FUSED_MERGE = 2
 FLAG_BALANCED_SPLIT = 4
 
+#: Size of the static scratch behind paged_attn_decode_scratch (PA_DECODE_SCRATCH_BYTES).
+DECODE_SCRATCH_BYTES = 32 << 20
+
 #: Every entry point include/pagedattn.h declares.
 EXPORTS = (
     "paged_attn_workspace_size",
     "paged_attn_append",
     "paged_attn_decode",
     "paged_attn_decode_tree",
+    "paged_attn_decode_scratch",
     "paged_kv_write",
     "split_kv_merge",
     "pa_gather_debug",
@@ -114,6 +118,9 @@ def lib() -> ctypes.CDLL:
     L.paged_attn_decode.argtypes = [ctypes.POINTER(PaProblem), _I32, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _P, _P, ctypes.c_size_t, _P]
     L.paged_attn_decode.restype = _I32
+    L.paged_attn_decode_scratch.argtypes = [ctypes.POINTER(PaProblem), _I32, _P, _P, _P, _P, _P, _P, _P,
+                                            _P, _P, _P]
+    L.paged_attn_decode_scratch.restype = _I32
     L.paged_attn_decode_tree.argtypes = [ctypes.POINTER(PaProblem), _I32, _P, _P, _P, _P, _P, _P, _P,
                                          _P, _I32, _P, _P, _P, ctypes.c_size_t, _P]
     L.paged_attn_decode_tree.restype = _I32
@@ -202,6 +209,13 @@ def paged_attn_decode(prob, q_len, q, k_cache, v_cache, k_scale, v_scale, seq_le
         ctypes.byref(prob), int(q_len), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
         _ptr(v_scale), _ptr(seq_lens_kv), _ptr(block_table), _ptr(out), _ptr(lse),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def paged_attn_decode_scratch(prob, q_len, q, k_cache, v_cache, k_scale, v_scale, seq_lens_kv,
+                              block_table, out, lse=None, stream=None) -> None:
+    _check(lib().paged_attn_decode_scratch(
+        ctypes.byref(prob), int(q_len), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+        _ptr(v_scale), _ptr(seq_lens_kv), _ptr(block_table), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def paged_attn_decode_tree(prob, q_len, q, k_cache, v_cache, k_scale, v_scale, seq_lens_kv,

@@ -125,5 +125,12 @@ hipError_t launch_gather(const GatherParams& p, int batch, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteParams& p, bool fp8, bool f32_in, int batch, int max_new,
                            hipStream_t stream);
 bool attention_supported(const AttnConfig& cfg);
+// Device address of the static decode scratch (PA_DECODE_SCRATCH_BYTES) on
+// device `dev`, looked up once per device with that device current; null
+// when the lookup failed (*err then holds the HIP error).
+void* decode_scratch(int dev, hipError_t* err);
+// Sets n int32 words at p to zero with a kernel on `stream` (no memset node,
+// so the call stays safe under graph capture).
+hipError_t launch_zero_words(int32_t* p, int64_t n, hipStream_t stream);
 
 }  // namespace pa

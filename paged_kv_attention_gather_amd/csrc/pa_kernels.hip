@@ -26,7 +26,9 @@
 // scales multiply Q, V scales multiply the final O).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "pa_internal.h"
 
@@ -2444,6 +2446,49 @@ hipError_t launch_merge(int dv, const MergeParams& p, int batch, int max_q_len,
     default:
       return hipErrorInvalidValue;
   }
+}
+
+// ---------------------------------------------------------- decode scratch --
+// The workspace of paged_attn_decode_scratch: one static array per device,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory, so its device address is looked up once per
+// device (hipGetSymbolAddress with that device current) and only that address
+// is ever handed to kernels.
+namespace {
+static __device__ __align__(256) uint8_t scratch[PA_DECODE_SCRATCH_BYTES];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(int32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
+}
+}  // namespace
+
+void* decode_scratch(int dev, hipError_t* err) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  *err = hipSuccess;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
+
+hipError_t launch_zero_words(int32_t* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_gather(const GatherParams& p, int batch, hipStream_t stream) {

@@ -172,7 +172,8 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
                          const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
                          const int32_t* seq_lens_kv, const int32_t* block_table, void* out,
                          float* lse, void* workspace, size_t workspace_bytes, void* stream,
-                         const uint8_t* tree_mask = nullptr, int32_t tree_mask_len = 0) {
+                         const uint8_t* tree_mask = nullptr, int32_t tree_mask_len = 0,
+                         bool clear_counters = false) {
   int32_t st = check_problem(p);
   if (st != PA_OK) return st;
   if (decode) {
@@ -371,6 +372,13 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
     ap.plan_out = static_cast<int32_t*>(workspace);
     if (p->group_order == 0) ap.compact_groups = 1;
   }
+  if (clear_counters && wl.count_bytes > 0) {
+    // a workspace shared across calls (the static scratch): the merge
+    // counters must start at zero whatever the last call left there
+    hipError_t ez = pa::launch_zero_words(reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.count_offset),
+                                          (int64_t)(wl.count_bytes / sizeof(int32_t)), s);
+    if (ez != hipSuccess) return fail(PA_ERR_HIP, "counter clear launch failed: %s", hipGetErrorString(ez));
+  }
   hipError_t e = pa::launch_attention(cfg, ap, grid, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
   if (p->chunk_size > 0 && !(p->flags & PA_FLAG_DEFER_MERGE) && !fused) {
@@ -421,6 +429,32 @@ int32_t paged_attn_decode(const pa_problem* prob, int32_t q_len, const void* q,
   return attention_common(prob, true, q_len, total_q, q, k_cache, v_cache, k_scale, v_scale,
                           nullptr, seq_lens_kv, block_table, out, lse, workspace, workspace_bytes,
                           stream);
+}
+
+int32_t paged_attn_decode_scratch(const pa_problem* prob, int32_t q_len, const void* q,
+                                  const void* k_cache, const void* v_cache, const float* k_scale,
+                                  const float* v_scale, const int32_t* seq_lens_kv,
+                                  const int32_t* block_table, void* out, float* lse, void* stream) {
+  int32_t st = check_problem(prob);
+  if (st != PA_OK) return st;
+  if (prob->flags & PA_FLAG_DEFER_MERGE)
+    return fail(PA_ERR_INVALID_ARG, "PA_FLAG_DEFER_MERGE: the static scratch's partials are not reachable by the caller");
+  if (q_len < 1 || q_len > 64) return fail(PA_ERR_INVALID_ARG, "decode q_len %d not in [1, 64]", q_len);
+  const int64_t total_q = (int64_t)prob->batch * q_len;
+  const size_t need = workspace_layout(prob, total_q).total;
+  if (need > PA_DECODE_SCRATCH_BYTES)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "this problem needs %zu bytes of split-KV workspace; the static scratch holds %zu",
+                need, (size_t)PA_DECODE_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) ws = pa::decode_scratch(dev, &e);
+    if (!ws) return fail(PA_ERR_HIP, "static scratch lookup failed: %s", hipGetErrorString(e));
+  }
+  return attention_common(prob, true, q_len, total_q, q, k_cache, v_cache, k_scale, v_scale, nullptr,
+                          seq_lens_kv, block_table, out, lse, ws, ws ? (size_t)PA_DECODE_SCRATCH_BYTES : 0, stream,
+                          nullptr, 0, /*clear_counters=*/true);
 }
 
 int32_t paged_attn_decode_tree(const pa_problem* prob, int32_t q_len, const void* q,

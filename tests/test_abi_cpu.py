@@ -139,6 +139,9 @@ def _append(prob, total_q=8, workspace=None, ws_bytes=0, **ptrs):
     (dict(flags=8), L.PA_ERR_INVALID_ARG),                        # unknown flag bit
     (dict(flags=3), L.PA_ERR_INVALID_ARG),                        # deferred and fused merge together
     (dict(flags=5), L.PA_ERR_INVALID_ARG),                        # deferred merge of a balanced split
+    (dict(decode_waves=3), L.PA_ERR_INVALID_ARG),                 # schedule overrides: 0 or a listed value
+    (dict(group_order=3), L.PA_ERR_INVALID_ARG),
+    (dict(merge_in_kernel=-1), L.PA_ERR_INVALID_ARG),
 ])
 def test_invalid_problems_are_rejected(lib, over, status):
     assert _decode(base_problem(**over)) == status
@@ -269,3 +272,33 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120, cwd=root)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and not r.stdout.strip()
+
+
+def _decode_scratch(prob, q_len=1, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, lens=FAKE, table=FAKE, out=FAKE, lse=None)
+    p.update(ptrs)
+    return L.lib().paged_attn_decode_scratch(ctypes.byref(prob), q_len, p["q"], p["k"], p["v"], p["ks"],
+                                             p["vs"], p["lens"], p["table"], p["out"], p["lse"], None)
+
+
+def test_decode_scratch_validation(lib):
+    """The allocation-free decode entry point rejects, before touching the GPU,
+    a problem whose split-KV workspace exceeds its static scratch, a deferred
+    merge (its partials are unreachable) and the usual invalid problems."""
+    assert L.DECODE_SCRATCH_BYTES == 32 << 20
+    header = open(HEADER).read()
+    assert "#define PA_DECODE_SCRATCH_BYTES ((size_t)32 << 20)" in header
+    # 64 requests x 32 heads x 128 dims x 9 chunks of fp32 partials: ~9.4 MB, fits;
+    # the same with 64-key chunks over 65536 cached keys does not
+    fits = base_problem(batch=64, num_q_heads=32, num_kv_heads=8, max_q_len=1, max_kv_len=4096,
+                        q_row_stride=32 * 128, chunk_size=512)
+    assert P.workspace_size(fits, 64) <= L.DECODE_SCRATCH_BYTES
+    big = base_problem(batch=64, num_q_heads=32, num_kv_heads=8, max_q_len=1, max_kv_len=65536,
+                       q_row_stride=32 * 128, chunk_size=64, max_pages_per_seq=1025)
+    assert P.workspace_size(big, 64) > L.DECODE_SCRATCH_BYTES
+    assert _decode_scratch(big) == L.PA_ERR_WORKSPACE_TOO_SMALL
+    assert "static scratch" in lib.pa_last_error().decode()
+    assert _decode_scratch(base_problem(flags=L.FLAG_DEFER_MERGE)) == L.PA_ERR_INVALID_ARG
+    assert _decode_scratch(base_problem(num_kv_heads=3)) == L.PA_ERR_INVALID_ARG
+    assert _decode_scratch(base_problem(), q_len=0) == L.PA_ERR_INVALID_ARG
+    assert _decode_scratch(base_problem(batch=0)) == L.PA_OK     # nothing to do, nothing touched
