@@ -6,8 +6,8 @@ batch of the synthetic workload, inputs resident in HBM.  Before every timed
 step the L2 and the 256 MB last-level cache are flushed (outside the events)
 by READING a 1 GiB buffer, so the KV bytes really come from HBM and no dirty
 flush data is left to be written back while the step runs (a write-based
-flush costs a read kernel about a third of its bandwidth).  The default workload is the int8 decode
-case (B=64, q_len 1, 32/8 heads, D=128, page 64, KV lens U[512, 4096],
+flush costs a read kernel about a third of its bandwidth).  The default
+workload is the int8 decode case (B=64, q_len 1, 32/8 heads, D=128, page 64, KV lens U[512, 4096],
 per-channel scales, chunk 512): the one the decode KV-bandwidth metric is
 quoted on.  --config 1..5 selects another workload.
 
@@ -16,13 +16,19 @@ kernel and the oracle's throughput on a bounded sample of the same workload
 (cpu_baseline).  A split-KV step makes the ABI call with PA_FLAG_DEFER_MERGE
 and then runs split_kv_merge, with HIP events on the launch stream before,
 between and after, so the attention kernel is timed on its own and a step is
-still the whole path.  --merge fused makes one call with PA_FLAG_FUSED_MERGE
-instead (where the library merges inside the attention kernel, the step is
-one launch; it measured slower on these workloads, so it is not the
-default).  The
-roofline's "traffic" (HBM bytes per launch of the attention kernel) comes from
-the FETCH_SIZE / WRITE_SIZE counter summary committed in profiles/, and is
-null when that summary was taken on other kernel sources.
+still the whole path.  roofline.frac is the attention kernel's (algorithmic
+bytes or flops over its event time); roofline.step_frac is the whole step's
+(attention + merge).  For the decode workloads the line also carries the
+read probe (pa_kv_read_probe: the same tiles through the same loader with no
+arithmetic), the read bandwidth this access pattern allows.  The default run
+also times the append, spec-decode and MLA workloads ("configs", fewer steps,
+same flush and events).  --merge fused makes one call with
+PA_FLAG_FUSED_MERGE instead (where the library merges inside the attention
+kernel, the step is one launch; it measured slower on these workloads, so it
+is not the default).  The roofline's "traffic" (HBM bytes per launch of the
+attention kernel) comes from the FETCH_SIZE / WRITE_SIZE counter summary
+committed in profiles/, and is null when that summary was taken on other
+kernel sources.
 """
 import argparse
 import json
@@ -225,6 +231,9 @@ def main():
     ap.add_argument("--balanced", action="store_true",
                     help="PA_FLAG_BALANCED_SPLIT: KV items sized on the device to fill one round "
                          "(chunk_size, or --chunk, is then the shortest item)")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="with the default workload, skip timing the append, spec-decode and MLA workloads")
+    ap.add_argument("--no-probe", action="store_true", help="skip the read probe of the decode workloads")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -248,8 +257,6 @@ def main():
         sys.exit(2)
 
     import torch
-    from paged_kv_attention_gather_amd import _lib as L
-    from paged_kv_attention_gather_amd.harness import DeviceProblem
     from workloads import config_workload
 
     if args.kv_write:
@@ -265,58 +272,18 @@ def main():
         # a balanced split's chunks are not split_kv_merge's: the call merges
         # itself, so the step is timed whole (attention kernel + merge)
         print("[bench] --balanced: the merge runs inside the ABI call", file=sys.stderr, flush=True)
-    dp = DeviceProblem(w, chunk_size=args.chunk, defer_merge=not fused and not args.balanced,
-                       fused_merge=fused, balanced=args.balanced)
-    chunk = dp.prob.chunk_size
+    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB, read before every timed step
+    m = measure(w, args.config, flush, args.steps, args.warmup, chunk=args.chunk, fused=fused,
+                balanced=args.balanced, no_flush=args.no_flush)
+    dp, chunk = m["dp"], m["chunk"]
     kv_bytes, alg_bytes, flops = work_figures(w)
-    stream = torch.cuda.current_stream()
-    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB
-
-    def do_flush():
-        if not args.no_flush:
-            flush.max()  # read-only pass over 1 GiB
-
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    separate = not fused and not args.balanced   # merge launched here, timed apart
-    for _ in range(args.warmup):
-        do_flush()
-        dp.run()
-        if separate:
-            dp.merge()
-    torch.cuda.synchronize()
-
-    # Timed steps: [flush] e0 attention e1 merge e2, all on the launch stream
-    # (with the fused merge e1 and e2 enclose nothing).
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t_wall0 = time.perf_counter()
-    for i in range(args.steps):
-        do_flush()
-        ev[i][0].record(stream)
-        dp.run()
-        ev[i][1].record(stream)
-        if separate:
-            dp.merge()
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall0
-    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
-    attn_list = [e[0].elapsed_time(e[1]) for e in ev]
-    ms = float(np.mean(step_ms))
-    attn_ms = float(np.mean(attn_list))
-    merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if chunk > 0 and separate else 0.0
+    ms, attn_ms = m["step_ms"], m["attn_ms"]
 
     if args.config in (1, 3):
         value, unit = flops / (ms * 1e-3) / 1e12, "TFLOP/s"
     else:
         value, unit = kv_bytes / (ms * 1e-3) / 1e9, "GB/s"
-    if args.config in (3, 5):
-        achieved = flops / (attn_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_F16_PEAK_TFS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFS, 4)}
-    else:
-        achieved = alg_bytes / (attn_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof = roofline(args.config, w, attn_ms, ms)
     traffic, note = ((None, "no counters for the draft-tree kernels") if args.tree
                      else hbm_traffic(args.config, chunk, args.merge, args.balanced))
     roof["traffic"] = traffic
@@ -325,8 +292,8 @@ def main():
     roof["traffic_source"] = note
     roof["kernel"] = kernel_name(dp)
     roof["kernel_ms"] = round(attn_ms, 5)
-    roof["kernel_min_ms"] = round(float(np.min(attn_list)), 5)
-    roof["merge_ms"] = round(merge_ms, 5)
+    roof["kernel_min_ms"] = round(m["attn_min_ms"], 5)
+    roof["merge_ms"] = round(m["merge_ms"], 5)
     roof["merge"] = (("in-kernel (PA_FLAG_FUSED_MERGE)" if fused else
                       "split_kv_merge launch" + (" inside the call (kernel_ms includes it)" if args.balanced else ""))
                      if chunk > 0 else "none")
@@ -334,6 +301,14 @@ def main():
                      if args.balanced and chunk > 0 else "fixed chunks")
     roof["alg_bytes_per_launch"] = alg_bytes
     roof["flops_per_launch"] = flops
+    if not args.no_probe and args.config in (2, 4) and not args.tree:
+        pr = read_probe(dp, flush, args.steps, args.warmup, args.no_flush)
+        roof["probe_gbs"] = round(kv_bytes / (pr * 1e-3) / 1e9, 1)
+        roof["probe_ms"] = round(pr, 5)
+        roof["probe_frac"] = round(roof["probe_gbs"] / HBM_PEAK_GBS, 4)
+        roof["kernel_over_probe"] = round(pr / attn_ms, 4)
+        roof["probe"] = ("pa_kv_read_probe: the decode kernel's tile loader over the same units and KV bytes, "
+                         "no arithmetic (read ceiling of this access pattern)")
 
     line = {
         "metric": "decode: KV GB/s & %HBM peak; append: attention TFLOP/s & %MFMA peak",
@@ -345,14 +320,140 @@ def main():
                    "global_batch": int(w.batch),
                    "kv_dtype": w.kv_dtype, "chunk_size": int(chunk), "cache_flush": not args.no_flush,
                    "kv_bytes": kv_bytes, "alg_bytes": alg_bytes, "flops": flops,
-                   "min_ms": round(float(np.min(step_ms)), 5),
-                   "wall_ms_per_step_incl_flush": round(t_wall / args.steps * 1e3, 4)},
+                   "min_ms": round(m["step_min_ms"], 5),
+                   "wall_ms_per_step_incl_flush": round(m["wall_ms"], 4)},
         "roofline": roof,
     }
+    del m, dp
+    if not args.no_extra_configs and args.config == 2 and not args.tree and not fused and not args.balanced \
+            and args.chunk is None:
+        line["configs"] = other_configs(flush, args)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_budget)
     print(json.dumps(line), flush=True)
+
+
+def measure(w, config, flush, steps, warmup, chunk=None, fused=False, balanced=False, no_flush=False):
+    """Time `steps` calls of the workload after `warmup` untimed ones.  Per
+    step: [flush] e0 attention e1 merge e2 on the launch stream (torch's
+    current stream, which the binding passes to the library); with the fused
+    or balanced merge e1..e2 encloses nothing."""
+    import torch
+    from paged_kv_attention_gather_amd.harness import DeviceProblem
+    dp = DeviceProblem(w, chunk_size=chunk, defer_merge=not fused and not balanced,
+                       fused_merge=fused, balanced=balanced)
+    chunk = dp.prob.chunk_size
+    stream = torch.cuda.current_stream()
+    separate = not fused and not balanced   # merge launched here, timed apart
+    print(f"[bench] {w.name}: warmup {warmup}", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        if not no_flush:
+            flush.max()   # read-only pass over 1 GiB
+        dp.run()
+        if separate:
+            dp.merge()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t_wall0 = time.perf_counter()
+    for i in range(steps):
+        if not no_flush:
+            flush.max()
+        ev[i][0].record(stream)
+        dp.run()
+        ev[i][1].record(stream)
+        if separate:
+            dp.merge()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    step = [e[0].elapsed_time(e[2]) for e in ev]
+    attn = [e[0].elapsed_time(e[1]) for e in ev]
+    merge = [e[1].elapsed_time(e[2]) for e in ev] if chunk > 0 and separate else [0.0]
+    print(f"[bench] {w.name}: step {np.mean(step) * 1e3:.1f} us, attention {np.mean(attn) * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+    return {"dp": dp, "chunk": int(chunk), "step_ms": float(np.mean(step)), "step_min_ms": float(np.min(step)),
+            "attn_ms": float(np.mean(attn)), "attn_min_ms": float(np.min(attn)), "merge_ms": float(np.mean(merge)),
+            "wall_ms": t_wall / steps * 1e3}
+
+
+def roofline(config, w, attn_ms, step_ms):
+    """Roofline of the dominant (attention) kernel: algorithmic bytes (decode)
+    or flops (append, MLA) per launch over its event time; the same over the
+    whole step (attention + split-KV merge) as step_achieved / step_frac."""
+    _, alg_bytes, flops = work_figures(w)
+    if config in (3, 5):
+        a, st = flops / (attn_ms * 1e-3) / 1e12, flops / (step_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(a, 3), "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(a / MFMA_F16_PEAK_TFS, 4), "step_achieved": round(st, 3),
+                "step_frac": round(st / MFMA_F16_PEAK_TFS, 4)}
+    a, st = alg_bytes / (attn_ms * 1e-3) / 1e9, alg_bytes / (step_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(a / HBM_PEAK_GBS, 4), "step_achieved": round(st, 1), "step_frac": round(st / HBM_PEAK_GBS, 4)}
+
+
+def read_probe(dp, flush, steps, warmup, no_flush=False):
+    """Mean event time (ms) of pa_kv_read_probe over the problem's units,
+    flushed like the attention steps."""
+    import torch
+    import paged_kv_attention_gather_amd as P
+    w = dp.w
+    C = int(dp.prob.chunk_size)
+    mc = max(1, -(-(int(dp.prob.max_kv_len) + int(dp.prob.max_q_len)) // C)) if C > 0 else 1
+    sink = torch.zeros(mc * w.batch * w.num_kv_heads, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        P.pa_kv_read_probe(dp.prob, int(w.decode_q_len), dp.k_cache, dp.v_cache, dp.seq_lens_kv, dp.block_table,
+                           sink)
+
+    for _ in range(warmup):
+        if not no_flush:
+            flush.max()
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        if not no_flush:
+            flush.max()
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+
+
+def other_configs(flush, args):
+    """The append, spec-decode and MLA workloads measured in the same run with
+    the same flush and events (fewer steps): kernel and step times, roofline
+    fractions, and the HBM traffic ratio where committed counters cover the
+    kernel sources."""
+    import torch
+    from workloads import config_workload
+    out = {}
+    for idx in (3, 4, 5):
+        print(f"[bench] generating workload {idx}", file=sys.stderr, flush=True)
+        w = config_workload(idx)
+        m = measure(w, idx, flush, max(5, args.steps // 2), max(2, args.warmup // 2), no_flush=args.no_flush)
+        kv_bytes, alg_bytes, flops = work_figures(w)
+        r = roofline(idx, w, m["attn_ms"], m["step_ms"])
+        row = {"workload": WORKLOAD_TEXT[idx], "kernel": kernel_name(m["dp"]), "dtype": compute_dtype(m["dp"]),
+               "chunk_size": m["chunk"], "kernel_ms": round(m["attn_ms"], 5), "merge_ms": round(m["merge_ms"], 5),
+               "step_ms": round(m["step_ms"], 5), "kv_gbs": round(kv_bytes / (m["step_ms"] * 1e-3) / 1e9, 1),
+               "flops": flops, "alg_bytes": alg_bytes, "roofline": r}
+        if idx in (3, 5):
+            row["tflops"] = round(flops / (m["step_ms"] * 1e-3) / 1e12, 3)
+        traffic, note = hbm_traffic(idx, m["chunk"], "separate")
+        row["traffic_over_alg_bytes"] = round(traffic / alg_bytes, 4) if traffic else None
+        row["traffic_source"] = note
+        if idx == 4 and not args.no_probe:
+            pr = read_probe(m["dp"], flush, max(5, args.steps // 2), 2, args.no_flush)
+            row["probe_gbs"] = round(kv_bytes / (pr * 1e-3) / 1e9, 1)
+        out[str(idx)] = row
+        del m
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":

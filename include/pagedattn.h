@@ -348,15 +348,52 @@ int32_t split_kv_merge(const float* partial_o, const float* partial_lse,
 /*
  * pa_gather_debug - raw-byte page gather (test aid).
  *
- * Copies the K rows of keys 0..T_b-1 of every request and KV head, in key
- * order, to dst [B, H_kv, t_max, D_qk] bytes (rows past T_b are left as they
- * are), using the same page-address function as the attention kernels
- * (FlashInfer persistent.cuh prefetch_offest; XQA KVTilePartLoader::loadPages).
- * T_b = seq_lens_kv[b] + q_lens[b]; q_lens int32 [B]; t_max >= max_b T_b.
+ * Copies the K rows (and V rows when v_dst is not NULL) of keys 0..T_b-1 of
+ * every request and KV head, in key order, to k_dst [B, H_kv, t_max, D_qk]
+ * and v_dst [B, H_kv, t_max, D_v] bytes (rows past T_b are left as they
+ * are).  T_b = seq_lens_kv[b] + q_lens[b]; q_lens int32 [B]; t_max >= max_b T_b.
+ * `loader` picks the code that computes the addresses (key j -> page
+ * block_table[b][j / P], slot j % P, as in FlashInfer persistent.cuh
+ * prefetch_offest and XQA KVTilePartLoader::loadPages):
+ *   PA_GATHER_ROWS        one key row at a time through the kernels' page
+ *                         and row address functions;
+ *   PA_GATHER_DECODE      the decode kernel's register tile loader (64-key
+ *                         tiles, one-page fast path, clamped last tile), over
+ *                         units of prob->chunk_size keys (whole sequences when
+ *                         0); head dims 64 or 128 with D_qk == D_v;
+ *   PA_GATHER_DMA_4W      the shared-tile / append / MLA kernels' LDS-DMA tile
+ *   PA_GATHER_DMA_3W      loader with 4 or 3 waves splitting each tile, over
+ *                         the same units; head dims 64/128 (D_qk == D_v) or,
+ *                         with 4 waves, the shared 576/512 layout (V is then
+ *                         the K prefix: v_dst must be NULL).
+ * Other combinations are UNSUPPORTED.
  */
-int32_t pa_gather_debug(const pa_problem* prob, const void* k_cache, const int32_t* block_table,
-                        const int32_t* seq_lens_kv, const int32_t* q_lens, int32_t t_max,
-                        uint8_t* dst, void* stream);
+enum {
+  PA_GATHER_ROWS = 0,
+  PA_GATHER_DECODE = 1,
+  PA_GATHER_DMA_4W = 2,
+  PA_GATHER_DMA_3W = 3
+};
+
+int32_t pa_gather_debug(const pa_problem* prob, int32_t loader, const void* k_cache, const void* v_cache,
+                        const int32_t* block_table, const int32_t* seq_lens_kv, const int32_t* q_lens,
+                        int32_t t_max, uint8_t* k_dst, uint8_t* v_dst, void* stream);
+
+/*
+ * pa_kv_read_probe - the decode kernel's KV reads alone (measurement aid).
+ *
+ * Walks the units of paged_attn_decode (request, KV head, chunk of
+ * prob->chunk_size keys; whole sequences when 0) with q_len tokens per
+ * request and reads every K/V byte the attention kernel reads, through the
+ * same tile loader, with no arithmetic on them but an xor folded into
+ * sink[c * B * H_kv + b * H_kv + g] (device uint32 [C_max * B * H_kv],
+ * C_max as in paged_attn_workspace_size).  Its time over the KV bytes is the
+ * read bandwidth the decode access pattern allows.  Head dims 64 or 128 with
+ * D_qk == D_v; other problems are UNSUPPORTED.
+ */
+int32_t pa_kv_read_probe(const pa_problem* prob, int32_t q_len, const void* k_cache, const void* v_cache,
+                         const int32_t* seq_lens_kv, const int32_t* block_table, uint32_t* sink,
+                         void* stream);
 
 /* Human-readable name of a status code. */
 const char* pa_status_string(int32_t status);

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     paged_attn_decode_tree,
     paged_kv_write,
     pa_gather_debug,
+    pa_kv_read_probe,
     split_kv_merge,
     workspace_size,
 )

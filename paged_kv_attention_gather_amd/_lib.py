@@ -33,6 +33,11 @@ FLAG_DEFER_MERGE = 1
 FLAG_FUSED_MERGE = 2
 FLAG_BALANCED_SPLIT = 4
 
+GATHER_ROWS = 0       # one key row at a time
+GATHER_DECODE = 1     # the decode kernel's register tile loader
+GATHER_DMA_4W = 2     # the LDS-DMA tile loader, 4 waves
+GATHER_DMA_3W = 3     # the LDS-DMA tile loader, 3 waves
+
 #: Size of the static scratch behind paged_attn_decode_scratch (PA_DECODE_SCRATCH_BYTES).
 DECODE_SCRATCH_BYTES = 32 << 20
 
@@ -46,6 +51,7 @@ EXPORTS = (
     "paged_kv_write",
     "split_kv_merge",
     "pa_gather_debug",
+    "pa_kv_read_probe",
     "pa_status_string",
     "pa_last_error",
 )
@@ -129,7 +135,9 @@ def lib() -> ctypes.CDLL:
     L.split_kv_merge.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                  _P, _P, _P]
     L.split_kv_merge.restype = _I32
-    L.pa_gather_debug.argtypes = [ctypes.POINTER(PaProblem), _P, _P, _P, _P, _I32, _P, _P]
+    L.pa_gather_debug.argtypes = [ctypes.POINTER(PaProblem), _I32, _P, _P, _P, _P, _P, _I32, _P, _P, _P]
+    L.pa_kv_read_probe.argtypes = [ctypes.POINTER(PaProblem), _I32, _P, _P, _P, _P, _P, _P]
+    L.pa_kv_read_probe.restype = _I32
     L.pa_gather_debug.restype = _I32
     L.pa_status_string.argtypes = [_I32]
     L.pa_status_string.restype = ctypes.c_char_p
@@ -244,8 +252,14 @@ def split_kv_merge(partial_o, partial_lse, cu_seqlens_q, seq_lens_kv, q_len_unif
         int(head_dim_v), int(chunk_size), int(max_chunks), _ptr(out), _ptr(lse), _stream(stream)))
 
 
-def pa_gather_debug(prob, k_cache, block_table, seq_lens_kv, q_lens, t_max, dst,
-                    stream=None) -> None:
+def pa_gather_debug(prob, k_cache, block_table, seq_lens_kv, q_lens, t_max, dst, stream=None,
+                    loader=0, v_cache=None, v_dst=None) -> None:
     _check(lib().pa_gather_debug(
-        ctypes.byref(prob), _ptr(k_cache), _ptr(block_table), _ptr(seq_lens_kv), _ptr(q_lens),
-        int(t_max), _ptr(dst), _stream(stream)))
+        ctypes.byref(prob), int(loader), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens_kv),
+        _ptr(q_lens), int(t_max), _ptr(dst), _ptr(v_dst), _stream(stream)))
+
+
+def pa_kv_read_probe(prob, q_len, k_cache, v_cache, seq_lens_kv, block_table, sink, stream=None) -> None:
+    _check(lib().pa_kv_read_probe(
+        ctypes.byref(prob), int(q_len), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens_kv), _ptr(block_table),
+        _ptr(sink), _stream(stream)))

@@ -83,6 +83,20 @@ struct GatherParams {
   int32_t t_max;
 };
 
+// The debug gather through an attention kernel's tile loader, and the read
+// probe: units (request, KV head, chunk) over keys [c * chunk, min(T_b,
+// (c + 1) * chunk)) with T_b = seq_lens_kv[b] + q_lens[b] (q_len_uniform when
+// q_lens is null); grid (B * H_kv, 1, C_max).
+struct TileWalkParams {
+  AttnParams a;                 // cache pointers, strides, block table, page shift
+  const int32_t* q_lens;        // [B] or null (a.q_len_uniform)
+  uint8_t* k_dst;               // gather: [B, H_kv, t_max, D_qk] or null
+  uint8_t* v_dst;               // gather: [B, H_kv, t_max, D_v] or null
+  uint32_t* sink;               // probe: [B * H_kv * C_max] xor of the bytes read
+  int32_t t_max;
+  int32_t chunk;                // keys per unit (> 0)
+};
+
 // One launch of the KV-cache append write (kv_write.hip).  Grid (token
 // slices of tokens_per_block, B); dv = 0 writes K rows only (shared layout).
 struct KvWriteParams {
@@ -122,6 +136,15 @@ hipError_t launch_attention(const AttnConfig& cfg, const AttnParams& p, dim3 gri
 hipError_t launch_merge(int dv, const MergeParams& p, int batch, int max_q_len,
                         hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, int batch, hipStream_t stream);
+// Debug gather through the decode kernel's register loader (loader 1) or the
+// shared-tile / MLA kernels' LDS-DMA loader with 4 or 3 waves (loader 2, 3);
+// head dims as in the problem.  hipErrorInvalidValue for other geometries.
+hipError_t launch_tile_gather(int loader, int dqk, int dv, bool shared_kv, const TileWalkParams& p, int batch,
+                              int num_kv_heads, int max_chunks, hipStream_t stream);
+// The read probe: every unit's K/V tiles through the decode kernel's loader,
+// no arithmetic on them but an xor into the sink (head dims 64 or 128).
+hipError_t launch_read_probe(int d, const TileWalkParams& p, int batch, int num_kv_heads, int max_chunks,
+                             hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteParams& p, bool fp8, bool f32_in, int batch, int max_new,
                            hipStream_t stream);
 bool attention_supported(const AttnConfig& cfg);

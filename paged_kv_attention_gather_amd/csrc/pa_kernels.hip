@@ -1218,6 +1218,127 @@ __device__ __forceinline__ void merge_if_last(const AttnParams& p, const Unit& u
   }
 }
 
+// DmaTileLoader: the shared-tile and MLA kernels' loader.  A 64-key tile
+// (K rows of KROW bytes, then V rows of VROW bytes unless V is the prefix of
+// the K row) travels by LDS DMA (global_load_lds_dwordx4, 16 bytes per lane)
+// into one LDS stage, its 16-byte chunks XOR-swizzled per row (swz).  The NW
+// waves of a workgroup split the tile's 1 KB blocks: block j*NW + wave of K,
+// then of V.  Page ids, the one-page fast path and the clamped general path
+// are as in RegTileLoader.
+template <int KROW, int VROW, int NW, bool SHARED>
+struct DmaTileLoader {
+  static constexpr int KTILE = TK * KROW;
+  static constexpr int VTILE = SHARED ? 0 : TK * VROW;
+  static constexpr int STAGE = KTILE + VTILE;
+  static constexpr int KCH = KTILE / 16;                 // 16-byte chunks per K tile
+  static constexpr int VCH = VTILE / 16;
+  static constexpr int KCPR = KROW / 16;                 // chunks per K row
+  static constexpr int VCPR = VROW / 16;
+  static constexpr int K_DMA = (KCH + 64 * NW - 1) / (64 * NW);   // DMA instructions per wave (at most)
+  static constexpr int V_DMA = (VCH + 64 * NW - 1) / (64 * NW);
+  const int32_t* table_row;
+  int g, wave, kv_lo, key_end, last_page, page_shift;
+  int pw_base, pw_val;
+  bool one_page, fast_addr;
+  uint32_t smem_base;
+  uint32_t koff[K_DMA], voff[V_DMA > 0 ? V_DMA : 1];
+
+  __device__ __forceinline__ void init(const AttnParams& p, int b, int g_, int wave_, int kv_lo_, int key_end_,
+                                       int n_tiles, int lane, uint32_t smem_base_) {
+    table_row = p.block_table + (int64_t)b * p.max_pages_per_seq;
+    g = g_;
+    wave = wave_;
+    kv_lo = kv_lo_;
+    key_end = key_end_;
+    page_shift = p.page_shift;
+    last_page = n_tiles > 0 ? (key_end - 1) >> page_shift : 0;   // never read past it
+    pw_base = -(1 << 30);
+    pw_val = 0;
+    one_page = page_shift >= 6;
+    fast_addr = one_page && (int64_t)TK * p.k_stride_token < (1LL << 30) &&
+                (SHARED || (int64_t)TK * p.v_stride_token < (1LL << 30));
+    smem_base = smem_base_;
+#pragma unroll
+    for (int j = 0; j < K_DMA; ++j) {
+      const int ch = (j * NW + wave) * 64 + lane;
+      const int row = ch / KCPR;
+      koff[j] = (uint32_t)(row * p.k_stride_token + swz<KROW>(ch % KCPR, row) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < V_DMA; ++j) {
+      const int ch = (j * NW + wave) * 64 + lane;
+      const int row = ch / VCPR;
+      voff[j] = (uint32_t)(row * p.v_stride_token + swz<VROW>(ch % VCPR, row) * 16);
+    }
+  }
+
+  // Issues this wave's share of tile `tile` into LDS stage `stage`.
+  __device__ __forceinline__ void issue(const AttnParams& p, int tile, int stage) {
+    const int kbase = kv_lo + tile * TK;
+    const int pg0 = kbase >> page_shift;
+    const int pg_last = min(pg0 + 3, last_page);
+    if (pg0 < pw_base || pg_last > pw_base + 63) {
+      // Refill the window (drains the DMA queue; once per 64 pages).
+      pw_base = pg0;
+      pw_val = load_i32_sync(table_row + min(pg0 + (int)(threadIdx.x & 63), last_page));
+    }
+    const int pp0 = __builtin_amdgcn_readlane(pw_val, pg0 - pw_base);
+    const uint32_t kdst = smem_base + stage * STAGE;
+    const uint32_t vdst = kdst + KTILE;
+    if (fast_addr && kbase + TK <= key_end) {
+      const uint8_t* kb = paged_row(p.k_cache, pp0, kbase, page_shift, g, p.k_stride_page, p.k_stride_head,
+                                    p.k_stride_token);
+#pragma unroll
+      for (int j = 0; j < K_DMA; ++j)
+        if ((j * NW + wave) * 64 < KCH) dma16_s(koff[j], kb, kdst + (j * NW + wave) * 1024);
+      if constexpr (!SHARED) {
+        const uint8_t* vb = paged_row(p.v_cache, pp0, kbase, page_shift, g, p.v_stride_page, p.v_stride_head,
+                                      p.v_stride_token);
+#pragma unroll
+        for (int j = 0; j < V_DMA; ++j)
+          if ((j * NW + wave) * 64 < VCH) dma16_s(voff[j], vb, vdst + (j * NW + wave) * 1024);
+      }
+      return;
+    }
+    // general path: up to four pages per tile (page_size >= 16), clamped rows
+    int pp1 = pp0, pp2 = pp0, pp3 = pp0;
+    if (!one_page) {
+      pp1 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 1, pg_last) - pw_base);
+      pp2 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 2, pg_last) - pw_base);
+      pp3 = __builtin_amdgcn_readlane(pw_val, pg_last - pw_base);
+    }
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < K_DMA; ++j) {
+      const int blk = j * NW + wave;
+      if (blk * 64 < KCH) {
+        const int ch = blk * 64 + lane;
+        const int row = ch / KCPR;
+        const int key = min(kbase + row, key_end - 1);
+        const uint8_t* src = paged_row(p.k_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3), key,
+                                       page_shift, g, p.k_stride_page, p.k_stride_head, p.k_stride_token) +
+                             swz<KROW>(ch % KCPR, row) * 16;
+        dma16(src, kdst + blk * 1024);
+      }
+    }
+    if constexpr (!SHARED) {
+#pragma unroll
+      for (int j = 0; j < V_DMA; ++j) {
+        const int blk = j * NW + wave;
+        if (blk * 64 < VCH) {
+          const int ch = blk * 64 + lane;
+          const int row = ch / VCPR;
+          const int key = min(kbase + row, key_end - 1);
+          const uint8_t* src = paged_row(p.v_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3), key,
+                                         page_shift, g, p.v_stride_page, p.v_stride_head, p.v_stride_token) +
+                               swz<VROW>(ch % VCPR, row) * 16;
+          dma16(src, vdst + blk * 1024);
+        }
+      }
+    }
+  }
+};
+
 // ----------------------------------------------- shared-tile attention kernel --
 //
 // Template parameters: head dims, cache format, NT 16-row MFMA tiles per wave,
@@ -1283,103 +1404,12 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
   int b, g;
   Unit u;
   if (!shared_tile_unit<ROWS>(p, b, g, u)) return;
-  const int32_t* table_row = p.block_table + (int64_t)b * p.max_pages_per_seq;
   const int key_end = u.key_end, kv_lo = u.kv_lo, n_tiles = u.n_tiles;
 
   // ---- KV tile loader ----
-  // Page-id window: lane l holds the physical page of page index pw_base + l.
-  const int page_shift = p.page_shift;
-  const int last_page = n_tiles > 0 ? (key_end - 1) >> page_shift : 0;  // never read past it
-  int pw_base = -(1 << 30);
-  int pw_val = 0;
-  // With pages of >= 64 keys a tile lies in one page: the page base is a scalar
-  // and every lane's source offset inside it is fixed (unless the tile is clamped).
-  const bool one_page = page_shift >= 6;
-  const bool fast_addr = one_page && (int64_t)TK * p.k_stride_token < (1LL << 30) &&
-                         (int64_t)TK * p.v_stride_token < (1LL << 30);
-  uint32_t koff[K_DMA], voff[V_DMA > 0 ? V_DMA : 1];
-#pragma unroll
-  for (int j = 0; j < K_DMA; ++j) {
-    const int ch = (j * NW + wave) * 64 + lane;
-    const int row = ch / KCPR;
-    koff[j] = (uint32_t)(row * p.k_stride_token + swz<KROW>(ch % KCPR, row) * 16);
-  }
-#pragma unroll
-  for (int j = 0; j < V_DMA; ++j) {
-    const int ch = (j * NW + wave) * 64 + lane;
-    const int row = ch / VCPR;
-    voff[j] = (uint32_t)(row * p.v_stride_token + swz<VROW>(ch % VCPR, row) * 16);
-  }
-  const uint32_t smem_base = lds_addr(smem);
-
-  auto issue_tile = [&](int tile, int stage) {
-    const int kbase = kv_lo + tile * TK;
-    const int pg0 = kbase >> page_shift;
-    const int pg_last = min(pg0 + 3, last_page);
-    if (pg0 < pw_base || pg_last > pw_base + 63) {
-      // Refill the window (drains the DMA queue; once per 64 pages).
-      pw_base = pg0;
-      pw_val = load_i32_sync(table_row + min(pg0 + lane, last_page));
-    }
-    const int pp0 = __builtin_amdgcn_readlane(pw_val, pg0 - pw_base);
-    const uint32_t kdst = smem_base + stage * STAGE;
-    const uint32_t vdst = kdst + KTILE;
-    if (fast_addr && kbase + TK <= key_end) {
-      const int slot0 = kbase & ((1 << page_shift) - 1);
-      const uint8_t* kb = p.k_cache + (int64_t)pp0 * p.k_stride_page + (int64_t)g * p.k_stride_head +
-                          (int64_t)slot0 * p.k_stride_token;
-#pragma unroll
-      for (int j = 0; j < K_DMA; ++j)
-        if ((j * NW + wave) * 64 < KCH) dma16_s(koff[j], kb, kdst + (j * NW + wave) * 1024);
-      if constexpr (!SHARED) {
-        const uint8_t* vb = p.v_cache + (int64_t)pp0 * p.v_stride_page +
-                            (int64_t)g * p.v_stride_head + (int64_t)slot0 * p.v_stride_token;
-#pragma unroll
-        for (int j = 0; j < V_DMA; ++j)
-          if ((j * NW + wave) * 64 < VCH) dma16_s(voff[j], vb, vdst + (j * NW + wave) * 1024);
-      }
-      return;
-    }
-    // general path: up to four pages per tile (page_size >= 16), clamped rows
-    int pp1 = pp0, pp2 = pp0, pp3 = pp0;
-    if (!one_page) {
-      pp1 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 1, pg_last) - pw_base);
-      pp2 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 2, pg_last) - pw_base);
-      pp3 = __builtin_amdgcn_readlane(pw_val, pg_last - pw_base);
-    }
-#pragma unroll
-    for (int j = 0; j < K_DMA; ++j) {
-      const int blk = j * NW + wave;
-      if (blk * 64 < KCH) {
-        const int ch = blk * 64 + lane;
-        const int row = ch / KCPR;
-        const int pos = ch % KCPR;
-        const int key = min(kbase + row, key_end - 1);
-        const uint8_t* src = paged_row(p.k_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3),
-                                       key, page_shift, g, p.k_stride_page, p.k_stride_head,
-                                       p.k_stride_token) +
-                             swz<KROW>(pos, row) * 16;
-        dma16(src, kdst + blk * 1024);
-      }
-    }
-    if constexpr (!SHARED) {
-#pragma unroll
-      for (int j = 0; j < V_DMA; ++j) {
-        const int blk = j * NW + wave;
-        if (blk * 64 < VCH) {
-          const int ch = blk * 64 + lane;
-          const int row = ch / VCPR;
-          const int pos = ch % VCPR;
-          const int key = min(kbase + row, key_end - 1);
-          const uint8_t* src = paged_row(p.v_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3),
-                                         key, page_shift, g, p.v_stride_page, p.v_stride_head,
-                                         p.v_stride_token) +
-                               swz<VROW>(pos, row) * 16;
-          dma16(src, vdst + blk * 1024);
-        }
-      }
-    }
-  };
+  DmaTileLoader<KROW, VROW, NW, SHARED> ld;
+  ld.init(p, b, g, wave, kv_lo, key_end, n_tiles, lane, lds_addr(smem));
+  auto issue_tile = [&](int tile, int stage) { ld.issue(p, tile, stage); };
 
   // First tiles go out before the query prologue so both latencies overlap.
 #pragma unroll
@@ -1581,78 +1611,67 @@ __global__ __launch_bounds__(64 * NW, NT == 1 ? 3 : (NW == 4 ? 2 : 1)) void page
 
 }
 
-// -------------------------------------------------------- decode attention --
+// ------------------------------------------------------------ tile loaders --
 //
-// KS waves per unit: wave w takes tiles w, w + KS, ... of the unit's key range
-// and the waves merge their softmax states through LDS at the end, so a unit
-// of n tiles finishes in about n / KS tile times (short units fill the tail of
-// the dispatch).  KV tiles are staged in registers with plain, row-coalesced
-// global loads (the compiler tracks their completion).  At the top of each
-// iteration the arrived tile is written to the wave's LDS tile and the same
-// registers immediately take the next tile, so every load has a whole
-// iteration to arrive while the register file, not LDS, holds the bytes in
-// flight.  K is then read back in the MFMA A-operand layout, V transposed.
+// The page-table-driven KV loads of the attention kernels, as reusable parts:
+// the attention kernels, the debug gather (pa_gather_debug) and the read probe
+// (pa_kv_read_probe) all run these same functions, so the byte-exact gather
+// test covers the address code the kernels execute.
+//
+// RegTileLoader: the decode kernel's loader.  A 64-key tile of one KV head
+// arrives in registers by row-coalesced 16-byte loads (lane l reads row
+// RPL*j + l / CPR, chunk l % CPR), with the non-temporal hint.  Page ids come
+// from a 64-entry register window (lane l holds the page of page index
+// pw_base + l), refilled with a load that waits for itself.  With pages of at
+// least 64 keys a full tile lies in one page: its base is computed once and
+// every lane adds a fixed offset (the fast path); otherwise, and for the
+// tile that ends the range, each row goes through paged_row with its key
+// clamped to the range's last key, so no byte past it is read.  Table entries
+// past the last key's page are never read.
+template <int D>
+struct RegTileLoader {
+  static constexpr int CPR = D / 16;     // 16-byte chunks per row
+  static constexpr int RPL = 64 / CPR;   // rows per 1 KB wave load
+  static constexpr int NLD = TK / RPL;   // loads per tile (K or V)
+  const int32_t* table_row;
+  int g, kv_lo, key_end, last_page, page_shift;
+  int pw_base, pw_val;
+  int ld_row, ld_chunk;
+  int64_t k_lane, v_lane;
+  bool one_page;
 
-template <int D, bool FP8, int NT, bool HILO, int KS, bool TREE>
-__global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnParams p) {
-  constexpr int KPAIRS = D / 64;
-  constexpr int MD = D / 16;
-  constexpr int CPR = D / 16;            // 16-byte chunks per row
-  constexpr int RPL = 64 / CPR;          // rows per 1 KB wave load
-  constexpr int NLD = TK / RPL;          // loads per tile (K or V)
-  constexpr float KV_OFF = FP8 ? 0.f : 1152.f;
+  __device__ __forceinline__ void init(const AttnParams& p, int b, int g_, int kv_lo_, int key_end_, int n_tiles,
+                                       int lane) {
+    table_row = p.block_table + (int64_t)b * p.max_pages_per_seq;
+    g = g_;
+    kv_lo = kv_lo_;
+    key_end = key_end_;
+    page_shift = p.page_shift;
+    last_page = n_tiles > 0 ? (key_end - 1) >> page_shift : 0;   // never read past it
+    pw_base = kv_lo >> page_shift;
+    pw_val = table_row[min(pw_base + lane, last_page)];
+    one_page = page_shift >= 6;
+    ld_row = lane / CPR;
+    ld_chunk = lane % CPR;
+    k_lane = (int64_t)ld_row * p.k_stride_token + 16 * ld_chunk;
+    v_lane = (int64_t)ld_row * p.v_stride_token + 16 * ld_chunk;
+  }
 
-  __shared__ __attribute__((aligned(1024))) uint8_t kvlds[KS][2][TK * D];   // per wave: K tile, V tile
-  __shared__ float vscale_lds[D];
-  __shared__ float mrg_m[KS][16 * NT], mrg_l[KS][16 * NT];
-
-  const int lane = threadIdx.x & 63;
-  const int wv = KS > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
-  uint8_t* const ktile = kvlds[wv][0];
-  uint8_t* const vtile = kvlds[wv][1];
-  const int l16 = lane & 15;
-  const int grp = lane >> 4;
-  // grid = (B * H_kv, row tiles, chunks): chunk-major, so the empty units of
-  // short requests (chunks past their length) are dispatched last
-  const int b = (int)blockIdx.x / p.num_kv_heads;
-  const int g = (int)blockIdx.x % p.num_kv_heads;
-  const int rt = p.row_tiles - 1 - (int)blockIdx.y;  // long (late-token) row tiles first
-  const int c = (int)blockIdx.z;
-  const int32_t* table_row = p.block_table + (int64_t)b * p.max_pages_per_seq;
-  const int page_shift = p.page_shift;
-
-  Unit u;
-  if (!unit_setup<16 * NT>(p, b, rt, c, u)) return;
-  const int key_end = u.key_end, kv_lo = u.kv_lo, n_tiles = u.n_tiles;
-  const int last_page = n_tiles > 0 ? (key_end - 1) >> page_shift : 0;  // never read past it
-
-  // Page-id window: lane l holds the physical page of page index pw_base + l
-  // (clamped to the unit's last page, so no entry past the request is read).
-  int pw_base = kv_lo >> page_shift;
-  int pw_val = table_row[min(pw_base + lane, last_page)];
-  const bool one_page = page_shift >= 6;
-  const int ld_row = lane / CPR, ld_chunk = lane % CPR;
-  const int64_t k_lane = (int64_t)ld_row * p.k_stride_token + 16 * ld_chunk;
-  const int64_t v_lane = (int64_t)ld_row * p.v_stride_token + 16 * ld_chunk;
-
-  uint4_t kr[NLD];   // K row RPL*j + ld_row, chunk ld_chunk
-  uint4_t vr[NLD];   // V row RPL*j + ld_row, chunk ld_chunk
-
-  auto load_tile = [&](int tile) {
+  // Tile `tile` of the range into kr / vr (rows RPL*j + ld_row, chunk ld_chunk).
+  __device__ __forceinline__ void load(const AttnParams& p, int tile, uint4_t (&kr)[NLD], uint4_t (&vr)[NLD]) {
     const int kbase = kv_lo + tile * TK;
     const int pg0 = kbase >> page_shift;
     const int pg_last = min(pg0 + 3, last_page);
     if (pg0 < pw_base || pg_last > pw_base + 63) {
       pw_base = pg0;
-      pw_val = load_i32_sync(table_row + min(pg0 + lane, last_page));  // waits here, not at a join
+      pw_val = load_i32_sync(table_row + min(pg0 + (int)(threadIdx.x & 63), last_page));  // waits here, not at a join
     }
     const int pp0 = __builtin_amdgcn_readlane(pw_val, pg0 - pw_base);
     if (one_page && kbase + TK <= key_end) {
-      const int64_t slot0 = kbase & ((1 << page_shift) - 1);
-      const uint8_t* kb = p.k_cache + (int64_t)pp0 * p.k_stride_page + (int64_t)g * p.k_stride_head +
-                          slot0 * p.k_stride_token;
-      const uint8_t* vb = p.v_cache + (int64_t)pp0 * p.v_stride_page + (int64_t)g * p.v_stride_head +
-                          slot0 * p.v_stride_token;
+      const uint8_t* kb = paged_row(p.k_cache, pp0, kbase, page_shift, g, p.k_stride_page, p.k_stride_head,
+                                    p.k_stride_token);
+      const uint8_t* vb = paged_row(p.v_cache, pp0, kbase, page_shift, g, p.v_stride_page, p.v_stride_head,
+                                    p.v_stride_token);
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
         kr[j] = stream_load16(kb + (int64_t)(RPL * j) * p.k_stride_token + k_lane);
@@ -1675,7 +1694,54 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
                                         p.v_stride_head, p.v_stride_token) + 16 * ld_chunk);
       }
     }
-  };
+  }
+};
+
+// -------------------------------------------------------- decode attention --
+//
+// KS waves per unit: wave w takes tiles w, w + KS, ... of the unit's key range
+// and the waves merge their softmax states through LDS at the end, so a unit
+// of n tiles finishes in about n / KS tile times (short units fill the tail of
+// the dispatch).  KV tiles are staged in registers with plain, row-coalesced
+// global loads (the compiler tracks their completion).  At the top of each
+// iteration the arrived tile is written to the wave's LDS tile and the same
+// registers immediately take the next tile, so every load has a whole
+// iteration to arrive while the register file, not LDS, holds the bytes in
+// flight.  K is then read back in the MFMA A-operand layout, V transposed.
+
+template <int D, bool FP8, int NT, bool HILO, int KS, bool TREE>
+__global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnParams p) {
+  constexpr int KPAIRS = D / 64;
+  constexpr int MD = D / 16;
+  constexpr int RPL = RegTileLoader<D>::RPL;   // rows per 1 KB wave load
+  constexpr int NLD = RegTileLoader<D>::NLD;   // loads per tile (K or V)
+  constexpr float KV_OFF = FP8 ? 0.f : 1152.f;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t kvlds[KS][2][TK * D];   // per wave: K tile, V tile
+  __shared__ float vscale_lds[D];
+  __shared__ float mrg_m[KS][16 * NT], mrg_l[KS][16 * NT];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = KS > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
+  uint8_t* const ktile = kvlds[wv][0];
+  uint8_t* const vtile = kvlds[wv][1];
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;
+  // grid = (B * H_kv, row tiles, chunks): chunk-major, so the empty units of
+  // short requests (chunks past their length) are dispatched last
+  const int b = (int)blockIdx.x / p.num_kv_heads;
+  const int g = (int)blockIdx.x % p.num_kv_heads;
+  const int rt = p.row_tiles - 1 - (int)blockIdx.y;  // long (late-token) row tiles first
+  const int c = (int)blockIdx.z;
+  Unit u;
+  if (!unit_setup<16 * NT>(p, b, rt, c, u)) return;
+  const int kv_lo = u.kv_lo, n_tiles = u.n_tiles;
+  RegTileLoader<D> ld;
+  ld.init(p, b, g, kv_lo, u.key_end, n_tiles, lane);
+  uint4_t kr[RegTileLoader<D>::NLD];   // K row RPL*j + ld_row, chunk ld_chunk
+  uint4_t vr[RegTileLoader<D>::NLD];   // V rows, same places
+  const int ld_row = ld.ld_row, ld_chunk = ld.ld_chunk;
+  auto load_tile = [&](int tile) { ld.load(p, tile, kr, vr); };
 
   SoftmaxState<NT, MD> st;
   softmax_init(st);
@@ -1911,60 +1977,12 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
   int b, g;
   Unit u;
   if (!shared_tile_unit<ROWS, BAL>(p, b, g, u)) return;   // a chunk's row tiles share an XCD
-  const int32_t* table_row = p.block_table + (int64_t)b * p.max_pages_per_seq;
-  const int key_end = u.key_end, kv_lo = u.kv_lo, n_tiles = u.n_tiles;
-  const int page_shift = p.page_shift;
-  const int last_page = n_tiles > 0 ? (key_end - 1) >> page_shift : 0;
-  int pw_base = -(1 << 30);
-  int pw_val = 0;
-  const bool one_page = page_shift >= 6;
-  const bool fast_addr = one_page && (int64_t)TK * p.k_stride_token < (1LL << 30);
-  const uint32_t kst_base = lds_addr(kst);
-
-  // Raw tile `tile` -> stage `stage` (this wave's K_DMA instructions).
-  auto issue_tile = [&](int tile, int stage) {
-    const int kbase = kv_lo + tile * TK;
-    const int pg0 = kbase >> page_shift;
-    const int pg_last = min(pg0 + 3, last_page);
-    if (pg0 < pw_base || pg_last > pw_base + 63) {
-      pw_base = pg0;
-      pw_val = load_i32_sync(table_row + min(pg0 + lane, last_page));
-    }
-    const int pp0 = __builtin_amdgcn_readlane(pw_val, pg0 - pw_base);
-    const uint32_t kdst = kst_base + stage * KTILE;
-    if (fast_addr && kbase + TK <= key_end) {
-      const uint8_t* kb = p.k_cache + (int64_t)pp0 * p.k_stride_page + (int64_t)g * p.k_stride_head +
-                          (int64_t)(kbase & ((1 << page_shift) - 1)) * p.k_stride_token;
-#pragma unroll
-      for (int j = 0; j < K_DMA; ++j) {
-        const int blk = j * NW + wave;
-        if (blk >= K_BLK) break;
-        const int ch = blk * 64 + lane;
-        const int row = ch / KCPR;
-        dma16_s((uint32_t)(row * p.k_stride_token + swz<KROW>(ch - row * KCPR, row) * 16), kb,
-                kdst + blk * 1024);
-      }
-      return;
-    }
-    int pp1 = pp0, pp2 = pp0, pp3 = pp0;
-    if (!one_page) {
-      pp1 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 1, pg_last) - pw_base);
-      pp2 = __builtin_amdgcn_readlane(pw_val, min(pg0 + 2, pg_last) - pw_base);
-      pp3 = __builtin_amdgcn_readlane(pw_val, pg_last - pw_base);
-    }
-#pragma unroll
-    for (int j = 0; j < K_DMA; ++j) {
-      const int blk = j * NW + wave;
-      if (blk >= K_BLK) break;
-      const int ch = blk * 64 + lane;
-      const int row = ch / KCPR;
-      const int key = min(kbase + row, key_end - 1);
-      const uint8_t* src = paged_row(p.k_cache, pick_page(key, page_shift, pg0, pp0, pp1, pp2, pp3), key,
-                                     page_shift, g, p.k_stride_page, p.k_stride_head, p.k_stride_token) +
-                           swz<KROW>(ch % KCPR, row) * 16;
-      dma16(src, kdst + blk * 1024);
-    }
-  };
+  const int kv_lo = u.kv_lo, n_tiles = u.n_tiles;
+  DmaTileLoader<KROW, KROW, NW, true> ld;
+  ld.init(p, b, g, wave, kv_lo, u.key_end, n_tiles, lane, lds_addr(kst));
+  auto issue_tile = [&](int tile, int stage) { ld.issue(p, tile, stage); };
+  static_assert(DmaTileLoader<KROW, KROW, NW, true>::K_DMA == K_DMA && DmaTileLoader<KROW, KROW, NW, true>::KTILE == KTILE,
+                "MLA stage geometry");
 
   if (n_tiles > 0) issue_tile(0, 0);
   if (n_tiles > 1) issue_tile(1, 1);
@@ -2293,6 +2311,108 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherParams p) {
     *(uint4_t*)(dst + d) = *(const uint4_t*)(src + d);
 }
 
+// ------------------------------------------- tile-loader gather and probe --
+// Unit (b, g, c) of a tile walk: keys [kv_lo, key_end); false when empty.
+__device__ __forceinline__ bool walk_unit(const TileWalkParams& w, int& b, int& g, int& kv_lo, int& key_end) {
+  b = (int)blockIdx.x / w.a.num_kv_heads;
+  g = (int)blockIdx.x % w.a.num_kv_heads;
+  const int n = w.q_lens ? w.q_lens[b] : w.a.q_len_uniform;
+  const int T = w.a.seq_lens_kv[b] + n;
+  kv_lo = (int)blockIdx.z * w.chunk;
+  key_end = min(T, kv_lo + w.chunk);
+  return kv_lo < key_end;
+}
+
+// The decode kernel's loader, tile by tile, rows written to the gather
+// destinations in key order.
+template <int D>
+__global__ __launch_bounds__(64) void gather_reg_kernel(TileWalkParams w) {
+  using LD = RegTileLoader<D>;
+  int b, g, kv_lo, key_end;
+  if (!walk_unit(w, b, g, kv_lo, key_end)) return;
+  const int lane = threadIdx.x & 63;
+  const int n_tiles = (key_end - kv_lo + TK - 1) / TK;
+  LD ld;
+  ld.init(w.a, b, g, kv_lo, key_end, n_tiles, lane);
+  uint4_t kr[LD::NLD], vr[LD::NLD];
+  const int64_t bg = (int64_t)b * w.a.num_kv_heads + g;
+  for (int it = 0; it < n_tiles; ++it) {
+    ld.load(w.a, it, kr, vr);
+#pragma unroll
+    for (int j = 0; j < LD::NLD; ++j) {
+      const int key = kv_lo + it * TK + LD::RPL * j + ld.ld_row;
+      if (key < key_end) {
+        const int64_t row = bg * w.t_max + key;
+        if (w.k_dst) *(uint4_t*)(w.k_dst + row * D + 16 * ld.ld_chunk) = kr[j];
+        if (w.v_dst) *(uint4_t*)(w.v_dst + row * D + 16 * ld.ld_chunk) = vr[j];
+      }
+    }
+  }
+}
+
+// The shared-tile / MLA kernels' loader: each tile lands in one LDS stage by
+// DMA (NW waves), then is copied out unswizzled.
+template <int KROW, int VROW, int NW, bool SHARED>
+__global__ __launch_bounds__(64 * NW) void gather_dma_kernel(TileWalkParams w) {
+  using LD = DmaTileLoader<KROW, VROW, NW, SHARED>;
+  __shared__ __attribute__((aligned(1024))) uint8_t stage[LD::STAGE];
+  int b, g, kv_lo, key_end;
+  if (!walk_unit(w, b, g, kv_lo, key_end)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int n_tiles = (key_end - kv_lo + TK - 1) / TK;
+  LD ld;
+  ld.init(w.a, b, g, wave, kv_lo, key_end, n_tiles, lane, lds_addr(stage));
+  const int64_t bg = (int64_t)b * w.a.num_kv_heads + g;
+  for (int it = 0; it < n_tiles; ++it) {
+    ld.issue(w.a, it, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int ch = threadIdx.x; ch < LD::KCH + LD::VCH; ch += 64 * NW) {
+      const bool is_k = ch < LD::KCH;
+      const int c2 = is_k ? ch : ch - LD::KCH;
+      const int cpr = is_k ? LD::KCPR : LD::VCPR;
+      const int row = c2 / cpr, pos = c2 % cpr;
+      const int key = kv_lo + it * TK + row;
+      if (key >= key_end) continue;
+      const int off = is_k ? row * KROW + swz<KROW>(pos, row) * 16 : LD::KTILE + row * VROW + swz<VROW>(pos, row) * 16;
+      const uint4_t v = *(const uint4_t*)(stage + off);
+      const int64_t r = bg * w.t_max + key;
+      if (is_k && w.k_dst) *(uint4_t*)(w.k_dst + r * KROW + pos * 16) = v;
+      if (!is_k && w.v_dst) *(uint4_t*)(w.v_dst + r * VROW + pos * 16) = v;
+    }
+    __syncthreads();
+  }
+}
+
+// Read probe: the decode kernel's loads and nothing else.  One tile stays in
+// flight while the previous one is folded into an xor (as the kernel keeps
+// one in flight while it computes).
+template <int D>
+__global__ __launch_bounds__(64) void read_probe_kernel(TileWalkParams w) {
+  using LD = RegTileLoader<D>;
+  int b, g, kv_lo, key_end;
+  if (!walk_unit(w, b, g, kv_lo, key_end)) return;
+  const int lane = threadIdx.x & 63;
+  const int n_tiles = (key_end - kv_lo + TK - 1) / TK;
+  LD ld;
+  ld.init(w.a, b, g, kv_lo, key_end, n_tiles, lane);
+  uint4_t kr[LD::NLD], vr[LD::NLD];
+  uint4_t acc = {0u, 0u, 0u, 0u};
+  ld.load(w.a, 0, kr, vr);
+  for (int it = 0; it < n_tiles; ++it) {
+    uint4_t x = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < LD::NLD; ++j) x ^= kr[j] ^ vr[j];
+    if (it + 1 < n_tiles) ld.load(w.a, it + 1, kr, vr);
+    acc ^= x;
+  }
+  uint32_t v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) v ^= (uint32_t)__shfl_xor((int)v, d, 64);
+  if (lane == 0) w.sink[(int64_t)blockIdx.z * gridDim.x + blockIdx.x] = v;
+}
+
 // ------------------------------------------------------------------ launch --
 
 namespace {
@@ -2488,6 +2608,38 @@ hipError_t launch_zero_words(int32_t* p, int64_t n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
   hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_gather(int loader, int dqk, int dv, bool shared_kv, const TileWalkParams& p, int batch,
+                              int num_kv_heads, int max_chunks, hipStream_t stream) {
+  const dim3 grid((unsigned)(batch * num_kv_heads), 1, (unsigned)max_chunks);
+#define PA_TG(KERNEL, THREADS)                                                  \
+  do {                                                                          \
+    hipLaunchKernelGGL(KERNEL, grid, dim3(THREADS), 0, stream, p);              \
+    return hipGetLastError();                                                   \
+  } while (0)
+  if (loader == 1 && !shared_kv && dqk == dv) {
+    if (dqk == 64) PA_TG((gather_reg_kernel<64>), 64);
+    if (dqk == 128) PA_TG((gather_reg_kernel<128>), 64);
+  }
+  if ((loader == 2 || loader == 3) && !shared_kv && dqk == dv) {
+    if (dqk == 64 && loader == 2) PA_TG((gather_dma_kernel<64, 64, 4, false>), 256);
+    if (dqk == 64 && loader == 3) PA_TG((gather_dma_kernel<64, 64, 3, false>), 192);
+    if (dqk == 128 && loader == 2) PA_TG((gather_dma_kernel<128, 128, 4, false>), 256);
+    if (dqk == 128 && loader == 3) PA_TG((gather_dma_kernel<128, 128, 3, false>), 192);
+  }
+  if (loader == 2 && shared_kv && dqk == 576) PA_TG((gather_dma_kernel<576, 576, MLA_WAVES, true>), 64 * MLA_WAVES);
+#undef PA_TG
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_read_probe(int d, const TileWalkParams& p, int batch, int num_kv_heads, int max_chunks,
+                             hipStream_t stream) {
+  const dim3 grid((unsigned)(batch * num_kv_heads), 1, (unsigned)max_chunks);
+  if (d == 64) hipLaunchKernelGGL(read_probe_kernel<64>, grid, dim3(64), 0, stream, p);
+  else if (d == 128) hipLaunchKernelGGL(read_probe_kernel<128>, grid, dim3(64), 0, stream, p);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

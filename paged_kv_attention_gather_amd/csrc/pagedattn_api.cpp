@@ -511,37 +511,125 @@ int32_t split_kv_merge(const float* partial_o, const float* partial_lse,
   return ok();
 }
 
-int32_t pa_gather_debug(const pa_problem* prob, const void* k_cache, const int32_t* block_table,
-                        const int32_t* seq_lens_kv, const int32_t* q_lens, int32_t t_max,
-                        uint8_t* dst, void* stream) {
+int32_t pa_gather_debug(const pa_problem* prob, int32_t loader, const void* k_cache, const void* v_cache,
+                        const int32_t* block_table, const int32_t* seq_lens_kv, const int32_t* q_lens,
+                        int32_t t_max, uint8_t* k_dst, uint8_t* v_dst, void* stream) {
   int32_t st = check_problem(prob);
   if (st != PA_OK) return st;
+  if (loader < PA_GATHER_ROWS || loader > PA_GATHER_DMA_3W)
+    return fail(PA_ERR_INVALID_ARG, "loader %d: PA_GATHER_ROWS, _DECODE, _DMA_4W or _DMA_3W", loader);
   if (t_max < 0) return fail(PA_ERR_INVALID_ARG, "t_max %d < 0", t_max);
   if ((int64_t)t_max > (int64_t)prob->max_pages_per_seq * prob->page_size)
     return fail(PA_ERR_INVALID_ARG, "t_max %d exceeds the block table capacity", t_max);
   if (prob->batch == 0 || t_max == 0) return ok();
-  if (!k_cache || !block_table || !seq_lens_kv || !q_lens || !dst)
+  if (!k_cache || !block_table || !seq_lens_kv || !q_lens || !k_dst || (v_dst && !v_cache))
     return fail(PA_ERR_INVALID_ARG, "a required device pointer is NULL");
-  if (!aligned16(k_cache) || !aligned16(dst) || prob->k_stride_page % 16 || prob->k_stride_head % 16 ||
-      prob->k_stride_token % 16 || prob->k_stride_page <= 0 || prob->k_stride_head <= 0 ||
-      prob->k_stride_token <= 0)
-    return fail(PA_ERR_INVALID_ARG, "k_cache, dst and cache strides must be 16-byte aligned and positive");
-  pa::GatherParams gp{};
-  gp.k_cache = static_cast<const uint8_t*>(k_cache);
-  gp.block_table = block_table;
-  gp.seq_lens_kv = seq_lens_kv;
-  gp.q_lens = q_lens;
-  gp.dst = dst;
-  gp.k_stride_page = prob->k_stride_page;
-  gp.k_stride_head = prob->k_stride_head;
-  gp.k_stride_token = prob->k_stride_token;
-  gp.num_kv_heads = prob->num_kv_heads;
-  gp.head_dim = prob->head_dim_qk;
-  gp.page_shift = log2_exact(prob->page_size);
-  gp.max_pages_per_seq = prob->max_pages_per_seq;
-  gp.t_max = t_max;
-  hipError_t e = pa::launch_gather(gp, prob->batch, static_cast<hipStream_t>(stream));
+  const int64_t ks[3] = {prob->k_stride_page, prob->k_stride_head, prob->k_stride_token};
+  const int64_t vs[3] = {prob->v_stride_page, prob->v_stride_head, prob->v_stride_token};
+  for (int i = 0; i < 3; ++i)
+    if (ks[i] <= 0 || ks[i] % 16 || (v_dst && (vs[i] <= 0 || vs[i] % 16)))
+      return fail(PA_ERR_INVALID_ARG, "cache strides must be positive multiples of 16 bytes");
+  if (!aligned16(k_cache) || !aligned16(k_dst) || (v_dst && (!aligned16(v_cache) || !aligned16(v_dst))))
+    return fail(PA_ERR_INVALID_ARG, "caches and destinations must be 16-byte aligned");
+  const bool shared = prob->head_dim_qk == 576;
+  if (shared && v_dst) return fail(PA_ERR_INVALID_ARG, "the shared latent layout has no separate V rows: v_dst must be NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (loader == PA_GATHER_ROWS) {
+    pa::GatherParams gp{};
+    gp.block_table = block_table;
+    gp.seq_lens_kv = seq_lens_kv;
+    gp.q_lens = q_lens;
+    gp.page_shift = log2_exact(prob->page_size);
+    gp.max_pages_per_seq = prob->max_pages_per_seq;
+    gp.num_kv_heads = prob->num_kv_heads;
+    gp.t_max = t_max;
+    for (int pass = 0; pass < (v_dst ? 2 : 1); ++pass) {
+      gp.k_cache = static_cast<const uint8_t*>(pass ? v_cache : k_cache);
+      gp.dst = pass ? v_dst : k_dst;
+      gp.k_stride_page = pass ? prob->v_stride_page : prob->k_stride_page;
+      gp.k_stride_head = pass ? prob->v_stride_head : prob->k_stride_head;
+      gp.k_stride_token = pass ? prob->v_stride_token : prob->k_stride_token;
+      gp.head_dim = pass ? prob->head_dim_v : prob->head_dim_qk;
+      hipError_t e = pa::launch_gather(gp, prob->batch, s);
+      if (e != hipSuccess) return fail(PA_ERR_HIP, "gather launch failed: %s", hipGetErrorString(e));
+    }
+    return ok();
+  }
+  pa::TileWalkParams w{};
+  w.a.k_cache = static_cast<const uint8_t*>(k_cache);
+  w.a.v_cache = static_cast<const uint8_t*>(v_cache ? v_cache : k_cache);
+  w.a.seq_lens_kv = seq_lens_kv;
+  w.a.block_table = block_table;
+  w.a.k_stride_page = prob->k_stride_page;
+  w.a.k_stride_head = prob->k_stride_head;
+  w.a.k_stride_token = prob->k_stride_token;
+  w.a.v_stride_page = v_cache ? prob->v_stride_page : prob->k_stride_page;
+  w.a.v_stride_head = v_cache ? prob->v_stride_head : prob->k_stride_head;
+  w.a.v_stride_token = v_cache ? prob->v_stride_token : prob->k_stride_token;
+  w.a.num_kv_heads = prob->num_kv_heads;
+  w.a.page_shift = log2_exact(prob->page_size);
+  w.a.max_pages_per_seq = prob->max_pages_per_seq;
+  w.q_lens = q_lens;
+  w.k_dst = k_dst;
+  w.v_dst = v_dst;
+  w.t_max = t_max;
+  const int64_t whole = ceil_div((int64_t)t_max, kTileKeys) * kTileKeys;
+  w.chunk = (int32_t)(prob->chunk_size > 0 ? prob->chunk_size : whole);
+  const int64_t chunks = ceil_div((int64_t)t_max, w.chunk);
+  if (chunks > 65535 || (int64_t)prob->batch * prob->num_kv_heads > 0x7fffffffLL)
+    return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  hipError_t e = pa::launch_tile_gather(loader, prob->head_dim_qk, prob->head_dim_v, shared, w, prob->batch,
+                                        prob->num_kv_heads, (int)chunks, s);
+  if (e == hipErrorInvalidValue)
+    return fail(PA_ERR_UNSUPPORTED, "loader %d has no instance for head dims (%d, %d)", loader, prob->head_dim_qk,
+                prob->head_dim_v);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "gather launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t pa_kv_read_probe(const pa_problem* prob, int32_t q_len, const void* k_cache, const void* v_cache,
+                         const int32_t* seq_lens_kv, const int32_t* block_table, uint32_t* sink,
+                         void* stream) {
+  int32_t st = check_problem(prob);
+  if (st != PA_OK) return st;
+  if (q_len < 1 || q_len > 64) return fail(PA_ERR_INVALID_ARG, "decode q_len %d not in [1, 64]", q_len);
+  if (prob->max_q_len < q_len) return fail(PA_ERR_INVALID_ARG, "max_q_len %d < q_len %d", prob->max_q_len, q_len);
+  if (prob->head_dim_qk != prob->head_dim_v || (prob->head_dim_qk != 64 && prob->head_dim_qk != 128))
+    return fail(PA_ERR_UNSUPPORTED, "the read probe follows the decode kernel: head dims 64 or 128");
+  if (prob->batch == 0) return ok();
+  if (!k_cache || !v_cache || !seq_lens_kv || !block_table || !sink)
+    return fail(PA_ERR_INVALID_ARG, "a required device pointer is NULL");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_INVALID_ARG, "caches must be 16-byte aligned");
+  const int64_t ks[3] = {prob->k_stride_page, prob->k_stride_head, prob->k_stride_token};
+  const int64_t vs[3] = {prob->v_stride_page, prob->v_stride_head, prob->v_stride_token};
+  for (int i = 0; i < 3; ++i)
+    if (ks[i] <= 0 || ks[i] % 16 || vs[i] <= 0 || vs[i] % 16)
+      return fail(PA_ERR_INVALID_ARG, "cache strides must be positive multiples of 16 bytes");
+  pa::TileWalkParams w{};
+  w.a.k_cache = static_cast<const uint8_t*>(k_cache);
+  w.a.v_cache = static_cast<const uint8_t*>(v_cache);
+  w.a.seq_lens_kv = seq_lens_kv;
+  w.a.block_table = block_table;
+  w.a.k_stride_page = prob->k_stride_page;
+  w.a.k_stride_head = prob->k_stride_head;
+  w.a.k_stride_token = prob->k_stride_token;
+  w.a.v_stride_page = prob->v_stride_page;
+  w.a.v_stride_head = prob->v_stride_head;
+  w.a.v_stride_token = prob->v_stride_token;
+  w.a.num_kv_heads = prob->num_kv_heads;
+  w.a.page_shift = log2_exact(prob->page_size);
+  w.a.max_pages_per_seq = prob->max_pages_per_seq;
+  w.a.q_len_uniform = q_len;
+  w.sink = sink;
+  const int64_t keys = (int64_t)prob->max_kv_len + q_len;
+  w.chunk = (int32_t)(prob->chunk_size > 0 ? prob->chunk_size : ceil_div(keys, kTileKeys) * kTileKeys);
+  const int64_t chunks = max_chunks_of(prob);
+  if (chunks > 65535 || (int64_t)prob->batch * prob->num_kv_heads > 0x7fffffffLL)
+    return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  hipError_t e = pa::launch_read_probe(prob->head_dim_qk, w, prob->batch, prob->num_kv_heads, (int)chunks,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "probe launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -250,9 +250,25 @@ def test_merge_validation(lib):
 def test_gather_validation(lib):
     prob = base_problem()
     g = lib.pa_gather_debug
-    assert g(ctypes.byref(prob), FAKE, FAKE, FAKE, FAKE, -1, FAKE, None) == L.PA_ERR_INVALID_ARG
-    assert g(ctypes.byref(prob), None, FAKE, FAKE, FAKE, 64, FAKE, None) == L.PA_ERR_INVALID_ARG
-    assert g(ctypes.byref(prob), FAKE, FAKE, FAKE, FAKE, 16 * 64 + 1, FAKE, None) == L.PA_ERR_INVALID_ARG
+    P_ = ctypes.byref(prob)
+    assert g(P_, 0, FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, None, None) == L.PA_ERR_INVALID_ARG
+    assert g(P_, 0, None, FAKE, FAKE, FAKE, FAKE, 64, FAKE, None, None) == L.PA_ERR_INVALID_ARG
+    assert g(P_, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 16 * 64 + 1, FAKE, None, None) == L.PA_ERR_INVALID_ARG
+    assert g(P_, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, None, None) == L.PA_ERR_INVALID_ARG   # loader
+    assert g(P_, 0, FAKE, None, FAKE, FAKE, FAKE, 64, FAKE, FAKE, None) == L.PA_ERR_INVALID_ARG   # V dst, no V
+    mla = base_problem(num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, q_row_stride=16 * 576,
+                       k_stride_page=64 * 576, k_stride_head=64 * 576, k_stride_token=576,
+                       v_stride_page=64 * 576, v_stride_head=64 * 576, v_stride_token=576)
+    assert g(ctypes.byref(mla), 2, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, FAKE, None) == L.PA_ERR_INVALID_ARG
+
+
+def test_read_probe_validation(lib):
+    r = lib.pa_kv_read_probe
+    assert r(ctypes.byref(base_problem()), 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.PA_ERR_INVALID_ARG
+    assert r(ctypes.byref(base_problem()), 1, FAKE, None, FAKE, FAKE, FAKE, None) == L.PA_ERR_INVALID_ARG
+    mla = base_problem(num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512)
+    assert r(ctypes.byref(mla), 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.PA_ERR_UNSUPPORTED
+    assert r(ctypes.byref(base_problem(batch=0)), 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.PA_OK
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

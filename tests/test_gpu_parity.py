@@ -25,43 +25,98 @@ def _run(w, **kw):
 
 
 # ------------------------------------------------------------ page gather --
+#
+# Byte-exact gathers through each loader the attention kernels run: one key
+# row at a time, the decode kernel's register tile loader, and the LDS-DMA
+# tile loader with 4 or 3 waves (also for the shared 576-byte latent rows),
+# over the workloads' chunked units (tiles that end a chunk or a sequence,
+# one-page fast path and page sizes below 64).
+
+LOADERS = {"rows": 0, "decode": 1, "dma4": 2, "dma3": 3}
+
+
+def _loaders_for(w):
+    if w.shared_kv:
+        return ["rows", "dma4"]
+    return list(LOADERS)
+
+
+def _gather(w, loader, reqs=None):
+    torch = need_gpu()
+    import paged_kv_attention_gather_amd as P
+    from paged_kv_attention_gather_amd.harness import DeviceProblem
+    dp = DeviceProblem(w)
+    T = w.kv_tokens()
+    t_max = int(T.max())
+    kd = torch.zeros((w.batch, w.num_kv_heads, t_max, w.head_dim_qk), dtype=torch.uint8, device="cuda")
+    vd = None if w.shared_kv else torch.zeros((w.batch, w.num_kv_heads, t_max, w.head_dim_v), dtype=torch.uint8,
+                                              device="cuda")
+    P.pa_gather_debug(dp.prob, dp.k_cache, dp.block_table, dp.seq_lens_kv, dp.q_lens, t_max, kd,
+                      loader=LOADERS[loader], v_cache=None if w.shared_kv else dp.v_cache, v_dst=vd)
+    torch.cuda.synchronize()
+    return kd.cpu().numpy(), None if vd is None else vd.cpu().numpy()
+
 
 @pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
 def test_gather_bit_exact_small(idx):
-    torch = need_gpu()
-    import paged_kv_attention_gather_amd as P
-    from paged_kv_attention_gather_amd.harness import DeviceProblem
+    need_gpu()
     w = small_variant(idx)
-    announce(f"gather small_variant({idx}) {w.name}")
-    dp = DeviceProblem(w)
-    T = w.kv_tokens()
-    t_max = int(T.max())
-    dst = torch.zeros((w.batch, w.num_kv_heads, t_max, w.head_dim_qk), dtype=torch.uint8, device="cuda")
-    P.pa_gather_debug(dp.prob, dp.k_cache, dp.block_table, dp.seq_lens_kv, dp.q_lens, t_max, dst)
-    torch.cuda.synchronize()
-    got = dst.cpu().numpy()
-    ref = oracle.gather_bytes(w)
-    assert np.array_equal(got, ref)
+    for loader in _loaders_for(w):
+        announce(f"gather small_variant({idx}) {w.name} loader={loader}")
+        k, v = _gather(w, loader)
+        assert np.array_equal(k, oracle.gather_bytes(w)), loader
+        if v is not None:
+            vw = type(w)(**{**w.__dict__, "k_cache": w.v_cache, "head_dim_qk": w.head_dim_v})
+            assert np.array_equal(v, oracle.gather_bytes(vw)), loader
 
 
-@pytest.mark.parametrize("idx", [2, 5])
+@pytest.mark.parametrize("idx", [2, 4, 5])
 def test_gather_bit_exact_full(idx):
+    need_gpu()
+    w = config_workload(idx)
+    T = w.kv_tokens()
+    for loader in _loaders_for(w):
+        announce(f"gather config_workload({idx}) {w.name} loader={loader}")
+        k, v = _gather(w, loader)
+        for b in range(w.batch):
+            for g in range(w.num_kv_heads):
+                ref = oracle.gather_rows(w.k_cache, w.block_table[b], g, int(T[b]), w.page_size, w.head_dim_qk)
+                assert np.array_equal(k[b, g, :T[b]], ref), (loader, b, g)
+                if v is not None:
+                    ref = oracle.gather_rows(w.v_cache, w.block_table[b], g, int(T[b]), w.page_size, w.head_dim_v)
+                    assert np.array_equal(v[b, g, :T[b]], ref), (loader, "V", b, g)
+
+
+def test_read_probe_reads_every_tile():
+    """The read probe's per-unit xor equals the xor of the unit's K and V
+    bytes as 16-byte words, where the last tile's rows past the unit's end
+    repeat its last key (the loader clamps them)."""
     torch = need_gpu()
     import paged_kv_attention_gather_amd as P
     from paged_kv_attention_gather_amd.harness import DeviceProblem
-    w = config_workload(idx)
-    announce(f"gather config_workload({idx}) {w.name}")
+    w = small_variant(2)
+    announce("read probe small_variant(2)")
     dp = DeviceProblem(w)
+    C = w.chunk_size
     T = w.kv_tokens()
-    t_max = int(T.max())
-    dst = torch.zeros((w.batch, w.num_kv_heads, t_max, w.head_dim_qk), dtype=torch.uint8, device="cuda")
-    P.pa_gather_debug(dp.prob, dp.k_cache, dp.block_table, dp.seq_lens_kv, dp.q_lens, t_max, dst)
+    mc = max(1, -(-(int(w.seq_lens_kv.max()) + int(w.decode_q_len)) // C))
+    sink = torch.zeros(mc * w.batch * w.num_kv_heads, dtype=torch.int32, device="cuda")
+    P.pa_kv_read_probe(dp.prob, int(w.decode_q_len), dp.k_cache, dp.v_cache, dp.seq_lens_kv, dp.block_table, sink)
     torch.cuda.synchronize()
-    got = dst.cpu().numpy()
-    for b in range(0, w.batch, max(1, w.batch // 8)):
+    got = sink.cpu().numpy().view(np.uint32)
+    for b in range(w.batch):
         for g in range(w.num_kv_heads):
-            ref = oracle.gather_rows(w.k_cache, w.block_table[b], g, int(T[b]), w.page_size, w.head_dim_qk)
-            assert np.array_equal(got[b, g, :T[b]], ref), (b, g)
+            k = oracle.gather_rows(w.k_cache, w.block_table[b], g, int(T[b]), w.page_size, w.head_dim_qk)
+            v = oracle.gather_rows(w.v_cache, w.block_table[b], g, int(T[b]), w.page_size, w.head_dim_v)
+            for c in range(mc):
+                lo, hi = c * C, min(int(T[b]), (c + 1) * C)
+                want = 0
+                if lo < hi:
+                    n_pad = -(-(hi - lo) // 64) * 64 - (hi - lo)
+                    rows = np.concatenate([k[lo:hi], v[lo:hi]] + ([np.repeat(k[hi - 1:hi], n_pad, 0),
+                                                                   np.repeat(v[hi - 1:hi], n_pad, 0)] if n_pad else []))
+                    want = int(np.bitwise_xor.reduce(rows.reshape(-1).view(np.uint32)))
+                assert got[c * w.batch * w.num_kv_heads + b * w.num_kv_heads + g] == want, (b, g, c)
 
 
 # --------------------------------------------------- attention, small sizes --
