@@ -231,6 +231,9 @@ def main():
     ap.add_argument("--balanced", action="store_true",
                     help="PA_FLAG_BALANCED_SPLIT: KV items sized on the device to fill one round "
                          "(chunk_size, or --chunk, is then the shortest item)")
+    ap.add_argument("--persistent", action="store_true",
+                    help="PA_FLAG_PERSISTENT: the decode kernel as one persistent launch with equal per-wave "
+                         "shares (chunk_size is the shortest share) and the merge inside")
     ap.add_argument("--no-extra-configs", action="store_true",
                     help="with the default workload, skip timing the append, spec-decode and MLA workloads")
     ap.add_argument("--no-probe", action="store_true", help="skip the read probe of the decode workloads")
@@ -274,7 +277,7 @@ def main():
         print("[bench] --balanced: the merge runs inside the ABI call", file=sys.stderr, flush=True)
     flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB, read before every timed step
     m = measure(w, args.config, flush, args.steps, args.warmup, chunk=args.chunk, fused=fused,
-                balanced=args.balanced, no_flush=args.no_flush)
+                balanced=args.balanced, no_flush=args.no_flush, persistent=args.persistent)
     dp, chunk = m["dp"], m["chunk"]
     kv_bytes, alg_bytes, flops = work_figures(w)
     ms, attn_ms = m["step_ms"], m["attn_ms"]
@@ -295,10 +298,13 @@ def main():
     roof["kernel_min_ms"] = round(m["attn_min_ms"], 5)
     roof["merge_ms"] = round(m["merge_ms"], 5)
     roof["merge"] = (("in-kernel (PA_FLAG_FUSED_MERGE)" if fused else
+                      "in-kernel, last wave of each (request, head) (PA_FLAG_PERSISTENT)" if args.persistent else
                       "split_kv_merge launch" + (" inside the call (kernel_ms includes it)" if args.balanced else ""))
                      if chunk > 0 else "none")
     roof["split"] = ("PA_FLAG_BALANCED_SPLIT requested (applied by the MLA kernel; the others keep fixed chunks)"
-                     if args.balanced and chunk > 0 else "fixed chunks")
+                     if args.balanced and chunk > 0 else
+                     "persistent: equal per-wave tile shares of at least chunk_size keys" if args.persistent and chunk > 0
+                     else "fixed chunks")
     roof["alg_bytes_per_launch"] = alg_bytes
     roof["flops_per_launch"] = flops
     if not args.no_probe and args.config in (2, 4) and not args.tree:
@@ -326,7 +332,7 @@ def main():
     }
     del m, dp
     if not args.no_extra_configs and args.config == 2 and not args.tree and not fused and not args.balanced \
-            and args.chunk is None:
+            and not args.persistent and args.chunk is None:
         line["configs"] = other_configs(flush, args)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -334,18 +340,20 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def measure(w, config, flush, steps, warmup, chunk=None, fused=False, balanced=False, no_flush=False):
+def measure(w, config, flush, steps, warmup, chunk=None, fused=False, balanced=False, no_flush=False,
+            persistent=False):
     """Time `steps` calls of the workload after `warmup` untimed ones.  Per
     step: [flush] e0 attention e1 merge e2 on the launch stream (torch's
     current stream, which the binding passes to the library); with the fused
     or balanced merge e1..e2 encloses nothing."""
     import torch
     from paged_kv_attention_gather_amd.harness import DeviceProblem
-    dp = DeviceProblem(w, chunk_size=chunk, defer_merge=not fused and not balanced,
-                       fused_merge=fused, balanced=balanced)
+    one_call = fused or balanced or persistent   # the call merges by itself
+    dp = DeviceProblem(w, chunk_size=chunk, defer_merge=not one_call, fused_merge=fused, balanced=balanced,
+                       persistent=persistent)
     chunk = dp.prob.chunk_size
     stream = torch.cuda.current_stream()
-    separate = not fused and not balanced   # merge launched here, timed apart
+    separate = not one_call   # merge launched here, timed apart
     print(f"[bench] {w.name}: warmup {warmup}", file=sys.stderr, flush=True)
     for _ in range(warmup):
         if not no_flush:
@@ -364,10 +372,12 @@ def measure(w, config, flush, steps, warmup, chunk=None, fused=False, balanced=F
         ev[i][1].record(stream)
         if separate:
             dp.merge()
-        ev[i][2].record(stream)
+            ev[i][2].record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
-    step = [e[0].elapsed_time(e[2]) for e in ev]
+    # a call that merges by itself is one event pair: an empty pair e1..e2
+    # still reads ~5 us on this stack and would be charged to it
+    step = [e[0].elapsed_time(e[2] if separate else e[1]) for e in ev]
     attn = [e[0].elapsed_time(e[1]) for e in ev]
     merge = [e[1].elapsed_time(e[2]) for e in ev] if chunk > 0 and separate else [0.0]
     print(f"[bench] {w.name}: step {np.mean(step) * 1e3:.1f} us, attention {np.mean(attn) * 1e3:.1f} us",

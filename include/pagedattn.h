@@ -157,10 +157,28 @@ typedef struct pa_problem {
  *   least chunk_size keys.  Not with PA_FLAG_DEFER_MERGE (INVALID_ARG):
  *   split_kv_merge derives chunks from chunk_size.  Ignored when chunk_size
  *   is 0. */
+/* PA_FLAG_PERSISTENT: with chunk_size > 0, paged_attn_decode problems of at
+ *   most 32 packed rows (q_len * G) and head dims 64 or 128 run as one
+ *   persistent launch, after FlashInfer persistent.cuh
+ *   (BlockBatchPagedAttentionPersistent over a work list, then the reduction
+ *   of each row's partial states): exactly as many one-wave workgroups as the
+ *   device holds at once; the (request, KV head) key ranges are laid end to
+ *   end in 64-key tiles and wave w takes the tiles [w N / W, (w + 1) N / W),
+ *   with W = min(resident waves, N / (chunk_size / 64)), so no wave's share
+ *   is shorter than chunk_size keys and every wave gets the same work.  The
+ *   planner runs on the device from the lengths.  A share is cut at the end of
+ *   each (request, head) range into pieces whose partials the wave that
+ *   finishes a range's last piece merges in the same launch (as with
+ *   PA_FLAG_FUSED_MERGE, whose counters it uses: the workspace must start
+ *   zeroed and stays zeroed after every call).  The partial buffer holds
+ *   C_max + 1 slots.  Not with PA_FLAG_DEFER_MERGE or PA_FLAG_BALANCED_SPLIT
+ *   (INVALID_ARG); other problems (append, draft trees, wider rows, MLA) run
+ *   as without the flag.  Ignored when chunk_size is 0. */
 enum {
   PA_FLAG_DEFER_MERGE = 1,
   PA_FLAG_FUSED_MERGE = 2,
-  PA_FLAG_BALANCED_SPLIT = 4
+  PA_FLAG_BALANCED_SPLIT = 4,
+  PA_FLAG_PERSISTENT = 8
 };
 
 /*
@@ -170,10 +188,10 @@ enum {
  * normalized fp32 partial output row and one natural-log fp32 partial LSE per
  * chunk: [total_q, C_max, H_q, D_v] floats followed (256-byte aligned) by
  * [total_q, C_max, H_q] floats, with C_max = ceil((max_kv_len + max_q_len) /
- * chunk_size).  PA_FLAG_BALANCED_SPLIT puts 256 bytes of plan first; with
- * PA_FLAG_FUSED_MERGE the int32 merge counters [B, H_kv, ceil(max_q_len *
- * H_q / H_kv / 16)] come next, and the partials start at the next 256-byte
- * boundary.  This is the partial-buffer layout of FastDeploy
+ * chunk_size) (one more with PA_FLAG_PERSISTENT).  PA_FLAG_BALANCED_SPLIT puts
+ * 256 bytes of plan first; with PA_FLAG_FUSED_MERGE or PA_FLAG_PERSISTENT the
+ * int32 merge counters [B, H_kv, ceil(max_q_len * H_q / H_kv / 16)] come next,
+ * and the partials start at the next 256-byte boundary.  This is the partial-buffer layout of FastDeploy
  * append_attention_c8_impl.cuh (tmp_workspace / tmp_m / tmp_d, indexed
  * [token, chunk, head, dim]), with FlashInfer persistent.cuh's normalized
  * output + LSE pair in place of the (m, d) pair.  Returns 0 when chunk_size is

@@ -32,6 +32,7 @@ SCALE_PER_CHANNEL = 2
 FLAG_DEFER_MERGE = 1
 FLAG_FUSED_MERGE = 2
 FLAG_BALANCED_SPLIT = 4
+FLAG_PERSISTENT = 8
 
 GATHER_ROWS = 0       # one key row at a time
 GATHER_DECODE = 1     # the decode kernel's register tile loader

@@ -122,7 +122,8 @@ struct AttnConfig {
   int nt;           // 16-row MFMA tiles per wave
   int nw;           // waves per workgroup (they split the rows, share KV tiles)
   bool hilo;        // Q carries per-channel scales or is fp32: f16 hi + lo parts
-  int nstage;       // KV tiles staged in LDS (0: register-staged decode kernel, 1: MLA kernel)
+  int nstage;       // KV tiles staged in LDS (0: register-staged decode kernel, 1: MLA kernel,
+                    // 4: persistent register-staged decode kernel)
   bool f16_tiles;   // shared-tile kernel converts each tile to f16 in LDS once
   bool tree;        // draft-tree mask over the appended keys (decode-path kernels)
 };

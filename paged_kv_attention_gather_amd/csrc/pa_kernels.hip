@@ -1709,32 +1709,36 @@ struct RegTileLoader {
 // iteration to arrive while the register file, not LDS, holds the bytes in
 // flight.  K is then read back in the MFMA A-operand layout, V transposed.
 
+// LDS of one decode workgroup (KS waves).
+template <int D, int NT, int KS, bool TREE>
+struct DecodeLds {
+  __attribute__((aligned(1024))) uint8_t kv[KS][2][TK * D];   // per wave: K tile, V tile
+  float vscale[D];
+  float mrg_m[KS][16 * NT], mrg_l[KS][16 * NT];
+  uint32_t tree[TREE ? NT * 32 : 1];   // tree kernels run one wave per unit
+};
+
+// One decode unit u of (request b, KV head g), computed by the KS waves of the
+// workgroup (wave wv takes tiles wv, wv + KS, ...), written as final rows or
+// as the chunk's partial (merged in-kernel by the unit that finishes the row
+// tile last when p.merge_count is set).
 template <int D, bool FP8, int NT, bool HILO, int KS, bool TREE>
-__global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnParams p) {
+__device__ __forceinline__ void decode_unit(const AttnParams& p, int b, int g, const Unit& u, int lane, int wv,
+                                            DecodeLds<D, NT, KS, TREE>& sm) {
   constexpr int KPAIRS = D / 64;
   constexpr int MD = D / 16;
   constexpr int RPL = RegTileLoader<D>::RPL;   // rows per 1 KB wave load
   constexpr int NLD = RegTileLoader<D>::NLD;   // loads per tile (K or V)
   constexpr float KV_OFF = FP8 ? 0.f : 1152.f;
-
-  __shared__ __attribute__((aligned(1024))) uint8_t kvlds[KS][2][TK * D];   // per wave: K tile, V tile
-  __shared__ float vscale_lds[D];
-  __shared__ float mrg_m[KS][16 * NT], mrg_l[KS][16 * NT];
-
-  const int lane = threadIdx.x & 63;
-  const int wv = KS > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
+  auto& kvlds = sm.kv;
+  float* const vscale_lds = sm.vscale;
+  auto& mrg_m = sm.mrg_m;
+  auto& mrg_l = sm.mrg_l;
   uint8_t* const ktile = kvlds[wv][0];
   uint8_t* const vtile = kvlds[wv][1];
   const int l16 = lane & 15;
   const int grp = lane >> 4;
-  // grid = (B * H_kv, row tiles, chunks): chunk-major, so the empty units of
-  // short requests (chunks past their length) are dispatched last
-  const int b = (int)blockIdx.x / p.num_kv_heads;
-  const int g = (int)blockIdx.x % p.num_kv_heads;
-  const int rt = p.row_tiles - 1 - (int)blockIdx.y;  // long (late-token) row tiles first
-  const int c = (int)blockIdx.z;
-  Unit u;
-  if (!unit_setup<16 * NT>(p, b, rt, c, u)) return;
+  const int c = u.c;
   const int kv_lo = u.kv_lo, n_tiles = u.n_tiles;
   RegTileLoader<D> ld;
   ld.init(p, b, g, kv_lo, u.key_end, n_tiles, lane);
@@ -1776,8 +1780,7 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
   float vs_lane[D / 64];   // per-channel V scales (other modes re-read the first one)
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) vs_lane[i] = p.v_scale[fold_channel ? (int64_t)g * D + lane + 64 * i : 0];
-  __shared__ uint32_t tree_lds[TREE ? NT * 32 : 1];   // tree kernels run one wave per unit
-  uint32_t* const tb = tree_lds;
+  uint32_t* const tb = sm.tree;
   if constexpr (TREE) load_tree_bits<NT>(p, b, u, u.row0, lane, tb);
   load_tile(min(wv, n_tiles - 1));
   QT q;
@@ -1924,6 +1927,159 @@ __global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(
   }
   write_rows<D, NT>(p, u, g, c, lane, KV_OFF, q, st, vsc);
   merge_if_last<D, 16 * NT>(p, u, b, g, lane);   // wave 0 alone is left when KS > 1
+}
+
+template <int D, bool FP8, int NT, bool HILO, int KS, bool TREE>
+__global__ __launch_bounds__(64 * KS, NT == 1 ? 2 : 1) void paged_decode_kernel(AttnParams p) {
+  __shared__ DecodeLds<D, NT, KS, TREE> sm;
+  const int lane = threadIdx.x & 63;
+  const int wv = KS > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
+  // grid = (B * H_kv, row tiles, chunks): chunk-major, so the empty units of
+  // short requests (chunks past their length) are dispatched last
+  const int b = (int)blockIdx.x / p.num_kv_heads;
+  const int g = (int)blockIdx.x % p.num_kv_heads;
+  const int rt = p.row_tiles - 1 - (int)blockIdx.y;  // long (late-token) row tiles first
+  const int c = (int)blockIdx.z;
+  Unit u;
+  if (!unit_setup<16 * NT>(p, b, rt, c, u)) return;
+  decode_unit<D, FP8, NT, HILO, KS, TREE>(p, b, g, u, lane, wv, sm);
+}
+
+// ------------------------------------------------ persistent decode (F-3) --
+//
+// After FlashInfer persistent.cuh (BlockBatchPagedAttentionPersistent walks a
+// per-CTA work list of (request, head, KV range) items; the partial states of
+// each row are then reduced): a grid of exactly the resident wave capacity,
+// each workgroup one wave, walks an equal share of all KV tiles.  The
+// (request b, KV head g) segments are laid end to end in 64-key tiles:
+// segment (b, g) is tiles [S_b + g t_b, S_b + (g + 1) t_b) with t_b =
+// ceil(T_b / 64) and S_b = H_kv sum_{b' < b} t_b'.  Of the N tiles, wave w
+// takes [start(w), start(w + 1)) with start(w) = floor(w N / W); W = the
+// smaller of the grid and N / floor (floor = chunk_size / 64 tiles, the
+// shortest share), so the starts strictly increase.  A wave's share is cut
+// at segment ends into pieces; piece k of segment s is its k-th piece in tile
+// order, k = #{w : a_s < start(w) <= x} for a piece starting at tile x of a
+// segment starting at a_s, and segment s has 1 + #{w : a_s < start(w) <= e_s
+// - 1} pieces.  The planner runs in every wave from the lengths (no host
+// plan, no device-to-host copy); each piece is a decode unit whose partial
+// goes to slot k, and the wave finishing a segment's last piece merges it
+// (the in-kernel merge), so the call is one launch with no grid barrier.
+struct PersistentPlan {
+  int n;   // tiles of all segments (< 2^31, checked by the host)
+  int w;   // waves that take a share (<= gridDim.x, <= n)
+  __device__ __forceinline__ int start(int v) const { return (int)((int64_t)v * n / w); }
+  // waves whose start is at or before tile x (0 <= x < n)
+  __device__ __forceinline__ int count(int x) const {
+    return (int)min((int64_t)w, (((int64_t)x + 1) * w + n - 1) / n);
+  }
+};
+
+// The wave's walk through its share, kept in LDS between pieces (the decode
+// unit's body needs every register): the request block b0 .. b0 + 63 (lane l:
+// tiles t of request b0 + l and the inclusive prefix of H_kv * t over the
+// block, `base` = the tiles before b0), the next tile x and the share's end.
+struct PersistentLds {
+  int t[64], incl[64];
+  int b0, base, x, x_end;
+};
+
+// Loads the request block starting at b0 (lane-parallel prefix sum).
+__device__ __forceinline__ int seg_block(const AttnParams& p, int b0, int lane, int& t, int& incl) {
+  const int bb = b0 + lane;
+  const int n = p.q_len_uniform;
+  t = bb < p.batch && n > 0 ? (p.seq_lens_kv[bb] + n + TK - 1) / TK : 0;
+  incl = t * p.num_kv_heads;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  return __builtin_amdgcn_readlane(incl, 63);   // the block's tiles
+}
+
+template <int D, bool FP8, int NT, bool HILO>
+__global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void paged_decode_persistent_kernel(AttnParams p) {
+  __shared__ DecodeLds<D, NT, 1, false> sm;
+  __shared__ PersistentLds pl;
+  const int lane = threadIdx.x & 63;
+  const int H = p.num_kv_heads;
+  // total tiles (every wave computes the same sum)
+  int n_all = 0;
+  for (int b0 = 0; b0 < p.batch; b0 += 64) {
+    int t, incl;
+    n_all += seg_block(p, b0, lane, t, incl);
+  }
+  const int floor_tiles = max(1, p.chunk_size / TK);
+  PersistentPlan plan;
+  plan.n = n_all;
+  plan.w = min((int)gridDim.x, max(1, n_all / floor_tiles));
+  const int me = (int)blockIdx.x;
+  if (me >= plan.w || n_all == 0) return;
+  {
+    // the request block holding the share's first tile
+    const int x0 = plan.start(me);
+    int base = 0, b0 = 0, t = 0, incl = 0;
+    for (;; b0 += 64) {
+      const int tot = seg_block(p, b0, lane, t, incl);
+      if (x0 < base + tot || b0 + 64 >= p.batch) break;
+      base += tot;
+    }
+    pl.t[lane] = t;
+    pl.incl[lane] = incl;
+    if (lane == 0) {
+      pl.b0 = b0;
+      pl.base = base;
+      pl.x = x0;
+      pl.x_end = plan.start(me + 1);
+    }
+  }
+  for (;;) {
+    // the state comes back from LDS after every piece (nothing kept live
+    // across the unit's body)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    asm volatile("" ::: "memory");
+    const int x = pl.x, x_end = pl.x_end;
+    if (x >= x_end) break;
+    const int base = pl.base;
+    const uint64_t hit = __ballot(base + pl.incl[lane] > x);
+    if (hit == 0) {   // past this block: the next one
+      int t, incl;
+      const int tot = __builtin_amdgcn_readlane(pl.incl[lane], 63);
+      seg_block(p, pl.b0 + 64, lane, t, incl);
+      pl.t[lane] = t;
+      pl.incl[lane] = incl;
+      if (lane == 0) {
+        pl.b0 += 64;
+        pl.base = base + tot;
+      }
+      continue;
+    }
+    const int lb = (int)__builtin_ctzll(hit);
+    const int b = pl.b0 + lb;
+    const int t_b = __builtin_amdgcn_readlane(pl.t[lane], lb);
+    const int s_b = base + __builtin_amdgcn_readlane(pl.incl[lane], lb) - t_b * H;
+    const int g = (x - s_b) / t_b;
+    const int a = s_b + g * t_b;   // the segment is tiles [a, a + t_b)
+    const int piece_end = min(a + t_b, x_end);
+    if (lane == 0) pl.x = piece_end;
+    Unit u;
+    u.n = p.q_len_uniform;
+    u.tok0 = b * u.n;
+    u.G = p.group;
+    u.rows_total = u.n * u.G;
+    u.row0 = 0;
+    u.L = p.seq_lens_kv[b];
+    u.T = u.L + u.n;
+    u.c = plan.count(x) - plan.count(a);
+    u.n_chunks = 1 + plan.count(a + t_b - 1) - plan.count(a);
+    u.split = u.n_chunks > 1;
+    u.kv_lo = (x - a) * TK;
+    u.kv_hi = min(u.T, (piece_end - a) * TK);
+    u.key_end = p.causal ? min(u.kv_hi, u.L + u.n) : u.kv_hi;   // the last token sees every key
+    u.mask_from = p.causal ? min(u.kv_hi, u.L + 1) : u.kv_hi;
+    u.n_tiles = u.key_end > u.kv_lo ? (u.key_end - u.kv_lo + TK - 1) / TK : 0;
+    decode_unit<D, FP8, NT, HILO, 1, false>(p, b, g, u, lane, 0, sm);
+  }
 }
 
 // ------------------------------------------------------- MLA latent decode --
@@ -2463,6 +2619,16 @@ int occ_decode() {
   return occupancy_of(paged_decode_kernel<D, FP8, NT, HILO, KS, TREE>, 64 * KS);
 }
 
+template <int D, bool FP8, int NT, bool HILO>
+hipError_t launch_persistent_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((paged_decode_persistent_kernel<D, FP8, NT, HILO>), grid, dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+template <int D, bool FP8, int NT, bool HILO>
+int occ_persistent() {
+  return occupancy_of(paged_decode_persistent_kernel<D, FP8, NT, HILO>, 64);
+}
+
 struct Entry {
   AttnConfig cfg;
   LaunchFn fn;
@@ -2483,6 +2649,14 @@ struct Entry {
   Entry{AttnConfig{D, D, FP8, false, NT, KS, HL, 0, false, TR}, &launch_decode<D, FP8, NT, HL, KS, TR>, \
         &occ_decode<D, FP8, NT, HL, KS, TR>}
 #define PA_DEC(D, FP8, NT, HL, KS) PA_DEC_T(D, FP8, NT, HL, KS, false)
+// the persistent decode kernel (one wave per workgroup) is marked nstage == 4
+#define PA_PERSIST(D, FP8, NT, HL)                                                              \
+  Entry{AttnConfig{D, D, FP8, false, NT, 1, HL, 4, false, false}, &launch_persistent_one<D, FP8, NT, HL>, \
+        &occ_persistent<D, FP8, NT, HL>}
+#define PA_PERSIST_SET(D)                                                                        \
+  PA_PERSIST(D, false, 1, false), PA_PERSIST(D, false, 1, true), PA_PERSIST(D, true, 1, false),     \
+      PA_PERSIST(D, true, 1, true), PA_PERSIST(D, false, 2, false), PA_PERSIST(D, false, 2, true),  \
+      PA_PERSIST(D, true, 2, false), PA_PERSIST(D, true, 2, true)
 // the MLA kernel (4 waves and 64 rows) is marked nstage == 1
 #define PA_MLA(FP8, HL) \
   Entry{AttnConfig{576, 512, FP8, true, 1, MLA_WAVES, HL, 1, false, false}, &launch_mla<FP8, HL>, &occ_mla<FP8, HL>}
@@ -2508,6 +2682,7 @@ const Entry kTable[] = {
     PA_TREE_SET(64, true, false),   PA_TREE_SET(64, true, true),
     PA_TREE_SET(128, false, false), PA_TREE_SET(128, false, true),
     PA_TREE_SET(128, true, false),  PA_TREE_SET(128, true, true),
+    PA_PERSIST_SET(64), PA_PERSIST_SET(128),
 };
 
 const Entry* find_entry(const AttnConfig& c) {

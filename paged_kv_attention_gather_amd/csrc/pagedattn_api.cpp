@@ -68,8 +68,12 @@ int32_t check_problem(const pa_problem* p) {
                 p->head_dim_qk, p->head_dim_v);
   if (log2_exact(p->page_size) < 0 || p->page_size < 16 || p->page_size > 1024)
     return fail(PA_ERR_UNSUPPORTED, "page_size %d must be a power of two in [16, 1024]", p->page_size);
-  if (p->flags & ~(PA_FLAG_DEFER_MERGE | PA_FLAG_FUSED_MERGE | PA_FLAG_BALANCED_SPLIT))
+  if (p->flags & ~(PA_FLAG_DEFER_MERGE | PA_FLAG_FUSED_MERGE | PA_FLAG_BALANCED_SPLIT | PA_FLAG_PERSISTENT))
     return fail(PA_ERR_INVALID_ARG, "unknown flag bits 0x%x", p->flags);
+  if ((p->flags & PA_FLAG_PERSISTENT) && (p->flags & (PA_FLAG_DEFER_MERGE | PA_FLAG_BALANCED_SPLIT)))
+    return fail(PA_ERR_INVALID_ARG,
+                "PA_FLAG_PERSISTENT merges in the launch and plans its own split: not with PA_FLAG_DEFER_MERGE or "
+                "PA_FLAG_BALANCED_SPLIT");
   if ((p->flags & PA_FLAG_DEFER_MERGE) && (p->flags & PA_FLAG_BALANCED_SPLIT))
     return fail(PA_ERR_INVALID_ARG,
                 "PA_FLAG_BALANCED_SPLIT cuts chunks split_kv_merge cannot derive: not with PA_FLAG_DEFER_MERGE");
@@ -115,7 +119,10 @@ int64_t device_capacity(const pa::AttnConfig& cfg) {
 
 int64_t max_chunks_of(const pa_problem* p) {
   if (p->chunk_size <= 0) return 1;
-  return std::max<int64_t>(1, ceil_div((int64_t)p->max_kv_len + p->max_q_len, p->chunk_size));
+  const int64_t c = std::max<int64_t>(1, ceil_div((int64_t)p->max_kv_len + p->max_q_len, p->chunk_size));
+  // the persistent split cuts a range into at most one piece more than
+  // fixed chunks would (its shares are at least chunk_size keys long)
+  return (p->flags & PA_FLAG_PERSISTENT) ? c + 1 : c;
 }
 
 // Waves that split one unit's key range in the register-staged decode kernel.
@@ -156,7 +163,7 @@ WorkspaceLayout workspace_layout(const pa_problem* p, int64_t total_q) {
   const int64_t mc = max_chunks_of(p);
   if (p->flags & PA_FLAG_BALANCED_SPLIT) w.plan_bytes = 256;
   w.count_offset = w.plan_bytes;
-  if (p->flags & PA_FLAG_FUSED_MERGE)
+  if (p->flags & (PA_FLAG_FUSED_MERGE | PA_FLAG_PERSISTENT))
     w.count_bytes = (size_t)p->batch * p->num_kv_heads * count_stride_of(p) * sizeof(int32_t);
   w.part_o_offset = (w.count_offset + w.count_bytes + 255) & ~size_t(255);
   w.part_o_bytes = (size_t)total_q * mc * p->num_q_heads * p->head_dim_v * sizeof(float);
@@ -228,6 +235,10 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
                   (long long)rows_max);
   }
 
+  // The persistent decode kernel (PA_FLAG_PERSISTENT): decode problems of at
+  // most 32 packed rows (one wave holds all of a request-head's rows).
+  const bool persistent = (p->flags & PA_FLAG_PERSISTENT) && p->chunk_size > 0 && decode && !tree_mask &&
+                          !shared && rows_max <= 32;
   pa::AttnConfig cfg{};
   cfg.tree = tree_mask != nullptr;
   cfg.dqk = p->head_dim_qk;
@@ -255,9 +266,16 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
     cfg.f16_tiles = cfg.dqk == 128;
     cfg.nstage = cfg.f16_tiles ? 3 : 2;
   }
+  if (persistent) {
+    cfg.nw = 1;
+    cfg.nstage = 4;
+  }
   if (!pa::attention_supported(cfg))
     return fail(PA_ERR_UNSUPPORTED, "no compiled kernel for this configuration");
-  const int64_t rows_per_wg = 16LL * cfg.nt * (cfg.nstage == 0 ? 1 : cfg.nw);  // decode: nw splits keys
+  if (persistent &&
+      ceil_div((int64_t)p->max_kv_len + p->max_q_len, kTileKeys) * p->num_kv_heads * p->batch > 0x7fffffffLL)
+    return fail(PA_ERR_UNSUPPORTED, "PA_FLAG_PERSISTENT: more than 2^31 - 1 tiles in the call");
+  const int64_t rows_per_wg = 16LL * cfg.nt * (cfg.nstage == 0 || cfg.nstage == 4 ? 1 : cfg.nw);  // decode: nw splits keys
   const int64_t row_tiles = ceil_div(rows_max, rows_per_wg);
   const int64_t max_chunks = max_chunks_of(p);
   if (row_tiles > 65535 || max_chunks > 65535 ||
@@ -301,7 +319,7 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   // the decode kernel, the one that compiles the merge tail (in the
   // shared-tile and MLA kernels it cost SGPR spills in the main loop, and
   // the host never picks the in-kernel merge for their wide tiles).
-  bool fused = wl.count_bytes > 0;
+  bool fused = wl.count_bytes > 0 && !persistent;
   if (fused) {
     const int64_t unit_rows = std::min<int64_t>(rows_max, 16LL * cfg.nt * (cfg.nstage == 0 ? 1 : cfg.nw));
     const int64_t merge_threads = 64LL * (cfg.nstage == 0 ? 1 : cfg.nw);   // decode: wave 0 merges
@@ -309,7 +327,8 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
     if (p->merge_in_kernel != 0) fused = p->merge_in_kernel == 1;
     fused = fused && cfg.nstage == 0;
   }
-  ap.merge_count = fused ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.count_offset) : nullptr;
+  ap.merge_count = fused || persistent ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + wl.count_offset)
+                                       : nullptr;
   ap.count_stride = (int32_t)count_stride_of(p);
   ap.q_row_stride = p->q_row_stride;
   ap.k_stride_page = p->k_stride_page;
@@ -348,7 +367,13 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   // CUs would run a second, mostly idle round); deeper grids balance by dispatch.
   // pa_problem.group_order (1 = grid slots, 2 = compact) fixes the choice.
   // The device's capacity is asked once per device and kernel, then cached.
-  const int64_t capacity = decode_kernel ? 0 : device_capacity(cfg);
+  const int64_t capacity = decode_kernel && !persistent ? 0 : device_capacity(cfg);
+  if (persistent) {
+    // one wave per workgroup, exactly the resident capacity
+    if (capacity <= 0 || capacity > 0x7fffffffLL)
+      return fail(PA_ERR_HIP, "PA_FLAG_PERSISTENT: the device's resident capacity could not be determined");
+    grid = dim3((unsigned)capacity, 1, 1);
+  }
   ap.compact_groups = 0;
   if (p->group_order != 0) {
     ap.compact_groups = p->group_order == 2;
@@ -381,7 +406,7 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   }
   hipError_t e = pa::launch_attention(cfg, ap, grid, s);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
-  if (p->chunk_size > 0 && !(p->flags & PA_FLAG_DEFER_MERGE) && !fused) {
+  if (p->chunk_size > 0 && !(p->flags & PA_FLAG_DEFER_MERGE) && !fused && !persistent) {
     pa::MergeParams mp{};
     mp.part_o = ap.part_o;
     mp.part_lse = ap.part_lse;

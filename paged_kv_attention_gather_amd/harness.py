@@ -42,7 +42,7 @@ class DeviceProblem:
     """Device tensors of a workload plus its outputs and workspace."""
 
     def __init__(self, w, device="cuda", chunk_size=None, decode=None, defer_merge=False, fused_merge=False,
-                 balanced=False, schedule=None):
+                 balanced=False, schedule=None, persistent=False):
         import torch
         self.torch = torch
         self.w = w
@@ -63,7 +63,7 @@ class DeviceProblem:
         tm = getattr(w, "tree_mask", None)
         self.tree_mask = None if tm is None else torch.from_numpy(np.ascontiguousarray(tm, dtype=np.uint8)).to(dev)
         flags = ((L.FLAG_DEFER_MERGE if defer_merge else 0) | (L.FLAG_FUSED_MERGE if fused_merge else 0) |
-                 (L.FLAG_BALANCED_SPLIT if balanced else 0))
+                 (L.FLAG_BALANCED_SPLIT if balanced else 0) | (L.FLAG_PERSISTENT if persistent else 0))
         self.prob = problem_for(w, chunk_size=chunk_size, flags=flags)
         for k, v in (schedule or {}).items():   # pa_problem schedule overrides
             if k not in L.SCHEDULE_FIELDS:
@@ -74,7 +74,7 @@ class DeviceProblem:
         self.lse = torch.empty((self.total_q, w.num_q_heads), dtype=torch.float32, device=dev)
         ws = L.workspace_size(self.prob, self.total_q)
         # the in-kernel merge's counters must start at zero (each call leaves them zero)
-        alloc = torch.zeros if fused_merge else torch.empty
+        alloc = torch.zeros if fused_merge or persistent else torch.empty
         self.workspace = alloc(max(ws, 256), dtype=torch.uint8, device=dev) if ws else None
         self.workspace_bytes = ws
 

@@ -71,7 +71,7 @@ def test_flag_values_match_header():
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     flags = dict((k, int(v)) for k, v in re.findall(r"PA_FLAG_([A-Z_]+)\s*=\s*(\d+)", text))
     assert flags == {"DEFER_MERGE": L.FLAG_DEFER_MERGE, "FUSED_MERGE": L.FLAG_FUSED_MERGE,
-                     "BALANCED_SPLIT": L.FLAG_BALANCED_SPLIT}
+                     "BALANCED_SPLIT": L.FLAG_BALANCED_SPLIT, "PERSISTENT": L.FLAG_PERSISTENT}
 
 
 def test_workspace_size_formula(lib):
@@ -102,6 +102,11 @@ def test_workspace_size_with_fused_merge_counters(lib):
     both = base_problem(flags=L.FLAG_FUSED_MERGE | L.FLAG_BALANCED_SPLIT)
     assert P.workspace_size(both, total_q) == 256 + (counters + 255) // 256 * 256 + plain
     assert P.workspace_size(base_problem(flags=L.FLAG_BALANCED_SPLIT), total_q) == 256 + plain
+    # the persistent split: the counters and one partial slot more per (token, head)
+    mc = -(-(900 + 4) // 256) + 1
+    po = total_q * mc * 8 * 128 * 4
+    pers = (counters + 255) // 256 * 256 + (po + 255) // 256 * 256 + total_q * mc * 8 * 4
+    assert P.workspace_size(base_problem(flags=L.FLAG_PERSISTENT), total_q) == pers
 
 
 def _decode(prob, q_len=1, workspace=None, ws_bytes=0, **ptrs):
@@ -136,7 +141,9 @@ def _append(prob, total_q=8, workspace=None, ws_bytes=0, **ptrs):
     (dict(k_stride_token=120), L.PA_ERR_INVALID_ARG),             # not 16-byte multiple
     (dict(batch=-1), L.PA_ERR_INVALID_ARG),
     (dict(batch=70000), L.PA_ERR_UNSUPPORTED),
-    (dict(flags=8), L.PA_ERR_INVALID_ARG),                        # unknown flag bit
+    (dict(flags=16), L.PA_ERR_INVALID_ARG),                       # unknown flag bit
+    (dict(flags=9), L.PA_ERR_INVALID_ARG),                        # persistent with a deferred merge
+    (dict(flags=12), L.PA_ERR_INVALID_ARG),                       # persistent with the balanced split
     (dict(flags=3), L.PA_ERR_INVALID_ARG),                        # deferred and fused merge together
     (dict(flags=5), L.PA_ERR_INVALID_ARG),                        # deferred merge of a balanced split
     (dict(decode_waves=3), L.PA_ERR_INVALID_ARG),                 # schedule overrides: 0 or a listed value

@@ -555,6 +555,55 @@ def test_balanced_split_full_config(idx):
     compare(out, lse, O_ref, lse_ref, what=f"{w.name} balanced, every request")
 
 
+# ---------------------------------------------------- persistent decode --
+#
+# PA_FLAG_PERSISTENT: one launch of resident-capacity waves, each taking an
+# equal share of all (request, KV head) tiles (at least chunk_size keys), the
+# pieces' partials merged by the wave that finishes each range last.  Any cut
+# merges to the same exact attention, so the outputs are checked against the
+# oracle; each case runs twice on one workspace (the counters must be back at
+# zero) and the second call must give the same bits.
+PERSISTENT_CASES = {
+    "decode_g4_chunk64": FUSED_CASES["decode_g4_chunk64"],
+    "decode_nt2_q8_g4": FUSED_CASES["decode_nt2_q8_g4"],
+    "decode_page16_chunk64": EDGE_CASES["decode_page16_chunk64"],
+    "decode_d64_fp8_tensor": EDGE_CASES["decode_d64_fp8_tensor"],
+    "decode_q8_g8": dict(num_q_heads=8, num_kv_heads=2, q_lens=[8, 8, 8], seq_lens_kv=[0, 500, 1300], decode=True,
+                         chunk_size=128),
+    "decode_noncausal_drafts": EDGE_CASES["decode_noncausal_drafts"],
+    "decode_f32_query_head": dict(q_dtype="f32", scale_mode="head", q_lens=[2, 2, 2, 2], seq_lens_kv=[1, 64, 65, 900],
+                                  decode=True, chunk_size=64),
+    "decode_many_requests": dict(q_lens=[1] * 70, seq_lens_kv=[(37 * i) % 700 for i in range(70)], decode=True,
+                                 chunk_size=64),
+}
+
+
+@pytest.mark.parametrize("case", sorted(PERSISTENT_CASES))
+def test_persistent_decode_parity(case):
+    need_gpu()
+    w = _edge(case, **PERSISTENT_CASES[case])
+    announce(f"persistent decode {case}")
+    dp, (out, lse) = _run(w, persistent=True)
+    O_ref, lse_ref = oracle.attention(w)
+    n = int(w.q_lens.sum())
+    compare(out[:n], lse[:n], O_ref[:n], lse_ref[:n], what=f"{case} persistent")
+    cnt = dp.workspace[:4 * _counter_words(dp.prob)].view(dp.torch.int32)
+    assert int(cnt.abs().sum().item()) == 0, "merge counters not reset"
+    dp.out.zero_()
+    dp.run()
+    again = dp.outputs()
+    assert np.array_equal(out, again[0]) and np.array_equal(lse, again[1]), "second call differs"
+
+
+def test_persistent_decode_full_workload():
+    need_gpu()
+    w = config_workload(2)
+    announce("persistent decode on the full decode workload (every request)")
+    _, (out, lse) = _run(w, persistent=True)
+    O_ref, lse_ref = oracle_every_request(2)
+    compare(out, lse, O_ref, lse_ref, what="decode_int8 persistent, every request")
+
+
 # ----------------------------------------------------- full-size workloads --
 
 @pytest.mark.parametrize("idx", [2, 3, 4, 5])
