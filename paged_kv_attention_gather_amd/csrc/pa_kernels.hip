@@ -806,6 +806,65 @@ __device__ __forceinline__ void query_digits(float (&xq)[DQK / 64][16], int nt, 
   }
 }
 
+// QRowsI8 of one 16-row tile for long heads (the MLA kernel's 576 dims): the
+// row is read twice (maximum, then digits), lane l taking dims 64 s + 16
+// (l / 16) + [0, 16) of row l % 16, with per-channel K scales and sm_scale *
+// log2(e) folded in when K is per channel.
+template <int DQK>
+__device__ __forceinline__ void load_query_i8(const AttnParams& p, const Unit& u, int g, int row_base, int lane,
+                                              QRowsI8<DQK, 1>& q) {
+  constexpr int KSTEPS = DQK / 64;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int mode = p.scale_mode;
+  const bool fold_channel = mode == PA_SCALE_PER_CHANNEL;
+  const float k_uniform = fold_channel ? 1.f : p.k_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
+  const int r = row_base + l16;
+  q.ok[0] = r < u.rows_total;
+  const int t = q.ok[0] ? r / u.G : 0;
+  q.tok[0] = t;
+  q.head[0] = g * u.G + (q.ok[0] ? r % u.G : 0);
+  const int64_t qoff = (int64_t)(u.tok0 + t) * p.q_row_stride + (int64_t)q.head[0] * DQK;
+  float xq[KSTEPS][16];
+#pragma unroll
+  for (int sp = 0; sp < KSTEPS; ++sp) {
+    const int d0 = 64 * sp + 16 * grp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) xq[sp][e] = 0.f;
+    if (q.ok[0]) {
+      if (p.q_is_f32) {
+        const float4_t* src = (const float4_t*)((const float*)p.q + qoff + d0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float4_t f = src[v];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xq[sp][4 * v + e] = f[e];
+        }
+      } else {
+        const uint4_t* src = (const uint4_t*)((const uint16_t*)p.q + qoff + d0);
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          const uint4_t w = src[v];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xq[sp][8 * v + 2 * e] = bf16_to_f32((uint16_t)(w[e] & 0xffffu));
+            xq[sp][8 * v + 2 * e + 1] = bf16_to_f32((uint16_t)(w[e] >> 16));
+          }
+        }
+      }
+      if (fold_channel) {
+        const float4_t* sc = (const float4_t*)(p.k_scale + (int64_t)g * DQK + d0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float4_t f = sc[v];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xq[sp][4 * v + e] *= p.qk_mult * f[e];
+        }
+      }
+    }
+  }
+  query_digits<DQK, 1>(xq, 0, fold_channel ? 1.f : p.qk_mult * k_uniform, q);
+}
+
 // query_finish for the int8 MFMA (see QRowsI8).
 template <int DQK, int NT>
 __device__ __forceinline__ void query_finish_i8(const AttnParams& p, const Unit& u, int g, int row_base,
@@ -839,6 +898,123 @@ __device__ __forceinline__ void query_finish_i8(const AttnParams& p, const Unit&
       }
     query_digits<DQK, NT>(xq, nt, fold_channel ? 1.f : p.qk_mult * k_uniform, q);
   }
+}
+
+// Query rows for S^T = K Q^T on the fp8 MFMA (v_mfma_scale_f32_16x16x128_
+// f8f6f4, unit scales), used with e4m3fn caches: the K bytes go to the MFMA as
+// they are, and each query row, scaled by a power of two that puts its
+// largest element in [64, 128), is split into ND e4m3fn digits q = d_0 + ...
+// + d_{ND-1}, each the nearest e4m3fn value to what the previous digits left.
+// A bf16 value (8 significant bits) is two 4-bit digits exactly, unless the
+// second digit falls below e4m3fn's subnormal step 2^-9 (elements under 2^-16
+// of the row maximum); fp32 queries and per-channel folded scales take three
+// digits (2^-12 relative per element).  Lane l holds, per 128-dim step s,
+// bytes for dims 128 s + 32 (l / 16) + [0, 32) of row l % 16 (the operand
+// layout of the instruction: A and B rows by lane % 16, 32 consecutive k per
+// lane group), zero past the head dim.
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+template <int DQK, int ND>
+struct QRowsF8 {
+  static constexpr int STEPS = (DQK + 127) / 128;
+  v8i_t qd[ND][STEPS];
+  float row_mult[1];
+  float kbias[1];   // 0: K operands are exact
+  int tok[1], head[1];
+  bool ok[1];
+};
+
+template <int DQK, int ND>
+__device__ __forceinline__ void load_query_f8(const AttnParams& p, const Unit& u, int g, int row_base, int lane,
+                                              QRowsF8<DQK, ND>& q) {
+  constexpr int STEPS = QRowsF8<DQK, ND>::STEPS;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int mode = p.scale_mode;
+  const bool fold_channel = mode == PA_SCALE_PER_CHANNEL;
+  const float k_uniform = fold_channel ? 1.f : p.k_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
+  const int r = row_base + l16;
+  q.ok[0] = r < u.rows_total;
+  const int t = q.ok[0] ? r / u.G : 0;
+  q.tok[0] = t;
+  q.head[0] = g * u.G + (q.ok[0] ? r % u.G : 0);
+  const int64_t qoff = (int64_t)(u.tok0 + t) * p.q_row_stride + (int64_t)q.head[0] * DQK;
+  // element j of step s: dim 128 s + 32 grp + j (8 at a time)
+  auto load8 = [&](int s, int j8, float* x) {
+    const int d0 = 128 * s + 32 * grp + 8 * j8;
+    if (!q.ok[0] || d0 >= DQK) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      return;
+    }
+    if (p.q_is_f32) {
+      const float4_t* src = (const float4_t*)((const float*)p.q + qoff + d0);
+      const float4_t a = src[0], b = src[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+    } else {
+      const uint4_t w = *(const uint4_t*)((const uint16_t*)p.q + qoff + d0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf16_to_f32((uint16_t)(w[e] & 0xffffu));
+        x[2 * e + 1] = bf16_to_f32((uint16_t)(w[e] >> 16));
+      }
+    }
+    if (fold_channel) {
+      const float4_t* sc = (const float4_t*)(p.k_scale + (int64_t)g * DQK + d0);
+      const float4_t a = sc[0], b = sc[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { x[e] *= p.qk_mult * a[e]; x[4 + e] *= p.qk_mult * b[e]; }
+    }
+  };
+  float amax = 0.f;
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+    for (int j8 = 0; j8 < 4; ++j8) {
+      float x[8];
+      load8(s, j8, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+      __builtin_amdgcn_sched_barrier(0);   // keep the row's loads from piling up in registers
+    }
+  amax = row_max4(amax);
+  int ex = 0;
+  if (amax > 0.f) (void)frexpf(amax, &ex);      // amax < 2^ex
+  const int k2 = min(max(7 - ex, -120), 120);   // largest element in [64, 128)
+  const float up = ldexpf(1.f, k2);
+  q.row_mult[0] = ldexpf(1.f, -k2) * (fold_channel ? 1.f : p.qk_mult * k_uniform);
+  q.kbias[0] = 0.f;
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+    for (int j8 = 0; j8 < 4; ++j8) {
+      float x[8];
+      load8(s, j8, x);
+      uint32_t w[ND][2] = {};
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float r0 = x[e] * up, r1 = x[e + 1] * up;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          // two e4m3fn (OCP) codes in one 16-bit half, and their exact values
+          typedef short short2_t __attribute__((ext_vector_type(2)));
+          const short2_t zero2 = {0, 0};
+          const uint32_t pk =
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(zero2, r0, r1, 1.0f, false)) &
+              0xffffu;
+          const auto back = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)pk, 1.0f, false);
+          r0 -= back[0];
+          r1 -= back[1];
+          w[d][(e / 2) >> 1] |= pk << (16 * ((e / 2) & 1));
+        }
+      }
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        q.qd[d][s][2 * j8] = (int)w[d][0];
+        q.qd[d][s][2 * j8 + 1] = (int)w[d][1];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // S^T += K Q^T over one 64-dim step on the int8 MFMA: `a` holds the lane's 16
@@ -1225,7 +1401,9 @@ __device__ __forceinline__ void merge_if_last(const AttnParams& p, const Unit& u
 // waves of a workgroup split the tile's 1 KB blocks: block j*NW + wave of K,
 // then of V.  Page ids, the one-page fast path and the clamped general path
 // are as in RegTileLoader.
-template <int KROW, int VROW, int NW, bool SHARED>
+// HOLD: keep each DMA's per-lane source offset in a register (else recompute
+// it at every issue, for kernels short of registers).
+template <int KROW, int VROW, int NW, bool SHARED, bool HOLD = true>
 struct DmaTileLoader {
   static constexpr int KTILE = TK * KROW;
   static constexpr int VTILE = SHARED ? 0 : TK * VROW;
@@ -1241,7 +1419,21 @@ struct DmaTileLoader {
   int pw_base, pw_val;
   bool one_page, fast_addr;
   uint32_t smem_base;
-  uint32_t koff[K_DMA], voff[V_DMA > 0 ? V_DMA : 1];
+  uint32_t koff[HOLD ? K_DMA : 1], voff[HOLD && V_DMA > 0 ? V_DMA : 1];
+  int64_t ks_tok, vs_tok;
+
+  __device__ __forceinline__ uint32_t k_offset(int j) const {
+    if constexpr (HOLD) return koff[j];
+    const int ch = (j * NW + wave) * 64 + (int)(threadIdx.x & 63);
+    const int row = ch / KCPR;
+    return (uint32_t)(row * ks_tok + swz<KROW>(ch % KCPR, row) * 16);
+  }
+  __device__ __forceinline__ uint32_t v_offset(int j) const {
+    if constexpr (HOLD) return voff[j];
+    const int ch = (j * NW + wave) * 64 + (int)(threadIdx.x & 63);
+    const int row = ch / VCPR;
+    return (uint32_t)(row * vs_tok + swz<VROW>(ch % VCPR, row) * 16);
+  }
 
   __device__ __forceinline__ void init(const AttnParams& p, int b, int g_, int wave_, int kv_lo_, int key_end_,
                                        int n_tiles, int lane, uint32_t smem_base_) {
@@ -1258,17 +1450,21 @@ struct DmaTileLoader {
     fast_addr = one_page && (int64_t)TK * p.k_stride_token < (1LL << 30) &&
                 (SHARED || (int64_t)TK * p.v_stride_token < (1LL << 30));
     smem_base = smem_base_;
+    ks_tok = p.k_stride_token;
+    vs_tok = p.v_stride_token;
+    if constexpr (HOLD) {
 #pragma unroll
-    for (int j = 0; j < K_DMA; ++j) {
-      const int ch = (j * NW + wave) * 64 + lane;
-      const int row = ch / KCPR;
-      koff[j] = (uint32_t)(row * p.k_stride_token + swz<KROW>(ch % KCPR, row) * 16);
-    }
+      for (int j = 0; j < K_DMA; ++j) {
+        const int ch = (j * NW + wave) * 64 + lane;
+        const int row = ch / KCPR;
+        koff[j] = (uint32_t)(row * p.k_stride_token + swz<KROW>(ch % KCPR, row) * 16);
+      }
 #pragma unroll
-    for (int j = 0; j < V_DMA; ++j) {
-      const int ch = (j * NW + wave) * 64 + lane;
-      const int row = ch / VCPR;
-      voff[j] = (uint32_t)(row * p.v_stride_token + swz<VROW>(ch % VCPR, row) * 16);
+      for (int j = 0; j < V_DMA; ++j) {
+        const int ch = (j * NW + wave) * 64 + lane;
+        const int row = ch / VCPR;
+        voff[j] = (uint32_t)(row * p.v_stride_token + swz<VROW>(ch % VCPR, row) * 16);
+      }
     }
   }
 
@@ -1290,13 +1486,13 @@ struct DmaTileLoader {
                                     p.k_stride_token);
 #pragma unroll
       for (int j = 0; j < K_DMA; ++j)
-        if ((j * NW + wave) * 64 < KCH) dma16_s(koff[j], kb, kdst + (j * NW + wave) * 1024);
+        if ((j * NW + wave) * 64 < KCH) dma16_s(k_offset(j), kb, kdst + (j * NW + wave) * 1024);
       if constexpr (!SHARED) {
         const uint8_t* vb = paged_row(p.v_cache, pp0, kbase, page_shift, g, p.v_stride_page, p.v_stride_head,
                                       p.v_stride_token);
 #pragma unroll
         for (int j = 0; j < V_DMA; ++j)
-          if ((j * NW + wave) * 64 < VCH) dma16_s(voff[j], vb, vdst + (j * NW + wave) * 1024);
+          if ((j * NW + wave) * 64 < VCH) dma16_s(v_offset(j), vb, vdst + (j * NW + wave) * 1024);
       }
       return;
     }
@@ -2390,6 +2586,521 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams
   }
 }
 
+// MLA, second form: no f16 copy of the tile.  The raw 64 x 576 tile arrives
+// by LDS DMA into a three-stage ring (two tiles ahead).  Phase A (wave w, rows
+// 16w..16w+15) feeds the raw K bytes to the MFMA as they are: e4m3fn keys to
+// the fp8 MFMA against the query in fp8 digits (QRowsF8), int8 keys to the
+// int8 MFMA against three int8 digits (QRowsI8); converting K to f16 costs a
+// quarter-rate conversion per two values, about 3x the MFMA time of the tile.
+// The softmax writes P^T and the per-row rescale factors to LDS.  Phase B (wave w, output dims 128w..128w+127 of all 64 rows) reads
+// V^T from the same raw rows with the 8-bit LDS transpose read and converts
+// it in registers (int8 V as the offset value 1152 + x, removed in the
+// epilogue).  Two barriers per tile: the tile has landed for every wave (and
+// the stage two tiles back is free again), then P^T is complete.
+template <bool FP8, bool HILO, bool BAL>
+__global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla2_kernel(AttnParams p) {
+  constexpr int DQK = 576, DV = 512, NW = MLA_WAVES;
+  constexpr int ROWS = 16 * NW;                   // 64 packed rows per workgroup
+  constexpr int NTB = ROWS / 16;                  // row tiles in phase B
+  constexpr int MDW = DV / 16 / NW;               // output-dim tiles per wave (8)
+  constexpr int KROW = DQK;
+  constexpr int KTILE = TK * KROW;                // 36 KB raw tile
+  constexpr int NSTAGE = 3;
+  constexpr int SP = DQK / 64;                    // 64-dim steps of S^T (9)
+  constexpr float KV_OFF = FP8 ? 0.f : 1152.f;    // int8 V operands carry 1152 + x
+  using LD = DmaTileLoader<KROW, KROW, NW, true>;
+  static_assert(LD::KCH % (64 * NW) == 0, "every wave issues the same number of DMA blocks");
+  constexpr int DMA_W = LD::K_DMA;                // per wave per tile
+
+  __shared__ __attribute__((aligned(1024))) uint8_t kst[NSTAGE * KTILE];   // raw tiles
+  __shared__ __attribute__((aligned(16))) half8_t pt_lds[NTB * 2 * 64];    // P^T operands
+  __shared__ float alpha_lds[ROWS];
+  __shared__ float lrow_lds[ROWS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;
+  int b, g;
+  Unit u;
+  if (!shared_tile_unit<ROWS, BAL>(p, b, g, u)) return;   // a chunk's row tiles share an XCD
+  const int kv_lo = u.kv_lo, n_tiles = u.n_tiles;
+  LD ld;
+  ld.init(p, b, g, wave, kv_lo, u.key_end, n_tiles, lane, lds_addr(kst));
+#pragma unroll
+  for (int st = 0; st < NSTAGE - 1; ++st)
+    if (st < n_tiles) ld.issue(p, st, st);
+
+  // S^T runs on the fp8 MFMA (e4m3fn caches, query in fp8 digits) or the
+  // int8 MFMA (int8 caches, query in three int8 digits): K bytes go to the
+  // MFMA as they are stored, with no conversion.
+  constexpr int ND = HILO ? 3 : 2;
+  using QT = typename std::conditional<FP8, QRowsF8<DQK, ND>, QRowsI8<DQK, 1>>::type;
+  QT q;
+  if constexpr (FP8) load_query_f8<DQK, ND>(p, u, g, u.row0 + wave * 16, lane, q);
+  else load_query_i8<DQK>(p, u, g, u.row0 + wave * 16, lane, q);
+  SoftmaxState<1, 0> sa;   // phase-A row state (m, l); O lives in phase B
+  softmax_init(sa);
+  float4_t o[MDW][NTB];    // dims 16*(MDW*wave + md) + 4*grp + i, row 16*nt + l16
+#pragma unroll
+  for (int md = 0; md < MDW; ++md)
+#pragma unroll
+    for (int nt = 0; nt < NTB; ++nt) o[md][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // phase A: lane reads key mt*16 + l16, chunk 4*sp + grp (dims 64sp + 16grp .. +16)
+  int ka_off[4][2];   // row offset and swizzle term per key tile (swz<576> depends on key % 32)
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int key = mt * 16 + l16;
+    ka_off[mt][0] = key * KROW;
+    ka_off[mt][1] = key;
+  }
+  // phase B: the tr8 read of V^T (see pv_tile): lanes 2j, 2j+1 of a 16-lane
+  // group read the halves of key row kappa(grp, j)
+  const int jr = l16 >> 1, hlf = lane & 1;
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const int stage = it % NSTAGE;
+    // this wave's DMA of tile it + 1 may stay in flight
+    if (it + 1 < n_tiles) wait_vmcnt<DMA_W>();
+    else wait_vmcnt<0>();
+    __syncthreads();   // X: tile it landed; every wave is done with phase B of it - 1
+    if (it + NSTAGE - 1 < n_tiles) ld.issue(p, it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
+    const uint8_t* ks = kst + stage * KTILE;
+    const int kbase = kv_lo + it * TK;
+
+    // ---- phase A: S^T = K Q^T for this wave's rows, K bytes straight to the MFMA ----
+    float4_t s[4][1];
+    if constexpr (FP8) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) s[mt][0] = float4_t{0.f, 0.f, 0.f, 0.f};
+      // lane: key mt*16 + l16, bytes 128 st + 32 grp .. + 32 (chunks 8 st + 2 grp, + 1);
+      // dims past 576 (the second half of the last step) are zero operands
+      constexpr int STEPS = QRowsF8<DQK, ND>::STEPS;
+      // dims 576..639 of the last step are zero operands: those lanes read
+      // the row's last two chunks (valid bytes) and drop them, with no branch,
+      // so that phase A stays one scheduling region
+      auto read_k = [&](int st, int mt) {
+        const int key = mt * 16 + l16;
+        const bool live = st * 128 + 32 * grp < DQK;
+        const int c0 = min(8 * st + 2 * grp, DQK / 16 - 2);
+        const uint4_t a = *(const uint4_t*)(ks + key * KROW + swz<KROW>(c0, key) * 16);
+        const uint4_t c = *(const uint4_t*)(ks + key * KROW + swz<KROW>(c0 + 1, key) * 16);
+        v8i_t r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          r[e] = live ? (int)a[e] : 0;
+          r[4 + e] = live ? (int)c[e] : 0;
+        }
+        return r;
+      };
+      // one operand buffer per key tile: the next step's bytes for key tile mt
+      // are read once mt's MFMAs of this step have issued, and arrive while the
+      // other key tiles' MFMAs run
+      v8i_t kr[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) kr[mt] = read_k(0, mt);
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+          for (int d = 0; d < ND; ++d)
+            s[mt][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kr[mt], q.qd[d][st], s[mt][0], 0, 0, 0, 127,
+                                                                         0, 127);
+          if (st + 1 < STEPS) kr[mt] = read_k(st + 1, mt);
+        }
+      }
+      // the order above, for the scheduler (MFMAs are pure and would
+      // otherwise all sink below the reads): 8 reads, then per (step, key
+      // tile) ND MFMAs followed by that tile's 2 reads of the next step
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * (STEPS - 1); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, ND, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * ND, 0);
+    } else {
+      constexpr int KSTEPS = DQK / 64;
+      int4_t acc[4][3][1];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int d = 0; d < 3; ++d) acc[mt][d][0] = int4_t{0, 0, 0, 0};
+      int4_t raw[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int key = mt * 16 + l16;
+        raw[mt] = *(const int4_t*)(ks + key * KROW + swz<KROW>(grp, key) * 16);
+      }
+#pragma unroll
+      for (int sp = 0; sp < KSTEPS; ++sp) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          qk_i8_step<1>(raw[mt], q.qd[sp], acc[mt]);
+          if (sp + 1 < KSTEPS) {
+            const int key = mt * 16 + l16;
+            raw[mt] = *(const int4_t*)(ks + key * KROW + swz<KROW>(4 * (sp + 1) + grp, key) * 16);
+          }
+        }
+      }
+      // (as for fp8: per key tile, its 3 digit MFMAs, then its next read)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * (KSTEPS - 1); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) s[mt][0] = s_from_i8(acc[mt][0][0], acc[mt][1][0], acc[mt][2][0]);
+    }
+    {
+      half8_t pb[2][1];
+      const float m_before = sa.m[0];
+      softmax_tile<1, 0>(p, u, kbase, grp, q, s, sa, pb);
+      const float m_use = sa.m[0] == -INFINITY ? 0.f : sa.m[0];
+      if (grp == 0) alpha_lds[wave * 16 + l16] = __builtin_amdgcn_exp2f(m_before - m_use);
+      pt_lds[(wave * 2 + 0) * 64 + lane] = pb[0][0];
+      pt_lds[(wave * 2 + 1) * 64 + lane] = pb[1][0];
+    }
+    __syncthreads();   // Y: P^T and factors ready
+
+    // ---- phase B: O^T[128 dims of this wave][all rows] += V^T P^T ----
+    {
+      float al[NTB];
+      bool grew = false;
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt) {
+        al[nt] = alpha_lds[nt * 16 + l16];
+        grew |= al[nt] != 1.f;
+      }
+      if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+#pragma unroll
+        for (int md = 0; md < MDW; ++md)
+#pragma unroll
+          for (int nt = 0; nt < NTB; ++nt) o[md][nt] *= al[nt];
+      }
+    }
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      const int vrow = 32 * ks2 + (jr < 4 ? 4 * grp + jr : 16 + 4 * grp + (jr - 4));
+      half8_t pbn[NTB];
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt) pbn[nt] = pt_lds[(nt * 2 + ks2) * 64 + lane];
+      int2_t vraw[MDW];
+#pragma unroll
+      for (int md = 0; md < MDW; ++md) {
+        const int chunk = wave * MDW + md;
+        vraw[md] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) int2_t*)(
+            ks + vrow * KROW + swz<KROW>(chunk, vrow) * 16 + hlf * 8));
+      }
+#pragma unroll
+      for (int md = 0; md < MDW; ++md) {
+        const half8_t a = bytes8_to_op<FP8>((uint32_t)vraw[md][0], (uint32_t)vraw[md][1]);
+#pragma unroll
+        for (int nt = 0; nt < NTB; ++nt)
+          o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pbn[nt], o[md][nt], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: row sums and lse from the owner waves, outputs per dim slice ----
+  const int H_q = p.num_q_heads;
+  {
+    const float lt = row_sum4(sa.l[0]);
+    const float lse_nat = lt > 0.f ? (sa.m[0] + __log2f(lt)) * LN2F : -INFINITY;
+    if (grp == 0) lrow_lds[wave * 16 + l16] = lt;
+    if (grp == 0 && q.ok[0]) {
+      const int tok = u.tok0 + q.tok[0];
+      if (u.split) p.part_lse[((int64_t)tok * p.max_chunks + u.c) * H_q + q.head[0]] = lse_nat;
+      else if (p.lse) p.lse[(int64_t)tok * H_q + q.head[0]] = lse_nat;
+    }
+  }
+  __syncthreads();
+  const int mode = p.scale_mode;
+  float4_t vsc[MDW];
+  if (mode == PA_SCALE_PER_CHANNEL) {
+#pragma unroll
+    for (int md = 0; md < MDW; ++md)
+      vsc[md] = *(const float4_t*)(p.v_scale + (int64_t)g * DV + (wave * MDW + md) * 16 + grp * 4);
+  } else {
+    const float v = p.v_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
+#pragma unroll
+    for (int md = 0; md < MDW; ++md) vsc[md] = float4_t{v, v, v, v};
+  }
+#pragma unroll
+  for (int nt = 0; nt < NTB; ++nt) {
+    const int r = u.row0 + nt * 16 + l16;
+    if (r >= u.rows_total) continue;
+    const float lt = lrow_lds[nt * 16 + l16];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float off = lt > 0.f ? KV_OFF : 0.f;
+    const int tok = u.tok0 + r / u.G;
+    const int h = g * u.G + r % u.G;
+    float* prow = u.split ? p.part_o + (((int64_t)tok * p.max_chunks + u.c) * H_q + h) * DV : nullptr;
+    uint16_t* orow = p.out + ((int64_t)tok * H_q + h) * DV;
+#pragma unroll
+    for (int md = 0; md < MDW; ++md) {
+      const int d = (wave * MDW + md) * 16 + grp * 4;
+      float4_t v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = fmaf(o[md][nt][i], inv, -off) * vsc[md][i];
+      if (u.split) {
+        *(float4_t*)(prow + d) = v;
+      } else {
+        const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *(int2_t*)(orow + d) = int2_t{(int)w0, (int)w1};
+      }
+    }
+  }
+}
+
+// MLA, third form (e4m3fn caches, one f16 query part): eight waves and 64
+// rows per workgroup, two waves per SIMD, so one wave's conversions, LDS
+// reads and DMA issue overlap the other's MFMAs.  Phase A: wave w takes the
+// 16 rows of tile w % 4 and the 32 keys of half w / 4 of each 64-key tile
+// (fp8 MFMA, query in two fp8 digits); the two waves of a row tile exchange
+// their row maxima through LDS (both then hold the same reference maximum, so
+// their weights share one scale), each writes the P^T operand of its key
+// half and keeps its own partial row sum.  Phase B: wave w accumulates O^T
+// for output dims 64w..64w+63 of all 64 rows.
+constexpr int MLA8_WAVES = 8;
+
+template <bool BAL>
+__global__ __launch_bounds__(MLA8_WAVES * 64, 1) void paged_mla8_kernel(AttnParams p) {
+  constexpr int DQK = 576, DV = 512, NW = MLA8_WAVES;
+  constexpr int ROWS = 64;                        // packed rows per workgroup
+  constexpr int NTB = ROWS / 16;                  // row tiles (phase B)
+  constexpr int MDW = DV / 16 / NW;               // output-dim tiles per wave (4)
+  constexpr int KROW = DQK;
+  constexpr int KTILE = TK * KROW;                // 36 KB raw tile
+  constexpr int NSTAGE = 3;
+  constexpr int ND = 2;                           // fp8 digits of the bf16 query
+  constexpr int STEPS = QRowsF8<DQK, ND>::STEPS;  // 128-dim steps of S^T (5)
+  using LD = DmaTileLoader<KROW, KROW, NW, true>;
+  constexpr int BLK = LD::KCH / 64;               // 1 KB DMA blocks per tile (36)
+  static_assert(LD::K_DMA == 5 && BLK == 36, "waves 0..3 issue 5 blocks per tile, waves 4..7 issue 4");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t kst[NSTAGE * KTILE];   // raw tiles
+  __shared__ __attribute__((aligned(16))) half8_t pt_lds[NTB * 2 * 64];    // P^T operands [row tile][key half]
+  __shared__ float mx_lds[2][ROWS];               // row maxima of each key half
+  __shared__ float alpha_lds[ROWS];
+  __shared__ float lrow_lds[2][ROWS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int rt = wave & 3, kh = wave >> 2;        // phase A: row tile and key half
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;
+  int b, g;
+  Unit u;
+  if (!shared_tile_unit<ROWS, BAL>(p, b, g, u)) return;
+  const int kv_lo = u.kv_lo, n_tiles = u.n_tiles;
+  LD ld;
+  ld.init(p, b, g, wave, kv_lo, u.key_end, n_tiles, lane, lds_addr(kst));
+#pragma unroll
+  for (int st = 0; st < NSTAGE - 1; ++st)
+    if (st < n_tiles) ld.issue(p, st, st);
+
+  QRowsF8<DQK, ND> q;
+  load_query_f8<DQK, ND>(p, u, g, u.row0 + rt * 16, lane, q);
+  SoftmaxState<1, 0> sa;   // this wave's rows: reference maximum and its key half's row sum
+  softmax_init(sa);
+  float4_t o[MDW][NTB];    // dims 16*(MDW*wave + md) + 4*grp + i, row 16*nt + l16
+#pragma unroll
+  for (int md = 0; md < MDW; ++md)
+#pragma unroll
+    for (int nt = 0; nt < NTB; ++nt) o[md][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  const int jr = l16 >> 1, hlf = lane & 1;        // phase B tr8 read (see pv_tile)
+  const half2_t ones2 = {(_Float16)1.0f, (_Float16)1.0f};
+
+  // Phase B of a tile (V^T from its raw stage, P^T and factors from LDS).
+  auto phase_b = [&](const uint8_t* vs) {
+    {
+      float al[NTB];
+      bool grew = false;
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt) {
+        al[nt] = alpha_lds[nt * 16 + l16];
+        grew |= al[nt] != 1.f;
+      }
+      if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+#pragma unroll
+        for (int md = 0; md < MDW; ++md)
+#pragma unroll
+          for (int nt = 0; nt < NTB; ++nt) o[md][nt] *= al[nt];
+      }
+    }
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      const int vrow = 32 * ks2 + (jr < 4 ? 4 * grp + jr : 16 + 4 * grp + (jr - 4));
+      half8_t pbn[NTB];
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt) pbn[nt] = pt_lds[(nt * 2 + ks2) * 64 + lane];
+#pragma unroll
+      for (int md = 0; md < MDW; ++md) {
+        const int chunk = wave * MDW + md;
+        const int2_t vraw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) int2_t*)(vs + vrow * KROW + swz<KROW>(chunk, vrow) * 16 + hlf * 8));
+        const half8_t a = bytes8_to_op<true>((uint32_t)vraw[0], (uint32_t)vraw[1]);
+#pragma unroll
+        for (int nt = 0; nt < NTB; ++nt)
+          o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pbn[nt], o[md][nt], 0, 0, 0);
+      }
+    }
+  };
+
+  // Barriers per tile: X (tile it landed; every wave is past phase B of tile
+  // it - 1, so its raw stage can take tile it + 2 and P^T can be rewritten),
+  // M (row maxima of both key halves exchanged), P (P^T and factors written).
+  for (int it = 0; it < n_tiles; ++it) {
+    const int stage = it % NSTAGE;
+    // this wave's DMA of tile it + 1 (5 or 4 blocks) may stay in flight
+    if (it + 1 >= n_tiles) wait_vmcnt<0>();
+    else if (wave < 4) wait_vmcnt<5>();
+    else wait_vmcnt<4>();
+    __syncthreads();   // X
+    if (it + NSTAGE - 1 < n_tiles) ld.issue(p, it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
+    const uint8_t* ks = kst + stage * KTILE;
+    const int kbase = kv_lo + it * TK;
+
+    // ---- phase A: S^T for keys 32 kh .. 32 kh + 31 of this wave's 16 rows ----
+    float4_t s[2];
+    s[0] = s[1] = float4_t{0.f, 0.f, 0.f, 0.f};
+    auto read_k = [&](int st, int j) {
+      const int key = (2 * kh + j) * 16 + l16;
+      const bool live = st * 128 + 32 * grp < DQK;
+      const int c0 = min(8 * st + 2 * grp, DQK / 16 - 2);
+      const uint4_t a = *(const uint4_t*)(ks + key * KROW + swz<KROW>(c0, key) * 16);
+      const uint4_t c = *(const uint4_t*)(ks + key * KROW + swz<KROW>(c0 + 1, key) * 16);
+      v8i_t r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        r[e] = live ? (int)a[e] : 0;
+        r[4 + e] = live ? (int)c[e] : 0;
+      }
+      return r;
+    };
+    v8i_t kr[2];
+    kr[0] = read_k(0, 0);
+    kr[1] = read_k(0, 1);
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+          s[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kr[j], q.qd[d][st], s[j], 0, 0, 0, 127, 0, 127);
+        if (st + 1 < STEPS) kr[j] = read_k(st + 1, j);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i2 = 0; i2 < 2 * (STEPS - 1); ++i2) {
+      __builtin_amdgcn_sched_group_barrier(0x008, ND, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * ND, 0);
+
+
+    // ---- softmax over the whole 64-key tile, the maxima shared by the two halves ----
+    const int k0 = kbase + 32 * kh;   // key of s[j][i]: k0 + 16 j + 4 grp + i
+    if (kbase + TK > u.mask_from) {
+      const int lim = p.causal ? min(u.kv_hi, u.L + q.tok[0] + 1) : u.kv_hi;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (k0 + 16 * j + 4 * grp + i >= lim) s[j][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[j][i]);
+    mx = row_max4(mx) * q.row_mult[0];
+    if (grp == 0) mx_lds[kh][rt * 16 + l16] = mx;
+    __syncthreads();   // M
+    mx = fmaxf(mx_lds[0][rt * 16 + l16], mx_lds[1][rt * 16 + l16]);
+    const float m_new = mx > sa.m[0] + LAZY_LOG2 ? mx : sa.m[0];
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(sa.m[0] - m_use);
+    sa.m[0] = m_new;
+    half8_t pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pb[i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[0][i], q.row_mult[0], -m_use));
+      pb[4 + i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[1][i], q.row_mult[0], -m_use));
+    }
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const half2_t pr = {pb[2 * e], pb[2 * e + 1]};
+      ls = __builtin_amdgcn_fdot2(pr, ones2, ls, false);
+    }
+    sa.l[0] = sa.l[0] * alpha + ls;
+    if (kh == 0 && grp == 0) alpha_lds[rt * 16 + l16] = alpha;
+    pt_lds[(rt * 2 + kh) * 64 + lane] = pb;
+    __syncthreads();   // P
+    phase_b(ks);
+  }
+
+  // ---- epilogue: row sums of both key halves, lse, outputs per dim slice ----
+  const int H_q = p.num_q_heads;
+  {
+    const float lt = row_sum4(sa.l[0]);
+    if (grp == 0) lrow_lds[kh][rt * 16 + l16] = lt;
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float lt = lrow_lds[0][rt * 16 + l16] + lrow_lds[1][rt * 16 + l16];
+    const float lse_nat = lt > 0.f ? (sa.m[0] + __log2f(lt)) * LN2F : -INFINITY;
+    if (grp == 0 && q.ok[0]) {
+      const int tok = u.tok0 + q.tok[0];
+      if (u.split) p.part_lse[((int64_t)tok * p.max_chunks + u.c) * H_q + q.head[0]] = lse_nat;
+      else if (p.lse) p.lse[(int64_t)tok * H_q + q.head[0]] = lse_nat;
+    }
+  }
+  const int mode = p.scale_mode;
+  float4_t vsc[MDW];
+  if (mode == PA_SCALE_PER_CHANNEL) {
+#pragma unroll
+    for (int md = 0; md < MDW; ++md)
+      vsc[md] = *(const float4_t*)(p.v_scale + (int64_t)g * DV + (wave * MDW + md) * 16 + grp * 4);
+  } else {
+    const float v = p.v_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
+#pragma unroll
+    for (int md = 0; md < MDW; ++md) vsc[md] = float4_t{v, v, v, v};
+  }
+#pragma unroll
+  for (int nt = 0; nt < NTB; ++nt) {
+    const int r = u.row0 + nt * 16 + l16;
+    if (r >= u.rows_total) continue;
+    const float lt = lrow_lds[0][nt * 16 + l16] + lrow_lds[1][nt * 16 + l16];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int tok = u.tok0 + r / u.G;
+    const int h = g * u.G + r % u.G;
+    float* prow = u.split ? p.part_o + (((int64_t)tok * p.max_chunks + u.c) * H_q + h) * DV : nullptr;
+    uint16_t* orow = p.out + ((int64_t)tok * H_q + h) * DV;
+#pragma unroll
+    for (int md = 0; md < MDW; ++md) {
+      const int d = (wave * MDW + md) * 16 + grp * 4;
+      float4_t v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = o[md][nt][i] * inv * vsc[md][i];
+      if (u.split) {
+        *(float4_t*)(prow + d) = v;
+      } else {
+        const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *(int2_t*)(orow + d) = int2_t{(int)w0, (int)w1};
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------- merge --
 // One group of DV/4 lanes per (token, head) row; each lane owns 4 channels.
 template <int DV>
@@ -2583,10 +3294,16 @@ template <bool FP8, bool HILO>
 hipError_t launch_mla(const AttnParams& p, dim3 grid, hipStream_t stream) {
   // the balanced split's planner is a variant of its own (it costs the main
   // loop SGPR spills)
-  if (p.balanced)
-    hipLaunchKernelGGL((paged_mla_kernel<FP8, HILO, true>), grid, dim3(MLA_WAVES * 64), 0, stream, p);
-  else
-    hipLaunchKernelGGL((paged_mla_kernel<FP8, HILO, false>), grid, dim3(MLA_WAVES * 64), 0, stream, p);
+  if constexpr (FP8 && !HILO) {   // e4m3fn keys with a one-part query: the eight-wave kernel
+    if (p.balanced)
+      hipLaunchKernelGGL((paged_mla8_kernel<true>), grid, dim3(MLA8_WAVES * 64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((paged_mla8_kernel<false>), grid, dim3(MLA8_WAVES * 64), 0, stream, p);
+  } else if (p.balanced) {
+    hipLaunchKernelGGL((paged_mla2_kernel<FP8, HILO, true>), grid, dim3(MLA_WAVES * 64), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((paged_mla2_kernel<FP8, HILO, false>), grid, dim3(MLA_WAVES * 64), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -2612,7 +3329,8 @@ int occ_one() {
 }
 template <bool FP8, bool HILO>
 int occ_mla() {
-  return occupancy_of(paged_mla_kernel<FP8, HILO, false>, MLA_WAVES * 64);
+  if constexpr (FP8 && !HILO) return occupancy_of(paged_mla8_kernel<false>, MLA8_WAVES * 64);
+  return occupancy_of(paged_mla2_kernel<FP8, HILO, false>, MLA_WAVES * 64);
 }
 template <int D, bool FP8, int NT, bool HILO, int KS, bool TREE>
 int occ_decode() {
