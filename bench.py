@@ -114,16 +114,24 @@ def kernel_name(dp):
     """Name of the attention kernel the library launches for this problem."""
     w = dp.w
     if w.shared_kv:
-        return "paged_mla_kernel"
+        eight_waves = w.kv_dtype == "fp8_e4m3" and w.q_dtype == "bf16" and w.scale_mode != "channel"
+        return "paged_mla8_kernel" if eight_waves else "paged_mla2_kernel"
     rows = (int(w.decode_q_len) if dp.decode else int(w.q_lens.max())) * (w.num_q_heads // w.num_kv_heads)
     return "paged_decode_kernel" if rows <= 32 else "paged_attn_kernel"
 
 
 def compute_dtype(dp):
-    """MFMA operand types: int8 caches through the decode kernel or the 16-row
-    shared-tile variants take S = K Q^T on the int8 MFMA (f16 for PV); every
-    other path multiplies f16 (cache values converted exactly)."""
+    """MFMA operand types: int8 caches through the decode kernel, the 16-row
+    shared-tile variants or the MLA kernel take S = K Q^T on the int8 MFMA (f16
+    for PV); e4m3fn MLA caches take it on the fp8 MFMA with the query in fp8
+    digits ("fp8x2": two digits, bf16 query; "fp8x3": three); every other path
+    multiplies f16 (cache values converted exactly)."""
     w = dp.w
+    if w.shared_kv:
+        if w.kv_dtype == "i8":
+            return "i8/f16"
+        two = w.q_dtype == "bf16" and w.scale_mode != "channel"
+        return ("fp8x2" if two else "fp8x3") + "/f16"
     rows = (int(w.decode_q_len) if dp.decode else int(w.q_lens.max())) * (w.num_q_heads // w.num_kv_heads)
     if w.kv_dtype == "i8" and not w.shared_kv and rows <= 64:
         return "i8/f16"
@@ -394,9 +402,14 @@ def roofline(config, w, attn_ms, step_ms):
     _, alg_bytes, flops = work_figures(w)
     if config in (3, 5):
         a, st = flops / (attn_ms * 1e-3) / 1e12, flops / (step_ms * 1e-3) / 1e12
-        return {"bound": "mfma", "achieved": round(a, 3), "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": round(a / MFMA_F16_PEAK_TFS, 4), "step_achieved": round(st, 3),
-                "step_frac": round(st / MFMA_F16_PEAK_TFS, 4)}
+        r = {"bound": "mfma", "achieved": round(a, 3), "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+             "frac": round(a / MFMA_F16_PEAK_TFS, 4), "step_achieved": round(st, 3),
+             "step_frac": round(st / MFMA_F16_PEAK_TFS, 4)}
+        if config == 5 and w.kv_dtype == "fp8_e4m3":
+            # QK^T runs on the fp8 MFMA (5.0 PFLOP/s dense) once per query digit
+            r["peak_basis"] = ("QK^T: fp8 MFMA over 2 query digits = 2.5 PFLOP/s per algorithmic flop; "
+                               "PV: f16 MFMA 2.5 PFLOP/s")
+        return r
     a, st = alg_bytes / (attn_ms * 1e-3) / 1e9, alg_bytes / (step_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(a / HBM_PEAK_GBS, 4), "step_achieved": round(st, 1), "step_frac": round(st / HBM_PEAK_GBS, 4)}
