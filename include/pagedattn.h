@@ -380,17 +380,21 @@ int32_t split_kv_merge(const float* partial_o, const float* partial_lse,
  *                         units of prob->chunk_size keys (whole sequences when
  *                         0); head dims 64 or 128 with D_qk == D_v;
  *   PA_GATHER_DMA_4W      the shared-tile / append / MLA kernels' LDS-DMA tile
- *   PA_GATHER_DMA_3W      loader with 4 or 3 waves splitting each tile, over
- *                         the same units; head dims 64/128 (D_qk == D_v) or,
- *                         with 4 waves, the shared 576/512 layout (V is then
- *                         the K prefix: v_dst must be NULL).
+ *   PA_GATHER_DMA_3W      loader with 4 or 3 waves splitting each 64-key
+ *                         tile, over the same units; head dims 64/128
+ *                         (D_qk == D_v) or, with 4 waves, the shared 576/512
+ *                         layout (V is then the K prefix: v_dst must be NULL);
+ *   PA_GATHER_DMA_MLA32   the same loader as the e4m3fn MLA kernel drives it:
+ *                         4 waves splitting 32-key tiles, shared 576/512
+ *                         layout only.
  * Other combinations are UNSUPPORTED.
  */
 enum {
   PA_GATHER_ROWS = 0,
   PA_GATHER_DECODE = 1,
   PA_GATHER_DMA_4W = 2,
-  PA_GATHER_DMA_3W = 3
+  PA_GATHER_DMA_3W = 3,
+  PA_GATHER_DMA_MLA32 = 4
 };
 
 int32_t pa_gather_debug(const pa_problem* prob, int32_t loader, const void* k_cache, const void* v_cache,

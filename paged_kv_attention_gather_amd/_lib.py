@@ -38,6 +38,7 @@ GATHER_ROWS = 0       # one key row at a time
 GATHER_DECODE = 1     # the decode kernel's register tile loader
 GATHER_DMA_4W = 2     # the LDS-DMA tile loader, 4 waves
 GATHER_DMA_3W = 3     # the LDS-DMA tile loader, 3 waves
+GATHER_DMA_MLA32 = 4  # the LDS-DMA tile loader as the e4m3fn MLA kernel drives it (32-key tiles)
 
 #: Size of the static scratch behind paged_attn_decode_scratch (PA_DECODE_SCRATCH_BYTES).
 DECODE_SCRATCH_BYTES = 32 << 20

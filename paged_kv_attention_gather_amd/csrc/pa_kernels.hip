@@ -938,9 +938,8 @@ __device__ __forceinline__ void load_query_f8(const AttnParams& p, const Unit& u
   q.tok[0] = t;
   q.head[0] = g * u.G + (q.ok[0] ? r % u.G : 0);
   const int64_t qoff = (int64_t)(u.tok0 + t) * p.q_row_stride + (int64_t)q.head[0] * DQK;
-  // element j of step s: dim 128 s + 32 grp + j (8 at a time)
-  auto load8 = [&](int s, int j8, float* x) {
-    const int d0 = 128 * s + 32 * grp + 8 * j8;
+  // 8 elements from dim d0 = 128 s + 32 grp + 8 j8 (step s, lane group grp)
+  auto load8 = [&](int d0, float* x) {
     if (!q.ok[0] || d0 >= DQK) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = 0.f;
@@ -967,16 +966,17 @@ __device__ __forceinline__ void load_query_f8(const AttnParams& p, const Unit& u
     }
   };
   float amax = 0.f;
+  auto amax8 = [&](int d0) {
+    float x[8];
+    load8(d0, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    __builtin_amdgcn_sched_barrier(0);   // keep the row's loads from piling up in registers
+  };
 #pragma unroll
   for (int s = 0; s < STEPS; ++s)
 #pragma unroll
-    for (int j8 = 0; j8 < 4; ++j8) {
-      float x[8];
-      load8(s, j8, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
-      __builtin_amdgcn_sched_barrier(0);   // keep the row's loads from piling up in registers
-    }
+    for (int j8 = 0; j8 < 4; ++j8) amax8(128 * s + 32 * grp + 8 * j8);
   amax = row_max4(amax);
   int ex = 0;
   if (amax > 0.f) (void)frexpf(amax, &ex);      // amax < 2^ex
@@ -984,36 +984,42 @@ __device__ __forceinline__ void load_query_f8(const AttnParams& p, const Unit& u
   const float up = ldexpf(1.f, k2);
   q.row_mult[0] = ldexpf(1.f, -k2) * (fold_channel ? 1.f : p.qk_mult * k_uniform);
   q.kbias[0] = 0.f;
+  // digits of 8 elements from dim d0: two words (4 codes each) per digit
+  auto digits8 = [&](int d0, uint32_t (&w)[ND][2]) {
+    float x[8];
+    load8(d0, x);
+#pragma unroll
+    for (int d = 0; d < ND; ++d) w[d][0] = w[d][1] = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      float r0 = x[e] * up, r1 = x[e + 1] * up;
+#pragma unroll
+      for (int d = 0; d < ND; ++d) {
+        // two e4m3fn (OCP) codes in one 16-bit half, and their exact values
+        typedef short short2_t __attribute__((ext_vector_type(2)));
+        const short2_t zero2 = {0, 0};
+        const uint32_t pk =
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(zero2, r0, r1, 1.0f, false)) &
+            0xffffu;
+        const auto back = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)pk, 1.0f, false);
+        r0 -= back[0];
+        r1 -= back[1];
+        w[d][(e / 2) >> 1] |= pk << (16 * ((e / 2) & 1));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
 #pragma unroll
   for (int s = 0; s < STEPS; ++s)
 #pragma unroll
     for (int j8 = 0; j8 < 4; ++j8) {
-      float x[8];
-      load8(s, j8, x);
-      uint32_t w[ND][2] = {};
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        float r0 = x[e] * up, r1 = x[e + 1] * up;
-#pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          // two e4m3fn (OCP) codes in one 16-bit half, and their exact values
-          typedef short short2_t __attribute__((ext_vector_type(2)));
-          const short2_t zero2 = {0, 0};
-          const uint32_t pk =
-              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(zero2, r0, r1, 1.0f, false)) &
-              0xffffu;
-          const auto back = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)pk, 1.0f, false);
-          r0 -= back[0];
-          r1 -= back[1];
-          w[d][(e / 2) >> 1] |= pk << (16 * ((e / 2) & 1));
-        }
-      }
+      uint32_t w[ND][2];
+      digits8(128 * s + 32 * grp + 8 * j8, w);
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
         q.qd[d][s][2 * j8] = (int)w[d][0];
         q.qd[d][s][2 * j8 + 1] = (int)w[d][1];
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -1403,10 +1409,11 @@ __device__ __forceinline__ void merge_if_last(const AttnParams& p, const Unit& u
 // are as in RegTileLoader.
 // HOLD: keep each DMA's per-lane source offset in a register (else recompute
 // it at every issue, for kernels short of registers).
-template <int KROW, int VROW, int NW, bool SHARED, bool HOLD = true>
+template <int KROW, int VROW, int NW, bool SHARED, bool HOLD = true, int TKEYS = TK>
 struct DmaTileLoader {
-  static constexpr int KTILE = TK * KROW;
-  static constexpr int VTILE = SHARED ? 0 : TK * VROW;
+  static_assert(TKEYS == 32 || TKEYS == 64, "32- or 64-key tiles");
+  static constexpr int KTILE = TKEYS * KROW;
+  static constexpr int VTILE = SHARED ? 0 : TKEYS * VROW;
   static constexpr int STAGE = KTILE + VTILE;
   static constexpr int KCH = KTILE / 16;                 // 16-byte chunks per K tile
   static constexpr int VCH = VTILE / 16;
@@ -1446,9 +1453,9 @@ struct DmaTileLoader {
     last_page = n_tiles > 0 ? (key_end - 1) >> page_shift : 0;   // never read past it
     pw_base = -(1 << 30);
     pw_val = 0;
-    one_page = page_shift >= 6;
-    fast_addr = one_page && (int64_t)TK * p.k_stride_token < (1LL << 30) &&
-                (SHARED || (int64_t)TK * p.v_stride_token < (1LL << 30));
+    one_page = page_shift >= (TKEYS == 64 ? 6 : 5);   // tiles start at multiples of TKEYS
+    fast_addr = one_page && (int64_t)TKEYS * p.k_stride_token < (1LL << 30) &&
+                (SHARED || (int64_t)TKEYS * p.v_stride_token < (1LL << 30));
     smem_base = smem_base_;
     ks_tok = p.k_stride_token;
     vs_tok = p.v_stride_token;
@@ -1470,7 +1477,7 @@ struct DmaTileLoader {
 
   // Issues this wave's share of tile `tile` into LDS stage `stage`.
   __device__ __forceinline__ void issue(const AttnParams& p, int tile, int stage) {
-    const int kbase = kv_lo + tile * TK;
+    const int kbase = kv_lo + tile * TKEYS;
     const int pg0 = kbase >> page_shift;
     const int pg_last = min(pg0 + 3, last_page);
     if (pg0 < pw_base || pg_last > pw_base + 63) {
@@ -1481,7 +1488,7 @@ struct DmaTileLoader {
     const int pp0 = __builtin_amdgcn_readlane(pw_val, pg0 - pw_base);
     const uint32_t kdst = smem_base + stage * STAGE;
     const uint32_t vdst = kdst + KTILE;
-    if (fast_addr && kbase + TK <= key_end) {
+    if (fast_addr && kbase + TKEYS <= key_end) {
       const uint8_t* kb = paged_row(p.k_cache, pp0, kbase, page_shift, g, p.k_stride_page, p.k_stride_head,
                                     p.k_stride_token);
 #pragma unroll
@@ -2281,312 +2288,15 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void paged_decode_persistent_k
 // ------------------------------------------------------- MLA latent decode --
 //
 // Shared 576/512 latent rows (V = first 512 bytes of each K row), one KV head,
-// NW waves and 16 * NW packed query rows per workgroup (8 waves and 128 rows;
-// 4 and 64 when Q needs hi + lo parts).  Per 64-key tile:
-//   staging  the raw tile (64 x 576 bytes) arrives by LDS DMA, two tiles ahead;
-//   convert  the waves turn its first 512 dims into an f16 tile in LDS once
-//            (each wave an equal share), instead of every wave converting the
-//            whole tile for its own rows;
-//   phase A  wave w computes S^T = K Q^T for rows 16w..16w+15 (its query rows
-//            stay in registers; K read as f16 from the converted tile, the 64
-//            rope dims converted from the raw tile), runs the online softmax
-//            and writes P^T to LDS in the B-operand layout of the PV MFMA;
-//   phase B  wave w accumulates O^T for output dims (512 / NW) * w onwards of
-//            all rows: V^T comes from the f16 tile by the 16-bit LDS transpose
-//            read, P^T and the per-row rescale factors from phase A.
+// 64 packed query rows (64 of the request's query heads) per workgroup, one
+// workgroup per CU.  Raw K tiles arrive by LDS DMA and are never converted as
+// a whole: S^T = K Q^T takes the K bytes on the fp8 or int8 MFMA as they are
+// (the query in fp8 or int8 digits), and PV converts the V^T operands in
+// registers after the 8-bit LDS transpose read.
 
-constexpr int MLA_WAVES = 4;  // waves (= 16-row tiles) per MLA workgroup
+constexpr int MLA_WAVES = 4;  // waves of the four-wave MLA kernel
 
-template <bool FP8, bool HILO, bool BAL>
-__global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_kernel(AttnParams p) {
-  constexpr int DQK = 576, DV = 512, NW = MLA_WAVES;
-  constexpr int NTA = 1;                          // 16-row tiles per wave in phase A
-  constexpr int ROWS = 16 * NTA * NW;             // 128 (64 with hi + lo query parts)
-  constexpr int NTB = ROWS / 16;                  // row tiles in phase B
-  constexpr int MDW = DV / 16 / NW;               // output-dim tiles per wave
-  constexpr int KROW = DQK;
-  constexpr int KTILE = TK * KROW;                // 36 KB raw tile
-  constexpr int KCPR = KROW / 16;                 // 36 chunks per raw row
-  constexpr int K_BLK = TK * KCPR / 64;           // 36 DMA instructions per tile
-  constexpr int K_DMA = (K_BLK + NW - 1) / NW;    // per wave (waves below K_BLK % NW issue one more)
-  constexpr int FROW = DV * 2;                    // 1024-byte f16 row
-  // K and V share the f16 tile, so int8 rows are converted exactly (an
-  // operand offset on K would put the fp32 logit accumulator at 1152 * sum(q))
-  constexpr float KV_OFF = 0.f;
-  static_assert(K_BLK * 64 == TK * KCPR, "raw tile is whole DMA blocks");
-  static_assert(K_BLK % NW == 0 || K_BLK % NW == NW / 2, "per-wave DMA count is K_DMA or K_DMA - 1");
-
-  __shared__ __attribute__((aligned(1024))) uint8_t kst[2 * KTILE];      // raw tiles
-  __shared__ __attribute__((aligned(1024))) uint8_t kf[TK * FROW];       // f16 dims 0..511
-  __shared__ __attribute__((aligned(16))) half8_t pt_lds[NTB * 2 * 64];  // P^T operands
-  __shared__ float alpha_lds[ROWS];
-  __shared__ float lrow_lds[ROWS];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int l16 = lane & 15;
-  const int grp = lane >> 4;
-  int b, g;
-  Unit u;
-  if (!shared_tile_unit<ROWS, BAL>(p, b, g, u)) return;   // a chunk's row tiles share an XCD
-  const int kv_lo = u.kv_lo, n_tiles = u.n_tiles;
-  DmaTileLoader<KROW, KROW, NW, true> ld;
-  ld.init(p, b, g, wave, kv_lo, u.key_end, n_tiles, lane, lds_addr(kst));
-  auto issue_tile = [&](int tile, int stage) { ld.issue(p, tile, stage); };
-  static_assert(DmaTileLoader<KROW, KROW, NW, true>::K_DMA == K_DMA && DmaTileLoader<KROW, KROW, NW, true>::KTILE == KTILE,
-                "MLA stage geometry");
-
-  if (n_tiles > 0) issue_tile(0, 0);
-  if (n_tiles > 1) issue_tile(1, 1);
-
-  QRows<DQK, NTA, HILO> q;
-  load_query<DQK, NTA, HILO>(p, u, g, u.row0 + wave * 16 * NTA, lane, KV_OFF, q);
-  SoftmaxState<NTA, 0> sa;   // phase-A row state (m, l); O lives in phase B
-  softmax_init(sa);
-  float4_t o[MDW][NTB];      // dims 16*(MDW*wave + md) + 4*grp + i, row 16*nt + l16
-#pragma unroll
-  for (int md = 0; md < MDW; ++md)
-#pragma unroll
-    for (int nt = 0; nt < NTB; ++nt) o[md][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Per-lane LDS offsets, hoisted so that each access below is a base plus a
-  // compile-time offset (kf_swz only permutes the low four chunk bits).
-  //  convert: raw read of key NW*i + wave, chunk lane/2 (swz<576> depends on
-  //           key % 32, so on i % CV_RP); f16 write of chunk lane (kf_swz
-  //           depends on key % 16, so on i % CV_WP)
-  constexpr int CV_RP = 32 / NW, CV_WP = 16 / NW;
-  int cv_rd[CV_RP], cv_wr[CV_WP];
-#pragma unroll
-  for (int i = 0; i < CV_RP; ++i) {
-    const int key = i * NW + wave;
-    cv_rd[i] = key * KROW + swz<KROW>(lane >> 1, key) * 16 + (lane & 1) * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < CV_WP; ++i) {
-    const int key = i * NW + wave;
-    cv_wr[i] = key * FROW + kf_swz(lane, key) * 16;
-  }
-  //  phase A: key l16 (+16mt), f16 chunk 8*(sp & 1) + 2grp + h (+16 * (sp >> 1))
-  int qa_off[2][2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) qa_off[par][h] = l16 * FROW + kf_swz(8 * par + 2 * grp + h, l16) * 16;
-  //  phase B: transposed reads; lanes 4j..4j+3 of a 16-lane group give key j
-  int vb_off[MDW];
-  {
-    const int tr_j = l16 >> 2, tr_q = l16 & 3;
-    const int kA = 4 * grp + tr_j;   // kf_swz depends on the key's low four bits only
-#pragma unroll
-    for (int md = 0; md < MDW; ++md)
-      vb_off[md] = kA * FROW + kf_swz(2 * (wave * MDW + md) + (tr_q >> 1), kA) * 16 + (tr_q & 1) * 8;
-  }
-
-  for (int it = 0; it < n_tiles; ++it) {
-    const int stage = it & 1;
-    // this wave's DMA of tile it + 1 (K_DMA or K_DMA - 1 instructions) may stay in flight
-    if (it + 1 >= n_tiles) wait_vmcnt<0>();
-    else if ((K_DMA - 1) * NW + wave < K_BLK) wait_vmcnt<K_DMA>();
-    else wait_vmcnt<K_DMA - 1>();
-    __syncthreads();  // B0: tile `it` landed for all waves; phase B of it - 1 is done with kf / pt
-    const uint8_t* ks = kst + stage * KTILE;
-    const int kbase = kv_lo + it * TK;
-
-    // ---- convert dims 0..511 of the raw tile to f16 (wave w: keys NW*i + w,
-    //      lane l: f16 chunk l = dims 8l .. 8l + 7) ----
-    {
-      int2_t raw[TK / NW];   // every read in flight before the first conversion
-#pragma unroll
-      for (int i = 0; i < TK / NW; ++i)
-        raw[i] = *(const int2_t*)(ks + cv_rd[i % CV_RP] + (i / CV_RP) * (CV_RP * NW * KROW));
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < TK / NW; ++i)
-        *(half8_t*)(kf + cv_wr[i % CV_WP] + (i / CV_WP) * (CV_WP * NW * FROW)) =
-            bytes8_to_f16<FP8>((uint32_t)raw[i][0], (uint32_t)raw[i][1]);
-    }
-    __syncthreads();  // B1: f16 tile complete
-
-    // ---- phase A: S^T = K Q^T for this wave's rows, softmax, P^T -> LDS ----
-    float4_t s[4][NTA];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NTA; ++nt) s[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
-    // K operands of the next 64 dims are read while the MFMAs of the current
-    // ones run (a single wave per SIMD has nothing else to hide LDS latency).
-    {
-      constexpr int SPF = DV / 64;        // 8 steps from the f16 tile, then the rope step
-      half8_t ka[2][4][2];
-      uint4_t rope_raw[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) ka[0][mt][h] = *(const half8_t*)(kf + mt * 16 * FROW + qa_off[0][h]);
-#pragma unroll
-      for (int sp = 0; sp < SPF; ++sp) {
-        const int cur = sp & 1;
-        if (sp + 1 < SPF) {
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-              ka[cur ^ 1][mt][h] =
-                  *(const half8_t*)(kf + mt * 16 * FROW + ((sp + 1) >> 1) * 256 + qa_off[(sp + 1) & 1][h]);
-        } else {
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            const int key = mt * 16 + l16;
-            rope_raw[mt] = *(const uint4_t*)(ks + key * KROW + swz<KROW>(4 * SPF + grp, key) * 16);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < NTA; ++nt) {
-            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[cur][mt][0], q.hi[nt][2 * sp], s[mt][nt], 0, 0, 0);
-            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[cur][mt][1], q.hi[nt][2 * sp + 1], s[mt][nt], 0, 0, 0);
-            if constexpr (HILO) {
-              s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[cur][mt][0], q.lo[nt][2 * sp], s[mt][nt], 0, 0, 0);
-              s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[cur][mt][1], q.lo[nt][2 * sp + 1], s[mt][nt], 0, 0, 0);
-            }
-          }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      constexpr int sp = SPF;   // rope dims 512..575, converted from the raw tile
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const half8_t a0 = bytes8_to_f16<FP8>(rope_raw[mt][0], rope_raw[mt][1]);
-        const half8_t a1 = bytes8_to_f16<FP8>(rope_raw[mt][2], rope_raw[mt][3]);
-#pragma unroll
-        for (int nt = 0; nt < NTA; ++nt) {
-          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, q.hi[nt][2 * sp], s[mt][nt], 0, 0, 0);
-          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.hi[nt][2 * sp + 1], s[mt][nt], 0, 0, 0);
-          if constexpr (HILO) {
-            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, q.lo[nt][2 * sp], s[mt][nt], 0, 0, 0);
-            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, q.lo[nt][2 * sp + 1], s[mt][nt], 0, 0, 0);
-          }
-        }
-      }
-    }
-    {
-      half8_t pb[2][NTA];
-      float m_before[NTA];
-#pragma unroll
-      for (int nt = 0; nt < NTA; ++nt) m_before[nt] = sa.m[nt];
-      // O lives in phase B, which applies the per-row factor published here.
-      softmax_tile<NTA, 0>(p, u, kbase, grp, q, s, sa, pb);
-#pragma unroll
-      for (int nt = 0; nt < NTA; ++nt) {
-        const float m_use = sa.m[nt] == -INFINITY ? 0.f : sa.m[nt];
-        if (grp == 0) alpha_lds[(wave * NTA + nt) * 16 + l16] = __builtin_amdgcn_exp2f(m_before[nt] - m_use);
-        pt_lds[((wave * NTA + nt) * 2 + 0) * 64 + lane] = pb[0][nt];
-        pt_lds[((wave * NTA + nt) * 2 + 1) * 64 + lane] = pb[1][nt];
-      }
-    }
-    __syncthreads();  // B2: P^T and factors ready; every wave is done with raw stage `stage`
-    if (it + 2 < n_tiles) issue_tile(it + 2, stage);
-
-    // ---- phase B: O^T[128 dims of this wave][all rows] += V^T P^T ----
-    {
-      float al[NTB];
-      bool grew = false;
-#pragma unroll
-      for (int nt = 0; nt < NTB; ++nt) {
-        al[nt] = alpha_lds[nt * 16 + l16];
-        grew |= al[nt] != 1.f;
-      }
-      if (__builtin_amdgcn_ballot_w64(grew) != 0) {
-#pragma unroll
-        for (int md = 0; md < MDW; ++md)
-#pragma unroll
-          for (int nt = 0; nt < NTB; ++nt) o[md][nt] *= al[nt];
-      }
-    }
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      half8_t va[MDW];
-      half8_t pbn[NTB];
-#pragma unroll
-      for (int md = 0; md < MDW; ++md) {
-        // lane: keys kappa(grp, j) for j = tr_j and tr_j + 4 (keys 32ks2 + 4grp + tr_j
-        // and 16 more), dims 4*tr_q .. 4*tr_q + 3 of this 16-dim tile; the
-        // transpose hands lane i dim i of keys j = 0..3
-        const uint8_t* va_base = kf + vb_off[md] + (32 * ks2) * FROW;
-        const short4_t ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4_t*)(va_base));
-        const short4_t rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4_t*)(va_base + 16 * FROW));
-        va[md] = __builtin_shufflevector(__builtin_bit_cast(half4_t, ra), __builtin_bit_cast(half4_t, rb),
-                                         0, 1, 2, 3, 4, 5, 6, 7);
-      }
-#pragma unroll
-      for (int nt = 0; nt < NTB; ++nt) pbn[nt] = pt_lds[(nt * 2 + ks2) * 64 + lane];
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int nt = 0; nt < NTB; ++nt)
-#pragma unroll
-        for (int md = 0; md < MDW; ++md)
-          o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[md], pbn[nt], o[md][nt], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-  // ---- epilogue: row sums and lse from the owner waves, outputs per dim slice ----
-  const int H_q = p.num_q_heads;
-#pragma unroll
-  for (int nt = 0; nt < NTA; ++nt) {
-    const float lt = row_sum4(sa.l[nt]);
-    const float lse_nat = lt > 0.f ? (sa.m[nt] + __log2f(lt)) * LN2F : -INFINITY;
-    if (grp == 0) lrow_lds[(wave * NTA + nt) * 16 + l16] = lt;
-    if (grp == 0 && q.ok[nt]) {
-      const int tok = u.tok0 + q.tok[nt];
-      if (u.split) p.part_lse[((int64_t)tok * p.max_chunks + u.c) * H_q + q.head[nt]] = lse_nat;
-      else if (p.lse) p.lse[(int64_t)tok * H_q + q.head[nt]] = lse_nat;
-    }
-  }
-  __syncthreads();
-  const int mode = p.scale_mode;
-  float4_t vsc[MDW];
-  if (mode == PA_SCALE_PER_CHANNEL) {
-#pragma unroll
-    for (int md = 0; md < MDW; ++md)
-      vsc[md] = *(const float4_t*)(p.v_scale + (int64_t)g * DV + (wave * MDW + md) * 16 + grp * 4);
-  } else {
-    const float v = p.v_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
-#pragma unroll
-    for (int md = 0; md < MDW; ++md) vsc[md] = float4_t{v, v, v, v};
-  }
-#pragma unroll
-  for (int nt = 0; nt < NTB; ++nt) {
-    const int r = u.row0 + nt * 16 + l16;
-    if (r >= u.rows_total) continue;
-    const float lt = lrow_lds[nt * 16 + l16];
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const float off = lt > 0.f ? KV_OFF : 0.f;
-    const int tok = u.tok0 + r / u.G;
-    const int h = g * u.G + r % u.G;
-    float* prow = u.split ? p.part_o + (((int64_t)tok * p.max_chunks + u.c) * H_q + h) * DV : nullptr;
-    uint16_t* orow = p.out + ((int64_t)tok * H_q + h) * DV;
-#pragma unroll
-    for (int md = 0; md < MDW; ++md) {
-      const int d = (wave * MDW + md) * 16 + grp * 4;
-      float4_t v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = fmaf(o[md][nt][i], inv, -off) * vsc[md][i];
-      if (u.split) {
-        *(float4_t*)(prow + d) = v;
-      } else {
-        const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        const uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-        *(int2_t*)(orow + d) = int2_t{(int)w0, (int)w1};
-      }
-    }
-  }
-}
-
-// MLA, second form: no f16 copy of the tile.  The raw 64 x 576 tile arrives
+// MLA, four-wave form (int8 caches, fp32 queries, per-channel K scales).  The raw 64 x 576 tile arrives
 // by LDS DMA into a three-stage ring (two tiles ahead).  Phase A (wave w, rows
 // 16w..16w+15) feeds the raw K bytes to the MFMA as they are: e4m3fn keys to
 // the fp8 MFMA against the query in fp8 digits (QRowsF8), int8 keys to the
@@ -2858,91 +2568,213 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla2_kernel(AttnParam
   }
 }
 
-// MLA, third form (e4m3fn caches, one f16 query part): eight waves and 64
-// rows per workgroup, two waves per SIMD, so one wave's conversions, LDS
-// reads and DMA issue overlap the other's MFMAs.  Phase A: wave w takes the
-// 16 rows of tile w % 4 and the 32 keys of half w / 4 of each 64-key tile
-// (fp8 MFMA, query in two fp8 digits); the two waves of a row tile exchange
-// their row maxima through LDS (both then hold the same reference maximum, so
-// their weights share one scale), each writes the P^T operand of its key
-// half and keeps its own partial row sum.  Phase B: wave w accumulates O^T
-// for output dims 64w..64w+63 of all 64 rows.
-constexpr int MLA8_WAVES = 8;
+// MLA, producer/consumer form (e4m3fn caches, bf16 query with a per-head or
+// per-tensor K scale).  Eight waves, 64 rows, 32-key tiles, one barrier per
+// tile.  Waves 0..3 (producers) own row tile w: they issue the tile DMA,
+// compute S^T for the tile's 32 keys on the fp8 MFMA (query in two fp8
+// digits), run the online softmax and write P^T and the rows' rescale factors
+// to LDS.  Waves 4..7 (consumers) own output dims 128 (w - 4) .. +127 of all
+// 64 rows and accumulate O^T += V^T P^T for the tile the producers finished in
+// the previous iteration.  Each SIMD holds one producer and one consumer, so
+// the MFMAs of one overlap the other's LDS reads, conversions and softmax
+// instead of every wave passing through the same phases between barriers.
+// Iteration j: producers handle tile j (j < n), consumers tile j - 1 (j > 0).
+// The barrier that opens iteration j says: tile j has landed, P^T of tile
+// j - 1 is written, and the consumers are done with tile j - 2, whose stage
+// then takes the DMA of tile j + NSTAGE - 2.
+constexpr int MLAPC_WAVES = 8;
+constexpr int MLAPC_TK = 32;       // keys per tile
+constexpr int MLAPC_NSTAGE = 8;    // producer's tile, consumer's tile, 6 in flight
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 31] (n > 31 waits for all).
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+#define PA_WAIT_CASE(N) \
+  case N:               \
+    wait_vmcnt<N>();    \
+    break;
+  switch (n) {
+    PA_WAIT_CASE(1) PA_WAIT_CASE(2) PA_WAIT_CASE(3) PA_WAIT_CASE(4) PA_WAIT_CASE(5) PA_WAIT_CASE(6)
+    PA_WAIT_CASE(7) PA_WAIT_CASE(8) PA_WAIT_CASE(9) PA_WAIT_CASE(10) PA_WAIT_CASE(11) PA_WAIT_CASE(12)
+    PA_WAIT_CASE(13) PA_WAIT_CASE(14) PA_WAIT_CASE(15) PA_WAIT_CASE(16) PA_WAIT_CASE(17) PA_WAIT_CASE(18)
+    PA_WAIT_CASE(19) PA_WAIT_CASE(20) PA_WAIT_CASE(21) PA_WAIT_CASE(22) PA_WAIT_CASE(23) PA_WAIT_CASE(24)
+    PA_WAIT_CASE(25) PA_WAIT_CASE(26) PA_WAIT_CASE(27) PA_WAIT_CASE(28) PA_WAIT_CASE(29) PA_WAIT_CASE(30)
+    PA_WAIT_CASE(31)
+    default: wait_vmcnt<0>(); break;
+  }
+#undef PA_WAIT_CASE
+}
 
 template <bool BAL>
-__global__ __launch_bounds__(MLA8_WAVES * 64, 1) void paged_mla8_kernel(AttnParams p) {
-  constexpr int DQK = 576, DV = 512, NW = MLA8_WAVES;
-  constexpr int ROWS = 64;                        // packed rows per workgroup
-  constexpr int NTB = ROWS / 16;                  // row tiles (phase B)
-  constexpr int MDW = DV / 16 / NW;               // output-dim tiles per wave (4)
+__global__ __launch_bounds__(MLAPC_WAVES * 64, 1) void paged_mla_pc_kernel(AttnParams p) {
+  constexpr int DQK = 576, DV = 512;
+  constexpr int ROWS = 64, NTB = ROWS / 16;      // packed rows, row tiles
+  constexpr int MDC = DV / 16 / 4;                // output-dim tiles per consumer (8)
   constexpr int KROW = DQK;
-  constexpr int KTILE = TK * KROW;                // 36 KB raw tile
-  constexpr int NSTAGE = 3;
+  constexpr int T32 = MLAPC_TK;
+  constexpr int KTILE = T32 * KROW;               // 18 KB raw tile
+  constexpr int NSTAGE = MLAPC_NSTAGE;
   constexpr int ND = 2;                           // fp8 digits of the bf16 query
   constexpr int STEPS = QRowsF8<DQK, ND>::STEPS;  // 128-dim steps of S^T (5)
-  using LD = DmaTileLoader<KROW, KROW, NW, true>;
-  constexpr int BLK = LD::KCH / 64;               // 1 KB DMA blocks per tile (36)
-  static_assert(LD::K_DMA == 5 && BLK == 36, "waves 0..3 issue 5 blocks per tile, waves 4..7 issue 4");
+  using LD = DmaTileLoader<KROW, KROW, 4, true, true, T32>;
+  static_assert(LD::K_DMA == 5 && LD::KCH == 18 * 64, "producers 0, 1 issue 5 blocks per tile, 2, 3 issue 4");
+  static_assert((NSTAGE - 3) * 5 <= 31, "wait_vmcnt_dyn covers the tiles in flight");
 
   __shared__ __attribute__((aligned(1024))) uint8_t kst[NSTAGE * KTILE];   // raw tiles
-  __shared__ __attribute__((aligned(16))) half8_t pt_lds[NTB * 2 * 64];    // P^T operands [row tile][key half]
-  __shared__ float mx_lds[2][ROWS];               // row maxima of each key half
-  __shared__ float alpha_lds[ROWS];
-  __shared__ float lrow_lds[2][ROWS];
+  __shared__ __attribute__((aligned(16))) half8_t pt_lds[2][NTB * 64];     // P^T operands per row tile
+  __shared__ float alpha_lds[2][ROWS];
+  __shared__ float lrow_lds[ROWS];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int rt = wave & 3, kh = wave >> 2;        // phase A: row tile and key half
   const int l16 = lane & 15;
   const int grp = lane >> 4;
   int b, g;
   Unit u;
   if (!shared_tile_unit<ROWS, BAL>(p, b, g, u)) return;
-  const int kv_lo = u.kv_lo, n_tiles = u.n_tiles;
-  LD ld;
-  ld.init(p, b, g, wave, kv_lo, u.key_end, n_tiles, lane, lds_addr(kst));
-#pragma unroll
-  for (int st = 0; st < NSTAGE - 1; ++st)
-    if (st < n_tiles) ld.issue(p, st, st);
+  const int kv_lo = u.kv_lo;
+  const int n = u.key_end > kv_lo ? (u.key_end - kv_lo + T32 - 1) / T32 : 0;
+  const int H_q = p.num_q_heads;
 
-  QRowsF8<DQK, ND> q;
-  load_query_f8<DQK, ND>(p, u, g, u.row0 + rt * 16, lane, q);
-  SoftmaxState<1, 0> sa;   // this wave's rows: reference maximum and its key half's row sum
-  softmax_init(sa);
-  float4_t o[MDW][NTB];    // dims 16*(MDW*wave + md) + 4*grp + i, row 16*nt + l16
+  if (wave < 4) {
+    // ------------------------------------------------------------ producer --
+    const int rt = wave;
+    LD ld;
+    ld.init(p, b, g, wave, kv_lo, u.key_end, n, lane, lds_addr(kst));
 #pragma unroll
-  for (int md = 0; md < MDW; ++md)
-#pragma unroll
-    for (int nt = 0; nt < NTB; ++nt) o[md][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
-  const int jr = l16 >> 1, hlf = lane & 1;        // phase B tr8 read (see pv_tile)
-  const half2_t ones2 = {(_Float16)1.0f, (_Float16)1.0f};
+    for (int st = 0; st < NSTAGE - 2; ++st)
+      if (st < n) ld.issue(p, st, st);
+    const int per_tile = wave < 2 ? 5 : 4;        // this wave's DMA blocks per tile
+    QRowsF8<DQK, ND> q;
+    load_query_f8<DQK, ND>(p, u, g, u.row0 + rt * 16, lane, q);
+    float m = -INFINITY, l = 0.f;
+    const half2_t ones2 = {(_Float16)1.0f, (_Float16)1.0f};
+    for (int j = 0; j <= n; ++j) {
+      if (j < n) wait_vmcnt_dyn(min(n - 1 - j, NSTAGE - 3) * per_tile);   // tile j landed
+      __syncthreads();
+      if (j == n) break;
+      if (j + NSTAGE - 2 < n) ld.issue(p, j + NSTAGE - 2, (j + NSTAGE - 2) % NSTAGE);
+      const uint8_t* ks = kst + (j % NSTAGE) * KTILE;
 
-  // Phase B of a tile (V^T from its raw stage, P^T and factors from LDS).
-  auto phase_b = [&](const uint8_t* vs) {
-    {
-      float al[NTB];
-      bool grew = false;
+      float4_t s[2];
+      s[0] = s[1] = float4_t{0.f, 0.f, 0.f, 0.f};
+      auto read_k = [&](int st, int jb) {
+        const int key = jb * 16 + l16;
+        const bool live = st * 128 + 32 * grp < DQK;
+        const int c0 = min(8 * st + 2 * grp, DQK / 16 - 2);
+        const uint4_t a = *(const uint4_t*)(ks + key * KROW + swz<KROW>(c0, key) * 16);
+        const uint4_t c = *(const uint4_t*)(ks + key * KROW + swz<KROW>(c0 + 1, key) * 16);
+        v8i_t r;
 #pragma unroll
-      for (int nt = 0; nt < NTB; ++nt) {
-        al[nt] = alpha_lds[nt * 16 + l16];
-        grew |= al[nt] != 1.f;
+        for (int e = 0; e < 4; ++e) {
+          r[e] = live ? (int)a[e] : 0;
+          r[4 + e] = live ? (int)c[e] : 0;
+        }
+        return r;
+      };
+      v8i_t kr[2];
+      kr[0] = read_k(0, 0);
+      kr[1] = read_k(0, 1);
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+          for (int d = 0; d < ND; ++d)
+            s[jb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kr[jb], q.qd[d][st], s[jb], 0, 0, 0, 127, 0, 127);
+          if (st + 1 < STEPS) kr[jb] = read_k(st + 1, jb);
+        }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i2 = 0; i2 < 2 * (STEPS - 1); ++i2) {
+        __builtin_amdgcn_sched_group_barrier(0x008, ND, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * ND, 0);
+
+      // online softmax of this tile's 32 keys (key of s[jb][i]: kbase + 16 jb + 4 grp + i)
+      const int kbase = kv_lo + j * T32;
+      if (kbase + T32 > u.mask_from) {
+        const int lim = p.causal ? min(u.kv_hi, u.L + q.tok[0] + 1) : u.kv_hi;
 #pragma unroll
-        for (int md = 0; md < MDW; ++md)
+        for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-          for (int nt = 0; nt < NTB; ++nt) o[md][nt] *= al[nt];
+          for (int i = 0; i < 4; ++i)
+            if (kbase + 16 * jb + 4 * grp + i >= lim) s[jb][i] = -INFINITY;
       }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[jb][i]);
+      mx = row_max4(mx) * q.row_mult[0];
+      const float m_new = mx > m + LAZY_LOG2 ? mx : m;
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+      m = m_new;
+      half8_t pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb[i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[0][i], q.row_mult[0], -m_use));
+        pb[4 + i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[1][i], q.row_mult[0], -m_use));
+      }
+      float ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const half2_t pr = {pb[2 * e], pb[2 * e + 1]};
+        ls = __builtin_amdgcn_fdot2(pr, ones2, ls, false);
+      }
+      l = l * alpha + ls;
+      if (grp == 0) alpha_lds[j & 1][rt * 16 + l16] = alpha;
+      pt_lds[j & 1][rt * 64 + lane] = pb;
     }
+    // row sums over the four lane groups; lse
+    const float lt = row_sum4(l);
+    if (grp == 0) lrow_lds[rt * 16 + l16] = lt;
+    const float lse_nat = lt > 0.f ? (m + __log2f(lt)) * LN2F : -INFINITY;
+    if (grp == 0 && q.ok[0]) {
+      const int tok = u.tok0 + q.tok[0];
+      if (u.split) p.part_lse[((int64_t)tok * p.max_chunks + u.c) * H_q + q.head[0]] = lse_nat;
+      else if (p.lse) p.lse[(int64_t)tok * H_q + q.head[0]] = lse_nat;
+    }
+    __syncthreads();   // row sums
+  } else {
+    // ------------------------------------------------------------ consumer --
+    const int cw = wave - 4;
+    float4_t o[MDC][NTB];    // dims 16 (MDC cw + md) + 4 grp + i, row 16 nt + l16
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      const int vrow = 32 * ks2 + (jr < 4 ? 4 * grp + jr : 16 + 4 * grp + (jr - 4));
+    for (int md = 0; md < MDC; ++md)
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt) o[md][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    const int jr = l16 >> 1, hlf = lane & 1;
+    // V^T operand rows in the key order of the P^T operand: lane group grp holds
+    // keys 4 grp .. 4 grp + 3 and 16 + 4 grp .. 16 + 4 grp + 3
+    const int vrow = jr < 4 ? 4 * grp + jr : 16 + 4 * grp + (jr - 4);
+    for (int j = 0; j <= n; ++j) {
+      __syncthreads();
+      if (j == 0) continue;
+      const int t = j - 1, buf = t & 1;
+      const uint8_t* vs = kst + (t % NSTAGE) * KTILE;
+      {
+        float al[NTB];
+        bool grew = false;
+#pragma unroll
+        for (int nt = 0; nt < NTB; ++nt) {
+          al[nt] = alpha_lds[buf][nt * 16 + l16];
+          grew |= al[nt] != 1.f;
+        }
+        if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+#pragma unroll
+          for (int md = 0; md < MDC; ++md)
+#pragma unroll
+            for (int nt = 0; nt < NTB; ++nt) o[md][nt] *= al[nt];
+        }
+      }
       half8_t pbn[NTB];
 #pragma unroll
-      for (int nt = 0; nt < NTB; ++nt) pbn[nt] = pt_lds[(nt * 2 + ks2) * 64 + lane];
+      for (int nt = 0; nt < NTB; ++nt) pbn[nt] = pt_lds[buf][nt * 64 + lane];
 #pragma unroll
-      for (int md = 0; md < MDW; ++md) {
-        const int chunk = wave * MDW + md;
+      for (int md = 0; md < MDC; ++md) {
+        const int chunk = cw * MDC + md;
         const int2_t vraw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (__attribute__((address_space(3))) int2_t*)(vs + vrow * KROW + swz<KROW>(chunk, vrow) * 16 + hlf * 8));
         const half8_t a = bytes8_to_op<true>((uint32_t)vraw[0], (uint32_t)vraw[1]);
@@ -2951,151 +2783,32 @@ __global__ __launch_bounds__(MLA8_WAVES * 64, 1) void paged_mla8_kernel(AttnPara
           o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pbn[nt], o[md][nt], 0, 0, 0);
       }
     }
-  };
-
-  // Barriers per tile: X (tile it landed; every wave is past phase B of tile
-  // it - 1, so its raw stage can take tile it + 2 and P^T can be rewritten),
-  // M (row maxima of both key halves exchanged), P (P^T and factors written).
-  for (int it = 0; it < n_tiles; ++it) {
-    const int stage = it % NSTAGE;
-    // this wave's DMA of tile it + 1 (5 or 4 blocks) may stay in flight
-    if (it + 1 >= n_tiles) wait_vmcnt<0>();
-    else if (wave < 4) wait_vmcnt<5>();
-    else wait_vmcnt<4>();
-    __syncthreads();   // X
-    if (it + NSTAGE - 1 < n_tiles) ld.issue(p, it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
-    const uint8_t* ks = kst + stage * KTILE;
-    const int kbase = kv_lo + it * TK;
-
-    // ---- phase A: S^T for keys 32 kh .. 32 kh + 31 of this wave's 16 rows ----
-    float4_t s[2];
-    s[0] = s[1] = float4_t{0.f, 0.f, 0.f, 0.f};
-    auto read_k = [&](int st, int j) {
-      const int key = (2 * kh + j) * 16 + l16;
-      const bool live = st * 128 + 32 * grp < DQK;
-      const int c0 = min(8 * st + 2 * grp, DQK / 16 - 2);
-      const uint4_t a = *(const uint4_t*)(ks + key * KROW + swz<KROW>(c0, key) * 16);
-      const uint4_t c = *(const uint4_t*)(ks + key * KROW + swz<KROW>(c0 + 1, key) * 16);
-      v8i_t r;
+    __syncthreads();   // row sums
+    const int mode = p.scale_mode;
+    const float vs1 = p.v_scale[mode == PA_SCALE_PER_HEAD ? g : 0];   // per-channel V goes to the four-wave kernel
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        r[e] = live ? (int)a[e] : 0;
-        r[4 + e] = live ? (int)c[e] : 0;
-      }
-      return r;
-    };
-    v8i_t kr[2];
-    kr[0] = read_k(0, 0);
-    kr[1] = read_k(0, 1);
+    for (int nt = 0; nt < NTB; ++nt) {
+      const int r = u.row0 + nt * 16 + l16;
+      if (r >= u.rows_total) continue;
+      const float lt = lrow_lds[nt * 16 + l16];
+      const float inv = lt > 0.f ? vs1 / lt : 0.f;
+      const int tok = u.tok0 + r / u.G;
+      const int h = g * u.G + r % u.G;
+      float* prow = u.split ? p.part_o + (((int64_t)tok * p.max_chunks + u.c) * H_q + h) * DV : nullptr;
+      uint16_t* orow = p.out + ((int64_t)tok * H_q + h) * DV;
 #pragma unroll
-    for (int st = 0; st < STEPS; ++st)
+      for (int md = 0; md < MDC; ++md) {
+        const int d = (cw * MDC + md) * 16 + grp * 4;
+        float4_t v;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int d = 0; d < ND; ++d)
-          s[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kr[j], q.qd[d][st], s[j], 0, 0, 0, 127, 0, 127);
-        if (st + 1 < STEPS) kr[j] = read_k(st + 1, j);
-      }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i2 = 0; i2 < 2 * (STEPS - 1); ++i2) {
-      __builtin_amdgcn_sched_group_barrier(0x008, ND, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * ND, 0);
-
-
-    // ---- softmax over the whole 64-key tile, the maxima shared by the two halves ----
-    const int k0 = kbase + 32 * kh;   // key of s[j][i]: k0 + 16 j + 4 grp + i
-    if (kbase + TK > u.mask_from) {
-      const int lim = p.causal ? min(u.kv_hi, u.L + q.tok[0] + 1) : u.kv_hi;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (k0 + 16 * j + 4 * grp + i >= lim) s[j][i] = -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[j][i]);
-    mx = row_max4(mx) * q.row_mult[0];
-    if (grp == 0) mx_lds[kh][rt * 16 + l16] = mx;
-    __syncthreads();   // M
-    mx = fmaxf(mx_lds[0][rt * 16 + l16], mx_lds[1][rt * 16 + l16]);
-    const float m_new = mx > sa.m[0] + LAZY_LOG2 ? mx : sa.m[0];
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(sa.m[0] - m_use);
-    sa.m[0] = m_new;
-    half8_t pb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pb[i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[0][i], q.row_mult[0], -m_use));
-      pb[4 + i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[1][i], q.row_mult[0], -m_use));
-    }
-    float ls = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const half2_t pr = {pb[2 * e], pb[2 * e + 1]};
-      ls = __builtin_amdgcn_fdot2(pr, ones2, ls, false);
-    }
-    sa.l[0] = sa.l[0] * alpha + ls;
-    if (kh == 0 && grp == 0) alpha_lds[rt * 16 + l16] = alpha;
-    pt_lds[(rt * 2 + kh) * 64 + lane] = pb;
-    __syncthreads();   // P
-    phase_b(ks);
-  }
-
-  // ---- epilogue: row sums of both key halves, lse, outputs per dim slice ----
-  const int H_q = p.num_q_heads;
-  {
-    const float lt = row_sum4(sa.l[0]);
-    if (grp == 0) lrow_lds[kh][rt * 16 + l16] = lt;
-  }
-  __syncthreads();
-  if (kh == 0) {
-    const float lt = lrow_lds[0][rt * 16 + l16] + lrow_lds[1][rt * 16 + l16];
-    const float lse_nat = lt > 0.f ? (sa.m[0] + __log2f(lt)) * LN2F : -INFINITY;
-    if (grp == 0 && q.ok[0]) {
-      const int tok = u.tok0 + q.tok[0];
-      if (u.split) p.part_lse[((int64_t)tok * p.max_chunks + u.c) * H_q + q.head[0]] = lse_nat;
-      else if (p.lse) p.lse[(int64_t)tok * H_q + q.head[0]] = lse_nat;
-    }
-  }
-  const int mode = p.scale_mode;
-  float4_t vsc[MDW];
-  if (mode == PA_SCALE_PER_CHANNEL) {
-#pragma unroll
-    for (int md = 0; md < MDW; ++md)
-      vsc[md] = *(const float4_t*)(p.v_scale + (int64_t)g * DV + (wave * MDW + md) * 16 + grp * 4);
-  } else {
-    const float v = p.v_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
-#pragma unroll
-    for (int md = 0; md < MDW; ++md) vsc[md] = float4_t{v, v, v, v};
-  }
-#pragma unroll
-  for (int nt = 0; nt < NTB; ++nt) {
-    const int r = u.row0 + nt * 16 + l16;
-    if (r >= u.rows_total) continue;
-    const float lt = lrow_lds[0][nt * 16 + l16] + lrow_lds[1][nt * 16 + l16];
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int tok = u.tok0 + r / u.G;
-    const int h = g * u.G + r % u.G;
-    float* prow = u.split ? p.part_o + (((int64_t)tok * p.max_chunks + u.c) * H_q + h) * DV : nullptr;
-    uint16_t* orow = p.out + ((int64_t)tok * H_q + h) * DV;
-#pragma unroll
-    for (int md = 0; md < MDW; ++md) {
-      const int d = (wave * MDW + md) * 16 + grp * 4;
-      float4_t v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = o[md][nt][i] * inv * vsc[md][i];
-      if (u.split) {
-        *(float4_t*)(prow + d) = v;
-      } else {
-        const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        const uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-        *(int2_t*)(orow + d) = int2_t{(int)w0, (int)w1};
+        for (int i = 0; i < 4; ++i) v[i] = o[md][nt][i] * inv;
+        if (u.split) {
+          *(float4_t*)(prow + d) = v;
+        } else {
+          const uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+          const uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+          *(int2_t*)(orow + d) = int2_t{(int)w0, (int)w1};
+        }
       }
     }
   }
@@ -3219,15 +2932,15 @@ __global__ __launch_bounds__(64) void gather_reg_kernel(TileWalkParams w) {
 
 // The shared-tile / MLA kernels' loader: each tile lands in one LDS stage by
 // DMA (NW waves), then is copied out unswizzled.
-template <int KROW, int VROW, int NW, bool SHARED>
+template <int KROW, int VROW, int NW, bool SHARED, int TKEYS = TK>
 __global__ __launch_bounds__(64 * NW) void gather_dma_kernel(TileWalkParams w) {
-  using LD = DmaTileLoader<KROW, VROW, NW, SHARED>;
+  using LD = DmaTileLoader<KROW, VROW, NW, SHARED, true, TKEYS>;
   __shared__ __attribute__((aligned(1024))) uint8_t stage[LD::STAGE];
   int b, g, kv_lo, key_end;
   if (!walk_unit(w, b, g, kv_lo, key_end)) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int n_tiles = (key_end - kv_lo + TK - 1) / TK;
+  const int n_tiles = (key_end - kv_lo + TKEYS - 1) / TKEYS;
   LD ld;
   ld.init(w.a, b, g, wave, kv_lo, key_end, n_tiles, lane, lds_addr(stage));
   const int64_t bg = (int64_t)b * w.a.num_kv_heads + g;
@@ -3240,7 +2953,7 @@ __global__ __launch_bounds__(64 * NW) void gather_dma_kernel(TileWalkParams w) {
       const int c2 = is_k ? ch : ch - LD::KCH;
       const int cpr = is_k ? LD::KCPR : LD::VCPR;
       const int row = c2 / cpr, pos = c2 % cpr;
-      const int key = kv_lo + it * TK + row;
+      const int key = kv_lo + it * TKEYS + row;
       if (key >= key_end) continue;
       const int off = is_k ? row * KROW + swz<KROW>(pos, row) * 16 : LD::KTILE + row * VROW + swz<VROW>(pos, row) * 16;
       const uint4_t v = *(const uint4_t*)(stage + off);
@@ -3294,11 +3007,11 @@ template <bool FP8, bool HILO>
 hipError_t launch_mla(const AttnParams& p, dim3 grid, hipStream_t stream) {
   // the balanced split's planner is a variant of its own (it costs the main
   // loop SGPR spills)
-  if constexpr (FP8 && !HILO) {   // e4m3fn keys with a one-part query: the eight-wave kernel
+  if constexpr (FP8 && !HILO) {   // e4m3fn keys with a two-digit query: producer/consumer kernel
     if (p.balanced)
-      hipLaunchKernelGGL((paged_mla8_kernel<true>), grid, dim3(MLA8_WAVES * 64), 0, stream, p);
+      hipLaunchKernelGGL((paged_mla_pc_kernel<true>), grid, dim3(MLAPC_WAVES * 64), 0, stream, p);
     else
-      hipLaunchKernelGGL((paged_mla8_kernel<false>), grid, dim3(MLA8_WAVES * 64), 0, stream, p);
+      hipLaunchKernelGGL((paged_mla_pc_kernel<false>), grid, dim3(MLAPC_WAVES * 64), 0, stream, p);
   } else if (p.balanced) {
     hipLaunchKernelGGL((paged_mla2_kernel<FP8, HILO, true>), grid, dim3(MLA_WAVES * 64), 0, stream, p);
   } else {
@@ -3329,7 +3042,7 @@ int occ_one() {
 }
 template <bool FP8, bool HILO>
 int occ_mla() {
-  if constexpr (FP8 && !HILO) return occupancy_of(paged_mla8_kernel<false>, MLA8_WAVES * 64);
+  if constexpr (FP8 && !HILO) return occupancy_of(paged_mla_pc_kernel<false>, MLAPC_WAVES * 64);
   return occupancy_of(paged_mla2_kernel<FP8, HILO, false>, MLA_WAVES * 64);
 }
 template <int D, bool FP8, int NT, bool HILO, int KS, bool TREE>
@@ -3523,6 +3236,7 @@ hipError_t launch_tile_gather(int loader, int dqk, int dv, bool shared_kv, const
     if (dqk == 128 && loader == 3) PA_TG((gather_dma_kernel<128, 128, 3, false>), 192);
   }
   if (loader == 2 && shared_kv && dqk == 576) PA_TG((gather_dma_kernel<576, 576, MLA_WAVES, true>), 64 * MLA_WAVES);
+  if (loader == 4 && shared_kv && dqk == 576) PA_TG((gather_dma_kernel<576, 576, 4, true, 32>), 256);
 #undef PA_TG
   return hipErrorInvalidValue;
 }

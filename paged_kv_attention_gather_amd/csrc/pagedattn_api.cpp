@@ -249,7 +249,7 @@ int32_t attention_common(const pa_problem* p, bool decode, int32_t q_len, int64_
   if (shared) {
     cfg.nt = 1;
     cfg.nw = 4;
-    cfg.nstage = 1;  // MLA kernel
+    cfg.nstage = 1;  // MLA kernels: 64 rows per workgroup
   } else if (rows_max <= 32) {
     // register-staged decode kernel
     cfg.nt = (int)ceil_div(rows_max, 16);
@@ -541,8 +541,8 @@ int32_t pa_gather_debug(const pa_problem* prob, int32_t loader, const void* k_ca
                         int32_t t_max, uint8_t* k_dst, uint8_t* v_dst, void* stream) {
   int32_t st = check_problem(prob);
   if (st != PA_OK) return st;
-  if (loader < PA_GATHER_ROWS || loader > PA_GATHER_DMA_3W)
-    return fail(PA_ERR_INVALID_ARG, "loader %d: PA_GATHER_ROWS, _DECODE, _DMA_4W or _DMA_3W", loader);
+  if (loader < PA_GATHER_ROWS || loader > PA_GATHER_DMA_MLA32)
+    return fail(PA_ERR_INVALID_ARG, "loader %d: PA_GATHER_ROWS, _DECODE, _DMA_4W, _DMA_3W or _DMA_MLA32", loader);
   if (t_max < 0) return fail(PA_ERR_INVALID_ARG, "t_max %d < 0", t_max);
   if ((int64_t)t_max > (int64_t)prob->max_pages_per_seq * prob->page_size)
     return fail(PA_ERR_INVALID_ARG, "t_max %d exceeds the block table capacity", t_max);

@@ -261,7 +261,8 @@ def test_gather_validation(lib):
     assert g(P_, 0, FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, None, None) == L.PA_ERR_INVALID_ARG
     assert g(P_, 0, None, FAKE, FAKE, FAKE, FAKE, 64, FAKE, None, None) == L.PA_ERR_INVALID_ARG
     assert g(P_, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 16 * 64 + 1, FAKE, None, None) == L.PA_ERR_INVALID_ARG
-    assert g(P_, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, None, None) == L.PA_ERR_INVALID_ARG   # loader
+    assert g(P_, 5, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, None, None) == L.PA_ERR_INVALID_ARG   # loader
+    assert g(P_, -1, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, None, None) == L.PA_ERR_INVALID_ARG
     assert g(P_, 0, FAKE, None, FAKE, FAKE, FAKE, 64, FAKE, FAKE, None) == L.PA_ERR_INVALID_ARG   # V dst, no V
     mla = base_problem(num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, q_row_stride=16 * 576,
                        k_stride_page=64 * 576, k_stride_head=64 * 576, k_stride_token=576,

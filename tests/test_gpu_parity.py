@@ -28,17 +28,18 @@ def _run(w, **kw):
 #
 # Byte-exact gathers through each loader the attention kernels run: one key
 # row at a time, the decode kernel's register tile loader, and the LDS-DMA
-# tile loader with 4 or 3 waves (also for the shared 576-byte latent rows),
-# over the workloads' chunked units (tiles that end a chunk or a sequence,
-# one-page fast path and page sizes below 64).
+# tile loader with 4 or 3 waves (also for the shared 576-byte latent rows, in
+# 64-key tiles and in the e4m3fn MLA kernel's 32-key tiles), over the
+# workloads' chunked units (tiles that end a chunk or a sequence, one-page
+# fast path and page sizes below 64).
 
-LOADERS = {"rows": 0, "decode": 1, "dma4": 2, "dma3": 3}
+LOADERS = {"rows": 0, "decode": 1, "dma4": 2, "dma3": 3, "mla32": 4}
 
 
 def _loaders_for(w):
     if w.shared_kv:
-        return ["rows", "dma4"]
-    return list(LOADERS)
+        return ["rows", "dma4", "mla32"]
+    return ["rows", "decode", "dma4", "dma3"]
 
 
 def _gather(w, loader, reqs=None):
