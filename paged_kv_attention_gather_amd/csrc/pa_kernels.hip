@@ -1475,6 +1475,34 @@ struct DmaTileLoader {
     }
   }
 
+  // Split issue of a K-only (SHARED) tile, for a wave that spreads its DMA
+  // instructions between MFMAs (an issue stalls while the CU's load path is
+  // full; with MFMAs in flight the stall is hidden): begin() returns true on
+  // the one-page fast path, where part(j), j < K_DMA, issues block j;
+  // otherwise begin() has issued the whole tile itself.
+  const uint8_t* part_kb;
+  uint32_t part_kdst;
+  __device__ __forceinline__ bool begin(const AttnParams& p, int tile, int stage) {
+    static_assert(SHARED, "split issue covers K-only tiles");
+    const int kbase = kv_lo + tile * TKEYS;
+    if (fast_addr && kbase + TKEYS <= key_end) {
+      const int pg0 = kbase >> page_shift;
+      if (pg0 < pw_base || pg0 > pw_base + 63) {
+        pw_base = pg0;
+        pw_val = load_i32_sync(table_row + min(pg0 + (int)(threadIdx.x & 63), last_page));
+      }
+      const int pp0 = __builtin_amdgcn_readlane(pw_val, pg0 - pw_base);
+      part_kb = paged_row(p.k_cache, pp0, kbase, page_shift, g, p.k_stride_page, p.k_stride_head, p.k_stride_token);
+      part_kdst = smem_base + stage * STAGE;
+      return true;
+    }
+    issue(p, tile, stage);
+    return false;
+  }
+  __device__ __forceinline__ void part(int j) {
+    if ((j * NW + wave) * 64 < KCH) dma16_s(k_offset(j), part_kb, part_kdst + (j * NW + wave) * 1024);
+  }
+
   // Issues this wave's share of tile `tile` into LDS stage `stage`.
   __device__ __forceinline__ void issue(const AttnParams& p, int tile, int stage) {
     const int kbase = kv_lo + tile * TKEYS;
@@ -2652,7 +2680,8 @@ __global__ __launch_bounds__(MLAPC_WAVES * 64, 1) void paged_mla_pc_kernel(AttnP
       if (j < n) wait_vmcnt_dyn(min(n - 1 - j, NSTAGE - 3) * per_tile);   // tile j landed
       __syncthreads();
       if (j == n) break;
-      if (j + NSTAGE - 2 < n) ld.issue(p, j + NSTAGE - 2, (j + NSTAGE - 2) % NSTAGE);
+      // tile j + NSTAGE - 2: one DMA block per QK step below (see begin())
+      const bool split = j + NSTAGE - 2 < n && ld.begin(p, j + NSTAGE - 2, (j + NSTAGE - 2) % NSTAGE);
       const uint8_t* ks = kst + (j % NSTAGE) * KTILE;
 
       float4_t s[2];
@@ -2671,11 +2700,12 @@ __global__ __launch_bounds__(MLAPC_WAVES * 64, 1) void paged_mla_pc_kernel(AttnP
         }
         return r;
       };
+      static_assert(LD::K_DMA == STEPS, "one DMA block per QK step");
       v8i_t kr[2];
       kr[0] = read_k(0, 0);
       kr[1] = read_k(0, 1);
 #pragma unroll
-      for (int st = 0; st < STEPS; ++st)
+      for (int st = 0; st < STEPS; ++st) {
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
@@ -2683,13 +2713,22 @@ __global__ __launch_bounds__(MLAPC_WAVES * 64, 1) void paged_mla_pc_kernel(AttnP
             s[jb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kr[jb], q.qd[d][st], s[jb], 0, 0, 0, 127, 0, 127);
           if (st + 1 < STEPS) kr[jb] = read_k(st + 1, jb);
         }
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        // this step's MFMAs interleaved with the next step's operand reads
+        if (st == 0) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        if (st + 1 < STEPS) {
 #pragma unroll
-      for (int i2 = 0; i2 < 2 * (STEPS - 1); ++i2) {
-        __builtin_amdgcn_sched_group_barrier(0x008, ND, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          for (int i2 = 0; i2 < 2; ++i2) {
+            __builtin_amdgcn_sched_group_barrier(0x008, ND, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * ND, 0);
+        }
+        // the accumulators pass through an empty asm here, so this step's
+        // MFMAs are issued before the DMA block (otherwise they sink to the softmax)
+        asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+        if (split) ld.part(st);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * ND, 0);
 
       // online softmax of this tile's 32 keys (key of s[jb][i]: kbase + 16 jb + 4 grp + i)
       const int kbase = kv_lo + j * T32;
