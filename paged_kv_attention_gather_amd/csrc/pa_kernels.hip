@@ -3134,8 +3134,9 @@ struct Entry {
 #define PA_SET(D, FP8, HL)                                                                       \
   PA_DEC(D, FP8, 1, HL, 1), PA_DEC(D, FP8, 1, HL, 2), PA_DEC(D, FP8, 1, HL, 4),                    \
       PA_DEC(D, FP8, 2, HL, 1), PA_DEC(D, FP8, 2, HL, 2), PA_DEC(D, FP8, 2, HL, 4),                 \
-      PA_ENTRY(D, D, FP8, 1, 3, false, HL, 2), PA_ENTRY(D, D, FP8, 1, 4, false, HL, 2),             \
-      PA_ENTRY(D, D, FP8, 2, 4, false, HL, 2)
+      PA_ENTRY(D, D, FP8, 1, 3, false, HL, 2), PA_ENTRY(D, D, FP8, 1, 4, false, HL, 2)
+// more than 64 rows: 2 x 4 waves on raw tiles (D = 64; D = 128 takes the f16-tile kernel)
+#define PA_WIDE(D, FP8, HL) PA_ENTRY(D, D, FP8, 2, 4, false, HL, 2)
 // draft-tree variants: up to 64 packed rows, one wave per decode unit
 #define PA_TREE_SET(D, FP8, HL)                                                                  \
   PA_DEC_T(D, FP8, 1, HL, 1, true), PA_DEC_T(D, FP8, 2, HL, 1, true),                              \
@@ -3144,6 +3145,8 @@ struct Entry {
 const Entry kTable[] = {
     PA_SET(64, false, false),   PA_SET(64, false, true),
     PA_SET(64, true, false),    PA_SET(64, true, true),
+    PA_WIDE(64, false, false),  PA_WIDE(64, false, true),
+    PA_WIDE(64, true, false),   PA_WIDE(64, true, true),
     PA_SET(128, false, false), PA_SET(128, false, true),
     PA_SET(128, true, false),  PA_SET(128, true, true),
     PA_MLA(true, false), PA_MLA(true, true), PA_MLA(false, false), PA_MLA(false, true),

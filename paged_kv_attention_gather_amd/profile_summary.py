@@ -34,10 +34,10 @@ WORKLOADS = {
 
 KT_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
           "-d $OUT/kt_c{c} -o run -- python3 $R/bench.py --config {c} --steps 10 "
-          "--warmup 3 --no-cpu-baseline")
+          "--warmup 3 --no-cpu-baseline --no-extra-configs")
 PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} --output-format csv "
            "-d $OUT/pmc_c{c}_{ctr} -o run -- python3 $R/bench.py --config {c} --steps 3 "
-           "--warmup 1 --no-cpu-baseline")
+           "--warmup 1 --no-cpu-baseline --no-extra-configs")
 COPY_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} --output-format csv "
             "-d $OUT/pmc_copy_{ctr} -o run -- python3 $R/bench.py --copy-probe-mib {mib}")
 
