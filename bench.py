@@ -114,8 +114,7 @@ def kernel_name(dp):
     """Name of the attention kernel the library launches for this problem."""
     w = dp.w
     if w.shared_kv:
-        eight_waves = w.kv_dtype == "fp8_e4m3" and w.q_dtype == "bf16" and w.scale_mode != "channel"
-        return "paged_mla_pc_kernel" if eight_waves else "paged_mla2_kernel"
+        return "paged_mla_pc_kernel" if w.kv_dtype == "fp8_e4m3" else "paged_mla_i8_kernel"
     rows = (int(w.decode_q_len) if dp.decode else int(w.q_lens.max())) * (w.num_q_heads // w.num_kv_heads)
     return "paged_decode_kernel" if rows <= 32 else "paged_attn_kernel"
 

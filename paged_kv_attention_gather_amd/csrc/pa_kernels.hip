@@ -901,23 +901,35 @@ __device__ __forceinline__ void query_finish_i8(const AttnParams& p, const Unit&
 }
 
 // Query rows for S^T = K Q^T on the fp8 MFMA (v_mfma_scale_f32_16x16x128_
-// f8f6f4, unit scales), used with e4m3fn caches: the K bytes go to the MFMA as
-// they are, and each query row, scaled by a power of two that puts its
-// largest element in [64, 128), is split into ND e4m3fn digits q = d_0 + ...
-// + d_{ND-1}, each the nearest e4m3fn value to what the previous digits left.
-// A bf16 value (8 significant bits) is two 4-bit digits exactly, unless the
-// second digit falls below e4m3fn's subnormal step 2^-9 (elements under 2^-16
-// of the row maximum); fp32 queries and per-channel folded scales take three
-// digits (2^-12 relative per element).  Lane l holds, per 128-dim step s,
-// bytes for dims 128 s + 32 (l / 16) + [0, 32) of row l % 16 (the operand
-// layout of the instruction: A and B rows by lane % 16, 32 consecutive k per
-// lane group), zero past the head dim.
+// f8f6f4), used with e4m3fn caches: the K bytes go to the MFMA as they are
+// (block scale 1), and the query is split into ND e4m3fn digits q = d_0 + ...
+// + d_{ND-1}, each the nearest e4m3fn value to what the earlier digits left.
+// The instruction scales each 32-deep K block of each row by a power of two
+// (E8M0).  Its K order: lane group g (lanes 16g..16g+15) holds K indices
+// 16g + [0, 16) in bytes 0..15 and 64 + 16g + [0, 16) in bytes 16..31, so
+// block b (K indices 32b..32b+31) is one 16-byte half (the first for b < 2)
+// of lane groups 2 (b % 2) and 2 (b % 2) + 1, and its scale is read from lane
+// group b (measured on the GPU; an unscaled product cannot tell, since A and B
+// share the order).  Every block of the query is scaled so that its largest
+// element lies in (224, 448], the top of e4m3fn's range, and the MFMA scales
+// it back.  A bf16 value (8 significant bits) is then two 4-bit digits
+// exactly unless its second digit falls below e4m3fn's subnormal step, i.e.
+// for elements under ~2^-9 of their block's maximum (an error of at most
+// 2^-18 of that maximum each); fp32 queries and per-channel folded scales take
+// three digits.  Scaling per block rather than per row keeps a few large
+// channels from pushing the rest of the row into that range (rows with two
+// channels 64x the rest: LSE error 3.1e-3 with one scale per row, 9.3e-5 per
+// block, in a CPU model of the split).  Lane l holds, per 128-dim step s,
+// bytes for dims 128 s + 32 (l / 16) + [0, 32) of row l % 16 (the same
+// permutation for K and Q), zero past the head dim, and in sc[s] the E8M0
+// exponent of block l / 16 of its row.
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 
 template <int DQK, int ND>
 struct QRowsF8 {
   static constexpr int STEPS = (DQK + 127) / 128;
   v8i_t qd[ND][STEPS];
+  int sc[STEPS];      // E8M0 block scale (2^(sc - 127)) of this lane's block per step
   float row_mult[1];
   float kbias[1];   // 0: K operands are exact
   int tok[1], head[1];
@@ -965,62 +977,61 @@ __device__ __forceinline__ void load_query_f8(const AttnParams& p, const Unit& u
       for (int e = 0; e < 4; ++e) { x[e] *= p.qk_mult * a[e]; x[4 + e] *= p.qk_mult * b[e]; }
     }
   };
-  float amax = 0.f;
-  auto amax8 = [&](int d0) {
-    float x[8];
-    load8(d0, x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
-    __builtin_amdgcn_sched_barrier(0);   // keep the row's loads from piling up in registers
+  q.row_mult[0] = fold_channel ? 1.f : p.qk_mult * k_uniform;
+  // 2^k2 puts amax = m 2^ex (m in [0.5, 1)) into (224, 448]
+  auto block_k2 = [](float amax) {
+    int ex = 0;
+    const float m = amax > 0.f ? frexpf(amax, &ex) : 1.f;
+    return min(max((m > 0.875f ? 8 : 9) - ex, -120), 120);
   };
 #pragma unroll
-  for (int s = 0; s < STEPS; ++s)
+  for (int st = 0; st < STEPS; ++st) {
+    float x[32];   // dims 128 st + 32 grp + [0, 32)
 #pragma unroll
-    for (int j8 = 0; j8 < 4; ++j8) amax8(128 * s + 32 * grp + 8 * j8);
-  amax = row_max4(amax);
-  int ex = 0;
-  if (amax > 0.f) (void)frexpf(amax, &ex);      // amax < 2^ex
-  const int k2 = min(max(7 - ex, -120), 120);   // largest element in [64, 128)
-  const float up = ldexpf(1.f, k2);
-  q.row_mult[0] = ldexpf(1.f, -k2) * (fold_channel ? 1.f : p.qk_mult * k_uniform);
-  q.kbias[0] = 0.f;
-  // digits of 8 elements from dim d0: two words (4 codes each) per digit
-  auto digits8 = [&](int d0, uint32_t (&w)[ND][2]) {
-    float x[8];
-    load8(d0, x);
+    for (int j8 = 0; j8 < 4; ++j8) load8(128 * st + 32 * grp + 8 * j8, x + 8 * j8);
+    float a_lo = 0.f, a_hi = 0.f;
 #pragma unroll
-    for (int d = 0; d < ND; ++d) w[d][0] = w[d][1] = 0u;
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      float r0 = x[e] * up, r1 = x[e + 1] * up;
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        // two e4m3fn (OCP) codes in one 16-bit half, and their exact values
-        typedef short short2_t __attribute__((ext_vector_type(2)));
-        const short2_t zero2 = {0, 0};
-        const uint32_t pk =
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(zero2, r0, r1, 1.0f, false)) &
-            0xffffu;
-        const auto back = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)pk, 1.0f, false);
-        r0 -= back[0];
-        r1 -= back[1];
-        w[d][(e / 2) >> 1] |= pk << (16 * ((e / 2) & 1));
-      }
+    for (int e = 0; e < 16; ++e) {
+      a_lo = fmaxf(a_lo, fabsf(x[e]));
+      a_hi = fmaxf(a_hi, fabsf(x[16 + e]));
     }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-#pragma unroll
-  for (int s = 0; s < STEPS; ++s)
+    // block maxima: this lane pair's two blocks (xor 16), the other pair's (xor 32)
+    const float p_lo = xor16_max(a_lo), p_hi = xor16_max(a_hi);
+    const float o_lo = __shfl_xor(p_lo, 32, 64), o_hi = __shfl_xor(p_hi, 32, 64);
+    const int k_lo = block_k2(p_lo), k_hi = block_k2(p_hi);
+    // block grp's maximum: groups 0, 1 hold blocks 0 (lo) and 2 (hi), groups 2, 3 blocks 1 and 3
+    const float bmax = grp == 0 ? p_lo : grp == 1 ? o_lo : grp == 2 ? o_hi : p_hi;
+    q.sc[st] = 127 - block_k2(bmax);
+    const float up_lo = ldexpf(1.f, k_lo), up_hi = ldexpf(1.f, k_hi);
 #pragma unroll
     for (int j8 = 0; j8 < 4; ++j8) {
-      uint32_t w[ND][2];
-      digits8(128 * s + 32 * grp + 8 * j8, w);
+      const float up = j8 < 2 ? up_lo : up_hi;
+      uint32_t w[ND][2] = {};
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float r0 = x[8 * j8 + e] * up, r1 = x[8 * j8 + e + 1] * up;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          // two e4m3fn (OCP) codes in one 16-bit half, and their exact values
+          typedef short short2_t __attribute__((ext_vector_type(2)));
+          const short2_t zero2 = {0, 0};
+          const uint32_t pk =
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(zero2, r0, r1, 1.0f, false)) &
+              0xffffu;
+          const auto back = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)pk, 1.0f, false);
+          r0 -= back[0];
+          r1 -= back[1];
+          w[d][(e / 2) >> 1] |= pk << (16 * ((e / 2) & 1));
+        }
+      }
 #pragma unroll
       for (int d = 0; d < ND; ++d) {
-        q.qd[d][s][2 * j8] = (int)w[d][0];
-        q.qd[d][s][2 * j8 + 1] = (int)w[d][1];
+        q.qd[d][st][2 * j8] = (int)w[d][0];
+        q.qd[d][st][2 * j8 + 1] = (int)w[d][1];
       }
     }
+    __builtin_amdgcn_sched_barrier(0);   // one step's 32 elements live at a time
+  }
 }
 
 // S^T += K Q^T over one 64-dim step on the int8 MFMA: `a` holds the lane's 16
@@ -2324,19 +2335,18 @@ __global__ __launch_bounds__(64, NT == 1 ? 2 : 1) void paged_decode_persistent_k
 
 constexpr int MLA_WAVES = 4;  // waves of the four-wave MLA kernel
 
-// MLA, four-wave form (int8 caches, fp32 queries, per-channel K scales).  The raw 64 x 576 tile arrives
-// by LDS DMA into a three-stage ring (two tiles ahead).  Phase A (wave w, rows
-// 16w..16w+15) feeds the raw K bytes to the MFMA as they are: e4m3fn keys to
-// the fp8 MFMA against the query in fp8 digits (QRowsF8), int8 keys to the
-// int8 MFMA against three int8 digits (QRowsI8); converting K to f16 costs a
-// quarter-rate conversion per two values, about 3x the MFMA time of the tile.
-// The softmax writes P^T and the per-row rescale factors to LDS.  Phase B (wave w, output dims 128w..128w+127 of all 64 rows) reads
-// V^T from the same raw rows with the 8-bit LDS transpose read and converts
-// it in registers (int8 V as the offset value 1152 + x, removed in the
-// epilogue).  Two barriers per tile: the tile has landed for every wave (and
-// the stage two tiles back is free again), then P^T is complete.
-template <bool FP8, bool HILO, bool BAL>
-__global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla2_kernel(AttnParams p) {
+// MLA, int8 caches: four waves.  The raw 64 x 576 tile arrives by LDS DMA
+// into a three-stage ring (two tiles ahead).  Phase A (wave w, rows
+// 16w..16w+15) feeds the raw K bytes to the int8 MFMA as they are, against
+// three int8 digits of the query (QRowsI8: fp32 queries and per-channel K
+// scales need nothing more).  The softmax writes P^T and the per-row rescale
+// factors to LDS.  Phase B (wave w, output dims 128w..128w+127 of all 64 rows)
+// reads V^T from the same raw rows with the 8-bit LDS transpose read and
+// converts it in registers (int8 V as the offset value 1152 + x, removed in
+// the epilogue).  Two barriers per tile: the tile has landed for every wave
+// (and the stage two tiles back is free again), then P^T is complete.
+template <bool BAL>
+__global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_i8_kernel(AttnParams p) {
   constexpr int DQK = 576, DV = 512, NW = MLA_WAVES;
   constexpr int ROWS = 16 * NW;                   // 64 packed rows per workgroup
   constexpr int NTB = ROWS / 16;                  // row tiles in phase B
@@ -2345,7 +2355,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla2_kernel(AttnParam
   constexpr int KTILE = TK * KROW;                // 36 KB raw tile
   constexpr int NSTAGE = 3;
   constexpr int SP = DQK / 64;                    // 64-dim steps of S^T (9)
-  constexpr float KV_OFF = FP8 ? 0.f : 1152.f;    // int8 V operands carry 1152 + x
+  constexpr float KV_OFF = 1152.f;                // int8 V operands carry 1152 + x
   using LD = DmaTileLoader<KROW, KROW, NW, true>;
   static_assert(LD::KCH % (64 * NW) == 0, "every wave issues the same number of DMA blocks");
   constexpr int DMA_W = LD::K_DMA;                // per wave per tile
@@ -2369,14 +2379,9 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla2_kernel(AttnParam
   for (int st = 0; st < NSTAGE - 1; ++st)
     if (st < n_tiles) ld.issue(p, st, st);
 
-  // S^T runs on the fp8 MFMA (e4m3fn caches, query in fp8 digits) or the
-  // int8 MFMA (int8 caches, query in three int8 digits): K bytes go to the
-  // MFMA as they are stored, with no conversion.
-  constexpr int ND = HILO ? 3 : 2;
-  using QT = typename std::conditional<FP8, QRowsF8<DQK, ND>, QRowsI8<DQK, 1>>::type;
-  QT q;
-  if constexpr (FP8) load_query_f8<DQK, ND>(p, u, g, u.row0 + wave * 16, lane, q);
-  else load_query_i8<DQK>(p, u, g, u.row0 + wave * 16, lane, q);
+  // S^T on the int8 MFMA: K bytes go to the MFMA as they are stored
+  QRowsI8<DQK, 1> q;
+  load_query_i8<DQK>(p, u, g, u.row0 + wave * 16, lane, q);
   SoftmaxState<1, 0> sa;   // phase-A row state (m, l); O lives in phase B
   softmax_init(sa);
   float4_t o[MDW][NTB];    // dims 16*(MDW*wave + md) + 4*grp + i, row 16*nt + l16
@@ -2409,90 +2414,40 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla2_kernel(AttnParam
 
     // ---- phase A: S^T = K Q^T for this wave's rows, K bytes straight to the MFMA ----
     float4_t s[4][1];
-    if constexpr (FP8) {
+    {
+    constexpr int KSTEPS = DQK / 64;
+    int4_t acc[4][3][1];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) s[mt][0] = float4_t{0.f, 0.f, 0.f, 0.f};
-      // lane: key mt*16 + l16, bytes 128 st + 32 grp .. + 32 (chunks 8 st + 2 grp, + 1);
-      // dims past 576 (the second half of the last step) are zero operands
-      constexpr int STEPS = QRowsF8<DQK, ND>::STEPS;
-      // dims 576..639 of the last step are zero operands: those lanes read
-      // the row's last two chunks (valid bytes) and drop them, with no branch,
-      // so that phase A stays one scheduling region
-      auto read_k = [&](int st, int mt) {
-        const int key = mt * 16 + l16;
-        const bool live = st * 128 + 32 * grp < DQK;
-        const int c0 = min(8 * st + 2 * grp, DQK / 16 - 2);
-        const uint4_t a = *(const uint4_t*)(ks + key * KROW + swz<KROW>(c0, key) * 16);
-        const uint4_t c = *(const uint4_t*)(ks + key * KROW + swz<KROW>(c0 + 1, key) * 16);
-        v8i_t r;
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          r[e] = live ? (int)a[e] : 0;
-          r[4 + e] = live ? (int)c[e] : 0;
-        }
-        return r;
-      };
-      // one operand buffer per key tile: the next step's bytes for key tile mt
-      // are read once mt's MFMAs of this step have issued, and arrive while the
-      // other key tiles' MFMAs run
-      v8i_t kr[4];
+      for (int d = 0; d < 3; ++d) acc[mt][d][0] = int4_t{0, 0, 0, 0};
+    int4_t raw[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) kr[mt] = read_k(0, mt);
+    for (int mt = 0; mt < 4; ++mt) {
+      const int key = mt * 16 + l16;
+      raw[mt] = *(const int4_t*)(ks + key * KROW + swz<KROW>(grp, key) * 16);
+    }
 #pragma unroll
-      for (int st = 0; st < STEPS; ++st) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-          for (int d = 0; d < ND; ++d)
-            s[mt][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kr[mt], q.qd[d][st], s[mt][0], 0, 0, 0, 127,
-                                                                         0, 127);
-          if (st + 1 < STEPS) kr[mt] = read_k(st + 1, mt);
-        }
-      }
-      // the order above, for the scheduler (MFMAs are pure and would
-      // otherwise all sink below the reads): 8 reads, then per (step, key
-      // tile) ND MFMAs followed by that tile's 2 reads of the next step
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-      for (int i = 0; i < 4 * (STEPS - 1); ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, ND, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4 * ND, 0);
-    } else {
-      constexpr int KSTEPS = DQK / 64;
-      int4_t acc[4][3][1];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int d = 0; d < 3; ++d) acc[mt][d][0] = int4_t{0, 0, 0, 0};
-      int4_t raw[4];
+    for (int sp = 0; sp < KSTEPS; ++sp) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const int key = mt * 16 + l16;
-        raw[mt] = *(const int4_t*)(ks + key * KROW + swz<KROW>(grp, key) * 16);
-      }
-#pragma unroll
-      for (int sp = 0; sp < KSTEPS; ++sp) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          qk_i8_step<1>(raw[mt], q.qd[sp], acc[mt]);
-          if (sp + 1 < KSTEPS) {
-            const int key = mt * 16 + l16;
-            raw[mt] = *(const int4_t*)(ks + key * KROW + swz<KROW>(4 * (sp + 1) + grp, key) * 16);
-          }
+        qk_i8_step<1>(raw[mt], q.qd[sp], acc[mt]);
+        if (sp + 1 < KSTEPS) {
+          const int key = mt * 16 + l16;
+          raw[mt] = *(const int4_t*)(ks + key * KROW + swz<KROW>(4 * (sp + 1) + grp, key) * 16);
         }
       }
-      // (as for fp8: per key tile, its 3 digit MFMAs, then its next read)
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
+    // (as for fp8: per key tile, its 3 digit MFMAs, then its next read)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int i = 0; i < 4 * (KSTEPS - 1); ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+    for (int i = 0; i < 4 * (KSTEPS - 1); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) s[mt][0] = s_from_i8(acc[mt][0][0], acc[mt][1][0], acc[mt][2][0]);
+    for (int mt = 0; mt < 4; ++mt) s[mt][0] = s_from_i8(acc[mt][0][0], acc[mt][1][0], acc[mt][2][0]);
     }
     {
       half8_t pb[2][1];
@@ -2536,7 +2491,7 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla2_kernel(AttnParam
       }
 #pragma unroll
       for (int md = 0; md < MDW; ++md) {
-        const half8_t a = bytes8_to_op<FP8>((uint32_t)vraw[md][0], (uint32_t)vraw[md][1]);
+        const half8_t a = bytes8_to_op<false>((uint32_t)vraw[md][0], (uint32_t)vraw[md][1]);
 #pragma unroll
         for (int nt = 0; nt < NTB; ++nt)
           o[md][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pbn[nt], o[md][nt], 0, 0, 0);
@@ -2596,9 +2551,9 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla2_kernel(AttnParam
   }
 }
 
-// MLA, producer/consumer form (e4m3fn caches, bf16 query with a per-head or
-// per-tensor K scale).  Eight waves, 64 rows, 32-key tiles, one barrier per
-// tile.  Waves 0..3 (producers) own row tile w: they issue the tile DMA,
+// MLA, producer/consumer form (e4m3fn caches; the query in two fp8 digits, or
+// three when it is fp32 or carries per-channel K scales: HILO).  Eight waves,
+// 64 rows, 32-key tiles, one barrier per tile.  Waves 0..3 (producers) own row tile w: they issue the tile DMA,
 // compute S^T for the tile's 32 keys on the fp8 MFMA (query in two fp8
 // digits), run the online softmax and write P^T and the rows' rescale factors
 // to LDS.  Waves 4..7 (consumers) own output dims 128 (w - 4) .. +127 of all
@@ -2632,7 +2587,7 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
 #undef PA_WAIT_CASE
 }
 
-template <bool BAL>
+template <bool BAL, bool HILO>
 __global__ __launch_bounds__(MLAPC_WAVES * 64, 1) void paged_mla_pc_kernel(AttnParams p) {
   constexpr int DQK = 576, DV = 512;
   constexpr int ROWS = 64, NTB = ROWS / 16;      // packed rows, row tiles
@@ -2641,7 +2596,7 @@ __global__ __launch_bounds__(MLAPC_WAVES * 64, 1) void paged_mla_pc_kernel(AttnP
   constexpr int T32 = MLAPC_TK;
   constexpr int KTILE = T32 * KROW;               // 18 KB raw tile
   constexpr int NSTAGE = MLAPC_NSTAGE;
-  constexpr int ND = 2;                           // fp8 digits of the bf16 query
+  constexpr int ND = HILO ? 3 : 2;                // fp8 digits of the query
   constexpr int STEPS = QRowsF8<DQK, ND>::STEPS;  // 128-dim steps of S^T (5)
   using LD = DmaTileLoader<KROW, KROW, 4, true, true, T32>;
   static_assert(LD::K_DMA == 5 && LD::KCH == 18 * 64, "producers 0, 1 issue 5 blocks per tile, 2, 3 issue 4");
@@ -2710,7 +2665,8 @@ __global__ __launch_bounds__(MLAPC_WAVES * 64, 1) void paged_mla_pc_kernel(AttnP
         for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
           for (int d = 0; d < ND; ++d)
-            s[jb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kr[jb], q.qd[d][st], s[jb], 0, 0, 0, 127, 0, 127);
+            s[jb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kr[jb], q.qd[d][st], s[jb], 0, 0, 0, 127, 0,
+                                                                  q.sc[st]);
           if (st + 1 < STEPS) kr[jb] = read_k(st + 1, jb);
         }
         // this step's MFMAs interleaved with the next step's operand reads
@@ -2824,13 +2780,22 @@ __global__ __launch_bounds__(MLAPC_WAVES * 64, 1) void paged_mla_pc_kernel(AttnP
     }
     __syncthreads();   // row sums
     const int mode = p.scale_mode;
-    const float vs1 = p.v_scale[mode == PA_SCALE_PER_HEAD ? g : 0];   // per-channel V goes to the four-wave kernel
+    float4_t vsc[MDC];   // V scales of this wave's dims
+    if (mode == PA_SCALE_PER_CHANNEL) {
+#pragma unroll
+      for (int md = 0; md < MDC; ++md)
+        vsc[md] = *(const float4_t*)(p.v_scale + (int64_t)g * DV + (cw * MDC + md) * 16 + grp * 4);
+    } else {
+      const float v = p.v_scale[mode == PA_SCALE_PER_HEAD ? g : 0];
+#pragma unroll
+      for (int md = 0; md < MDC; ++md) vsc[md] = float4_t{v, v, v, v};
+    }
 #pragma unroll
     for (int nt = 0; nt < NTB; ++nt) {
       const int r = u.row0 + nt * 16 + l16;
       if (r >= u.rows_total) continue;
       const float lt = lrow_lds[nt * 16 + l16];
-      const float inv = lt > 0.f ? vs1 / lt : 0.f;
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
       const int tok = u.tok0 + r / u.G;
       const int h = g * u.G + r % u.G;
       float* prow = u.split ? p.part_o + (((int64_t)tok * p.max_chunks + u.c) * H_q + h) * DV : nullptr;
@@ -2840,7 +2805,7 @@ __global__ __launch_bounds__(MLAPC_WAVES * 64, 1) void paged_mla_pc_kernel(AttnP
         const int d = (cw * MDC + md) * 16 + grp * 4;
         float4_t v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = o[md][nt][i] * inv;
+        for (int i = 0; i < 4; ++i) v[i] = o[md][nt][i] * inv * vsc[md][i];
         if (u.split) {
           *(float4_t*)(prow + d) = v;
         } else {
@@ -3046,15 +3011,15 @@ template <bool FP8, bool HILO>
 hipError_t launch_mla(const AttnParams& p, dim3 grid, hipStream_t stream) {
   // the balanced split's planner is a variant of its own (it costs the main
   // loop SGPR spills)
-  if constexpr (FP8 && !HILO) {   // e4m3fn keys with a two-digit query: producer/consumer kernel
+  if constexpr (FP8) {   // e4m3fn keys: producer/consumer kernel
     if (p.balanced)
-      hipLaunchKernelGGL((paged_mla_pc_kernel<true>), grid, dim3(MLAPC_WAVES * 64), 0, stream, p);
+      hipLaunchKernelGGL((paged_mla_pc_kernel<true, HILO>), grid, dim3(MLAPC_WAVES * 64), 0, stream, p);
     else
-      hipLaunchKernelGGL((paged_mla_pc_kernel<false>), grid, dim3(MLAPC_WAVES * 64), 0, stream, p);
-  } else if (p.balanced) {
-    hipLaunchKernelGGL((paged_mla2_kernel<FP8, HILO, true>), grid, dim3(MLA_WAVES * 64), 0, stream, p);
+      hipLaunchKernelGGL((paged_mla_pc_kernel<false, HILO>), grid, dim3(MLAPC_WAVES * 64), 0, stream, p);
+  } else if (p.balanced) {   // int8 keys (the query's dtype and scales change nothing there)
+    hipLaunchKernelGGL((paged_mla_i8_kernel<true>), grid, dim3(MLA_WAVES * 64), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((paged_mla2_kernel<FP8, HILO, false>), grid, dim3(MLA_WAVES * 64), 0, stream, p);
+    hipLaunchKernelGGL((paged_mla_i8_kernel<false>), grid, dim3(MLA_WAVES * 64), 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -3081,8 +3046,8 @@ int occ_one() {
 }
 template <bool FP8, bool HILO>
 int occ_mla() {
-  if constexpr (FP8 && !HILO) return occupancy_of(paged_mla_pc_kernel<false>, MLAPC_WAVES * 64);
-  return occupancy_of(paged_mla2_kernel<FP8, HILO, false>, MLA_WAVES * 64);
+  if constexpr (FP8) return occupancy_of(paged_mla_pc_kernel<false, HILO>, MLAPC_WAVES * 64);
+  return occupancy_of(paged_mla_i8_kernel<false>, MLA_WAVES * 64);
 }
 template <int D, bool FP8, int NT, bool HILO, int KS, bool TREE>
 int occ_decode() {

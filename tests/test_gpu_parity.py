@@ -233,7 +233,7 @@ def test_edge_case_parity(case):
 # logits, so these cases also run under several seeds: a numerics margin must
 # hold for every draw, not one.  Per-head and per-channel K scales, int8 and
 # fp8 caches, each kernel family (decode unit, 40-row shared tile, append tile,
-# int8 MLA-shaped rows).
+# int8 and e4m3fn MLA-shaped rows).
 OUTLIER_CASES = {
     "decode_query_outliers_head": EDGE_CASES["decode_query_outliers_head"],
     "spec40_query_outliers_channel": EDGE_CASES["spec40_query_outliers_channel"],
@@ -245,11 +245,34 @@ OUTLIER_CASES = {
     "mla_int8_query_outliers": dict(num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
                                     shared_kv=True, scale_mode="tensor", q_lens=[2, 2], seq_lens_kv=[63, 900],
                                     decode=True, chunk_size=256, q_outliers=((3, 530), 64.0)),
+    # e4m3fn MLA: the query goes to the fp8 MFMA in two digits (bf16, per-tensor
+    # scale) or three (per-channel scales folded in)
+    "mla_fp8_query_outliers": dict(num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
+                                   shared_kv=True, kv_dtype="fp8_e4m3", scale_mode="tensor",
+                                   scale_range=(0.0005, 0.008), q_lens=[2, 2], seq_lens_kv=[63, 900],
+                                   decode=True, chunk_size=256, q_outliers=((3, 530), 64.0)),
+    "mla_fp8_query_outliers_channel": dict(num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
+                                           shared_kv=True, kv_dtype="fp8_e4m3", scale_mode="channel",
+                                           scale_range=(0.0005, 0.008), q_lens=[2, 2], seq_lens_kv=[63, 900],
+                                           decode=True, chunk_size=256, q_outliers=((3, 530), 64.0)),
 }
 
 
+# QK^T of the e4m3fn MLA kernel runs on the fp8 MFMA, whose accumulation was
+# measured to keep ~11 bits below the largest product of an instruction
+# (error 2^-11.3 of it; the f16 MFMA on the same values: 2e-7).  With two
+# query channels 64x the rest, that product is the outlier's, and the LSE
+# error reaches ~1.3e-2 at sm_scale 1/sqrt(128), over the 1e-3 bound; the
+# seeded workloads' N(0, 1) queries stay near 2e-4.  Kept as strict expected
+# failures so that a change in either direction shows.
+FP8_MFMA_ACCUMULATION = pytest.mark.xfail(
+    strict=True, reason="fp8 MFMA accumulation (~2^-11 of the largest product) with 64x outlier query channels")
+OUTLIER_PARAMS = [pytest.param(c, marks=FP8_MFMA_ACCUMULATION) if c.startswith("mla_fp8") else c
+                  for c in sorted(OUTLIER_CASES)]
+
+
 @pytest.mark.parametrize("seed", [11, 2024, 7777])
-@pytest.mark.parametrize("case", sorted(OUTLIER_CASES))
+@pytest.mark.parametrize("case", OUTLIER_PARAMS)
 def test_query_outliers_seeds(case, seed):
     need_gpu()
     kw = dict(OUTLIER_CASES[case])
