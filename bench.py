@@ -14,10 +14,12 @@ quoted on.  --config 1..5 selects another workload.
 Prints ONE JSON line with the headline metric, the roofline of the attention
 kernel and the oracle's throughput on a bounded sample of the same workload
 (cpu_baseline).  A split-KV step makes the ABI call with PA_FLAG_DEFER_MERGE
-and then runs split_kv_merge, with HIP events on the launch stream before,
-between and after, so the attention kernel is timed on its own and a step is
-still the whole path.  roofline.frac is the attention kernel's (algorithmic
-bytes or flops over its event time); roofline.step_frac is the whole step's
+and then runs split_kv_merge.  The steps are timed twice with HIP events on
+the launch stream: once with one event pair around the whole step (nothing
+recorded between the two launches: ms_per_step and value), once more with an
+event between them as well (roofline.kernel_ms, the attention kernel alone,
+and merge_ms).  roofline.frac is the attention kernel's (algorithmic bytes
+or flops over its event time); roofline.step_frac is the whole step's
 (attention + merge).  For the decode workloads the line also carries the
 read probe (pa_kv_read_probe: the same tiles through the same loader with no
 arithmetic), the read bandwidth this access pattern allows.  The default run
@@ -220,7 +222,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--chunk", type=int, default=None, help="override chunk_size")
     ap.add_argument("--no-flush", action="store_true", help="skip the per-step cache flush")
@@ -349,10 +351,12 @@ def main():
 
 def measure(w, config, flush, steps, warmup, chunk=None, fused=False, balanced=False, no_flush=False,
             persistent=False):
-    """Time `steps` calls of the workload after `warmup` untimed ones.  Per
-    step: [flush] e0 attention e1 merge e2 on the launch stream (torch's
-    current stream, which the binding passes to the library); with the fused
-    or balanced merge e1..e2 encloses nothing."""
+    """Time `steps` calls of the workload after `warmup` untimed ones, twice on
+    the launch stream (torch's current stream, which the binding passes to the
+    library).  The step pass brackets each call with one event pair, [flush]
+    e0 attention [merge] e2, so nothing is recorded between the two launches
+    (an event there costs 2-5 us on this stack).  The breakdown pass records
+    e0 attention e1 [merge e2] for the kernel and merge times."""
     import torch
     from paged_kv_attention_gather_amd.harness import DeviceProblem
     one_call = fused or balanced or persistent   # the call merges by itself
@@ -360,7 +364,7 @@ def measure(w, config, flush, steps, warmup, chunk=None, fused=False, balanced=F
                        persistent=persistent)
     chunk = dp.prob.chunk_size
     stream = torch.cuda.current_stream()
-    separate = not one_call   # merge launched here, timed apart
+    separate = not one_call and chunk > 0   # a merge launched here, timed apart
     print(f"[bench] {w.name}: warmup {warmup}", file=sys.stderr, flush=True)
     for _ in range(warmup):
         if not no_flush:
@@ -369,24 +373,30 @@ def measure(w, config, flush, steps, warmup, chunk=None, fused=False, balanced=F
         if separate:
             dp.merge()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+
+    def timed(breakdown):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(steps):
+            if not no_flush:
+                flush.max()
+            ev[i][0].record(stream)
+            dp.run()
+            if breakdown:
+                ev[i][1].record(stream)
+            if separate:
+                dp.merge()
+            if separate or not breakdown:
+                ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        return ev
+
     t_wall0 = time.perf_counter()
-    for i in range(steps):
-        if not no_flush:
-            flush.max()
-        ev[i][0].record(stream)
-        dp.run()
-        ev[i][1].record(stream)
-        if separate:
-            dp.merge()
-            ev[i][2].record(stream)
-    torch.cuda.synchronize()
+    ev = timed(False)
     t_wall = time.perf_counter() - t_wall0
-    # a call that merges by itself is one event pair: an empty pair e1..e2
-    # still reads ~5 us on this stack and would be charged to it
-    step = [e[0].elapsed_time(e[2] if separate else e[1]) for e in ev]
+    step = [e[0].elapsed_time(e[2]) for e in ev]
+    ev = timed(True)
     attn = [e[0].elapsed_time(e[1]) for e in ev]
-    merge = [e[1].elapsed_time(e[2]) for e in ev] if chunk > 0 and separate else [0.0]
+    merge = [e[1].elapsed_time(e[2]) for e in ev] if separate else [0.0]
     print(f"[bench] {w.name}: step {np.mean(step) * 1e3:.1f} us, attention {np.mean(attn) * 1e3:.1f} us",
           file=sys.stderr, flush=True)
     return {"dp": dp, "chunk": int(chunk), "step_ms": float(np.mean(step)), "step_min_ms": float(np.min(step)),
@@ -456,7 +466,7 @@ def other_configs(flush, args):
     for idx in (3, 4, 5):
         print(f"[bench] generating workload {idx}", file=sys.stderr, flush=True)
         w = config_workload(idx)
-        m = measure(w, idx, flush, max(5, args.steps // 2), max(2, args.warmup // 2), no_flush=args.no_flush)
+        m = measure(w, idx, flush, max(5, args.steps // 2), max(2, args.warmup), no_flush=args.no_flush)
         kv_bytes, alg_bytes, flops = work_figures(w)
         r = roofline(idx, w, m["attn_ms"], m["step_ms"])
         row = {"workload": WORKLOAD_TEXT[idx], "kernel": kernel_name(m["dp"]), "dtype": compute_dtype(m["dp"]),
