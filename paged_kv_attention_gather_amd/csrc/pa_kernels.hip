@@ -1486,34 +1486,6 @@ struct DmaTileLoader {
     }
   }
 
-  // Split issue of a K-only (SHARED) tile, for a wave that spreads its DMA
-  // instructions between MFMAs (an issue stalls while the CU's load path is
-  // full; with MFMAs in flight the stall is hidden): begin() returns true on
-  // the one-page fast path, where part(j), j < K_DMA, issues block j;
-  // otherwise begin() has issued the whole tile itself.
-  const uint8_t* part_kb;
-  uint32_t part_kdst;
-  __device__ __forceinline__ bool begin(const AttnParams& p, int tile, int stage) {
-    static_assert(SHARED, "split issue covers K-only tiles");
-    const int kbase = kv_lo + tile * TKEYS;
-    if (fast_addr && kbase + TKEYS <= key_end) {
-      const int pg0 = kbase >> page_shift;
-      if (pg0 < pw_base || pg0 > pw_base + 63) {
-        pw_base = pg0;
-        pw_val = load_i32_sync(table_row + min(pg0 + (int)(threadIdx.x & 63), last_page));
-      }
-      const int pp0 = __builtin_amdgcn_readlane(pw_val, pg0 - pw_base);
-      part_kb = paged_row(p.k_cache, pp0, kbase, page_shift, g, p.k_stride_page, p.k_stride_head, p.k_stride_token);
-      part_kdst = smem_base + stage * STAGE;
-      return true;
-    }
-    issue(p, tile, stage);
-    return false;
-  }
-  __device__ __forceinline__ void part(int j) {
-    if ((j * NW + wave) * 64 < KCH) dma16_s(k_offset(j), part_kb, part_kdst + (j * NW + wave) * 1024);
-  }
-
   // Issues this wave's share of tile `tile` into LDS stage `stage`.
   __device__ __forceinline__ void issue(const AttnParams& p, int tile, int stage) {
     const int kbase = kv_lo + tile * TKEYS;
@@ -2553,14 +2525,18 @@ __global__ __launch_bounds__(MLA_WAVES * 64, 1) void paged_mla_i8_kernel(AttnPar
 
 // MLA, producer/consumer form (e4m3fn caches; the query in two fp8 digits, or
 // three when it is fp32 or carries per-channel K scales: HILO).  Eight waves,
-// 64 rows, 32-key tiles, one barrier per tile.  Waves 0..3 (producers) own row tile w: they issue the tile DMA,
-// compute S^T for the tile's 32 keys on the fp8 MFMA (query in two fp8
-// digits), run the online softmax and write P^T and the rows' rescale factors
-// to LDS.  Waves 4..7 (consumers) own output dims 128 (w - 4) .. +127 of all
-// 64 rows and accumulate O^T += V^T P^T for the tile the producers finished in
-// the previous iteration.  Each SIMD holds one producer and one consumer, so
-// the MFMAs of one overlap the other's LDS reads, conversions and softmax
-// instead of every wave passing through the same phases between barriers.
+// 64 rows, 32-key tiles, one barrier per tile.  Waves 0..3 (producers) own
+// row tile w: they compute S^T for the tile's 32 keys on the fp8 MFMA (query
+// in two fp8 digits), run the online softmax and write P^T and the rows'
+// rescale factors to LDS.  Waves 4..7 (consumers) issue the tile DMA and wait
+// for it, own output dims 128 (w - 4) .. +127 of all 64 rows and accumulate
+// O^T += V^T P^T for the tile the producers finished in the previous
+// iteration.  Each SIMD holds one producer and one consumer, so the MFMAs of
+// one overlap the other's LDS reads, conversions and softmax instead of every
+// wave passing through the same phases between barriers.  The DMA sits with
+// the consumers because an issue that stalls on a full load path would hold
+// back the producers' dependent QK^T chain; the consumers' 32 accumulators
+// are independent (measured 129-133 against 134-135 us on the MLA workload).
 // Iteration j: producers handle tile j (j < n), consumers tile j - 1 (j > 0).
 // The barrier that opens iteration j says: tile j has landed, P^T of tile
 // j - 1 is written, and the consumers are done with tile j - 2, whose stage
@@ -2599,7 +2575,7 @@ __global__ __launch_bounds__(MLAPC_WAVES * 64, 1) void paged_mla_pc_kernel(AttnP
   constexpr int ND = HILO ? 3 : 2;                // fp8 digits of the query
   constexpr int STEPS = QRowsF8<DQK, ND>::STEPS;  // 128-dim steps of S^T (5)
   using LD = DmaTileLoader<KROW, KROW, 4, true, true, T32>;
-  static_assert(LD::K_DMA == 5 && LD::KCH == 18 * 64, "producers 0, 1 issue 5 blocks per tile, 2, 3 issue 4");
+  static_assert(LD::K_DMA == 5 && LD::KCH == 18 * 64, "consumers 0, 1 issue 5 blocks per tile, 2, 3 issue 4");
   static_assert((NSTAGE - 3) * 5 <= 31, "wait_vmcnt_dyn covers the tiles in flight");
 
   __shared__ __attribute__((aligned(1024))) uint8_t kst[NSTAGE * KTILE];   // raw tiles
@@ -2621,22 +2597,13 @@ __global__ __launch_bounds__(MLAPC_WAVES * 64, 1) void paged_mla_pc_kernel(AttnP
   if (wave < 4) {
     // ------------------------------------------------------------ producer --
     const int rt = wave;
-    LD ld;
-    ld.init(p, b, g, wave, kv_lo, u.key_end, n, lane, lds_addr(kst));
-#pragma unroll
-    for (int st = 0; st < NSTAGE - 2; ++st)
-      if (st < n) ld.issue(p, st, st);
-    const int per_tile = wave < 2 ? 5 : 4;        // this wave's DMA blocks per tile
     QRowsF8<DQK, ND> q;
     load_query_f8<DQK, ND>(p, u, g, u.row0 + rt * 16, lane, q);
     float m = -INFINITY, l = 0.f;
     const half2_t ones2 = {(_Float16)1.0f, (_Float16)1.0f};
     for (int j = 0; j <= n; ++j) {
-      if (j < n) wait_vmcnt_dyn(min(n - 1 - j, NSTAGE - 3) * per_tile);   // tile j landed
       __syncthreads();
       if (j == n) break;
-      // tile j + NSTAGE - 2: one DMA block per QK step below (see begin())
-      const bool split = j + NSTAGE - 2 < n && ld.begin(p, j + NSTAGE - 2, (j + NSTAGE - 2) % NSTAGE);
       const uint8_t* ks = kst + (j % NSTAGE) * KTILE;
 
       float4_t s[2];
@@ -2655,7 +2622,6 @@ __global__ __launch_bounds__(MLAPC_WAVES * 64, 1) void paged_mla_pc_kernel(AttnP
         }
         return r;
       };
-      static_assert(LD::K_DMA == STEPS, "one DMA block per QK step");
       v8i_t kr[2];
       kr[0] = read_k(0, 0);
       kr[1] = read_k(0, 1);
@@ -2680,10 +2646,9 @@ __global__ __launch_bounds__(MLAPC_WAVES * 64, 1) void paged_mla_pc_kernel(AttnP
         } else {
           __builtin_amdgcn_sched_group_barrier(0x008, 2 * ND, 0);
         }
-        // the accumulators pass through an empty asm here, so this step's
-        // MFMAs are issued before the DMA block (otherwise they sink to the softmax)
+        // the accumulators pass through an empty asm here, so each step's
+        // MFMAs stay in their step (otherwise they sink to the softmax)
         asm volatile("" : "+v"(s[0]), "+v"(s[1]));
-        if (split) ld.part(st);
       }
 
       // online softmax of this tile's 32 keys (key of s[jb][i]: kbase + 16 jb + 4 grp + i)
@@ -2744,8 +2709,16 @@ __global__ __launch_bounds__(MLAPC_WAVES * 64, 1) void paged_mla_pc_kernel(AttnP
     // V^T operand rows in the key order of the P^T operand: lane group grp holds
     // keys 4 grp .. 4 grp + 3 and 16 + 4 grp .. 16 + 4 grp + 3
     const int vrow = jr < 4 ? 4 * grp + jr : 16 + 4 * grp + (jr - 4);
+    LD ld;
+    ld.init(p, b, g, cw, kv_lo, u.key_end, n, lane, lds_addr(kst));
+#pragma unroll
+    for (int st = 0; st < NSTAGE - 2; ++st)
+      if (st < n) ld.issue(p, st, st);
+    const int per_tile = cw < 2 ? 5 : 4;          // this wave's DMA blocks per tile
     for (int j = 0; j <= n; ++j) {
+      if (j < n) wait_vmcnt_dyn(min(n - 1 - j, NSTAGE - 3) * per_tile);   // tile j landed
       __syncthreads();
+      if (j + NSTAGE - 2 < n) ld.issue(p, j + NSTAGE - 2, (j + NSTAGE - 2) % NSTAGE);
       if (j == 0) continue;
       const int t = j - 1, buf = t & 1;
       const uint8_t* vs = kst + (t % NSTAGE) * KTILE;
